@@ -1,0 +1,27 @@
+"""CPU oracle for the weight-only LUT-quantized matmul -- TEST INFRASTRUCTURE.
+
+Plain, slow, obviously correct numpy code, fp64 accumulation. Only the test
+suite, the smoke check and the benchmark's CPU-baseline leg may import it.
+The library under ``weight_only_lut_amd`` never calls it: it has no CPU
+fallback, and it shares no code, table or constant with this package.
+
+What it computes (page 2, FLUTE abstract: weight-only quantization with the
+dequantization fused into the matmul; page 2, BitMoD abstract: per-group
+rescaling of partial sums, which is the same sum in another order):
+
+    W_hat[n, k] = T[c[n, k]] * s[n, k // group]      (s[0] when group == 0)
+    y[m, n]     = sum_k x[m, k] * W_hat[n, k]
+
+Every function cites the passage it follows. Parity status of each function
+is in the docstring; all are pinned by tests/test_oracle.py.
+"""
+
+from .lutq_ref import (  # noqa: F401
+    pack_codes,
+    unpack_codes,
+    dequant,
+    reference,
+    reference_rows,
+    error_bound,
+    check,
+)

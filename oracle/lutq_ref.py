@@ -1,0 +1,122 @@
+"""The oracle's arithmetic. See the package docstring for scope and status.
+
+Readings taken where the pages leave a step open:
+
+- codes are b-bit integers, b in {2, 3, 4} (page 2, FLUTE abstract: packed
+  codes including the non-evenly-divisible 3 bits);
+- the table has 2^b fp16 entries and the scales are fp16, one per ``group``
+  consecutive weights along K, or one per tensor (``group == 0``; page 1,
+  LogbQuant abstract, tensor-wise granularity);
+- dequantization is one fp32 multiply (round to nearest even) of the table
+  entry by its scale; the product is accumulated in fp64.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+ROW_CHUNK = 2048
+
+
+# -- canonical packing (the oracle's own format; page 2, FLUTE abstract:
+#    weights are stored as packed b-bit codes) --------------------------------
+
+def pack_codes(codes: np.ndarray, bits: int) -> np.ndarray:
+    """Row-wise LSB-first bit stream: code k of a row occupies bits [k*b, k*b+b).
+
+    Returns uint8 [N, ceil(K*b/8)]. Codes must already be < 2^bits.
+    Pinned: hand-derived byte fixture + exhaustive round trip.
+    """
+    N, K = codes.shape
+    if np.any(codes >> bits):
+        raise ValueError("code out of range")
+    # bit j of code k lands at stream bit k*bits + j
+    bitmat = ((codes[:, :, None] >> np.arange(bits, dtype=np.uint8)) & 1).astype(np.uint8)
+    stream = bitmat.reshape(N, K * bits)
+    nbytes = (K * bits + 7) // 8
+    pad = nbytes * 8 - K * bits
+    if pad:
+        stream = np.concatenate([stream, np.zeros((N, pad), np.uint8)], axis=1)
+    return np.packbits(stream.reshape(N, nbytes, 8), axis=2, bitorder="little").reshape(N, nbytes)
+
+
+def unpack_codes(packed: np.ndarray, N: int, K: int, bits: int) -> np.ndarray:
+    """Inverse of ``pack_codes``: uint8 codes [N, K]."""
+    stream = np.unpackbits(packed.reshape(N, -1, 1), axis=2, bitorder="little").reshape(N, -1)
+    stream = stream[:, : K * bits].reshape(N, K, bits).astype(np.uint8)
+    return (stream << np.arange(bits, dtype=np.uint8)).sum(axis=2, dtype=np.uint8)
+
+
+# -- dequantization (page 2, FLUTE abstract: LUT-quantized weights; scale per
+#    group of 128 along K; page 1: one scale per tensor) ----------------------
+
+def dequant(codes: np.ndarray, lut: np.ndarray, scales: np.ndarray, group: int) -> np.ndarray:
+    """W_hat = fp32(T[c]) * fp32(s[n, k // group]), one RNE fp32 multiply. [N, K] fp32.
+
+    Pinned: the uniform table reproduces INT RTN dequantization bit-exactly;
+    one-hot products decode single weights.
+    """
+    N, K = codes.shape
+    t = lut.astype(np.float32)[codes]
+    if group == 0:
+        return t * np.float32(scales.reshape(-1)[0])
+    if K % group:
+        raise ValueError("K must be a multiple of group")
+    s = scales.astype(np.float32).reshape(N, K // group)
+    return (t.reshape(N, K // group, group) * s[:, :, None]).reshape(N, K)
+
+
+# -- the product (fp64 accumulation) ------------------------------------------
+
+def _rows(codes, lut, scales, group, rows):
+    if group == 0:
+        return dequant(codes[rows], lut, scales, 0)
+    return dequant(codes[rows], lut, scales[rows], group)
+
+
+def reference(x: np.ndarray, codes: np.ndarray, lut: np.ndarray, scales: np.ndarray,
+              group: int):
+    """(y_ref, B): y_ref = fp64(x) @ fp64(W_hat).T and B = |x| @ |W_hat|.T, both [M, N] fp64.
+
+    Chunked over N to bound memory. Pinned: exact rational brute force on
+    tiny shapes, linearity in the scale, one-hot x.
+    """
+    N, K = codes.shape
+    x64 = x.astype(np.float64)
+    ax = np.abs(x64)
+    M = x.shape[0]
+    y = np.empty((M, N), np.float64)
+    B = np.empty((M, N), np.float64)
+    for n0 in range(0, N, ROW_CHUNK):
+        n1 = min(N, n0 + ROW_CHUNK)
+        w = _rows(codes, lut, scales, group, slice(n0, n1)).astype(np.float64)
+        y[:, n0:n1] = x64 @ w.T
+        B[:, n0:n1] = ax @ np.abs(w).T
+    return y, B
+
+
+def reference_rows(x, codes, lut, scales, group, rows):
+    """``reference`` restricted to output columns ``rows`` (indices into N)."""
+    rows = np.asarray(rows)
+    w = _rows(codes, lut, scales, group, rows).astype(np.float64)
+    x64 = x.astype(np.float64)
+    return x64 @ w.T, np.abs(x64) @ np.abs(w).T
+
+
+# -- acceptance ---------------------------------------------------------------
+
+REL_TOL = 1e-3
+ABS_TOL = 1e-5
+
+
+def error_bound(B: np.ndarray) -> np.ndarray:
+    """Per-output tolerance 1e-3 * sum_k |x_k * w_k| + 1e-5."""
+    return REL_TOL * B + ABS_TOL
+
+
+def check(y: np.ndarray, y_ref: np.ndarray, B: np.ndarray):
+    """(ok, worst): ok when every |y - y_ref| <= error_bound(B); worst is max(err / bound)."""
+    err = np.abs(y.astype(np.float64) - y_ref)
+    ratio = err / error_bound(B)
+    worst = float(ratio.max()) if ratio.size else 0.0
+    return bool(np.all(np.isfinite(y)) and worst <= 1.0), worst

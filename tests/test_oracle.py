@@ -1,0 +1,216 @@
+"""Pins for the CPU oracle: each check rests on something other than the oracle.
+
+- packing: hand-derived byte fixtures and an exhaustive round trip;
+- dequantization: the uniform table reproduces INT RTN (an integer formula);
+- product: exact rational arithmetic on tiny non-square shapes, linearity in
+  the scale, one-hot activations;
+- acceptance: the tolerance accepts and rejects where it should;
+- mutations: plausible mistakes planted in a copy of the oracle fail a pin.
+"""
+
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import lutq_ref
+from synth import draw, rtn, tables, workloads
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _read_fixture(name):
+    rows = []
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            rows.append([p.strip() for p in line.split("|")])
+    return rows
+
+
+# -- packing ------------------------------------------------------------------
+
+def test_pack_matches_hand_derived_bytes():
+    for bits, codes, want in _read_fixture("pack_lsb_first.txt"):
+        b = int(bits)
+        c = np.array([[int(v) for v in codes.split()]], dtype=np.uint8)
+        got = oracle.pack_codes(c, b)[0]
+        assert bytes(got) == bytes(int(h, 16) for h in want.split()), (bits, codes)
+        assert np.array_equal(oracle.unpack_codes(got[None], 1, c.shape[1], b), c)
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_pack_roundtrip_every_value_every_offset(bits):
+    # every code value at every bit offset within a 96-bit period
+    period = 96 // bits
+    L = 1 << bits
+    rows = []
+    for v in range(L):
+        for off in range(period):
+            r = np.zeros(period + 3, np.uint8)
+            r[off] = v
+            rows.append(r)
+            r2 = np.full(period + 3, L - 1, np.uint8)
+            r2[off] = v
+            rows.append(r2)
+    c = np.stack(rows)
+    p = oracle.pack_codes(c, bits)
+    assert p.shape[1] == (c.shape[1] * bits + 7) // 8
+    assert np.array_equal(oracle.unpack_codes(p, c.shape[0], c.shape[1], bits), c)
+
+
+@pytest.mark.parametrize("bits,table", [(2, "nf"), (3, "lloyd_max"), (4, "int"), (4, "log")])
+def test_quantize_pack_unpack_roundtrip(bits, table):
+    c, T, s, _ = workloads.small_case(bits, table, 128, 1, 37, 384, seed=bits)
+    p = oracle.pack_codes(c, bits)
+    assert np.array_equal(oracle.unpack_codes(p, *c.shape, bits), c)
+    assert c.max() < (1 << bits)
+
+
+def test_pack_rejects_out_of_range_codes():
+    with pytest.raises(ValueError):
+        oracle.pack_codes(np.array([[8]], np.uint8), 3)
+
+
+# -- dequantization -----------------------------------------------------------
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+@pytest.mark.parametrize("group", [128, 0])
+def test_uniform_lut_reproduces_int_rtn(bits, group):
+    """A uniform table T[i] = i - z dequantizes exactly like asymmetric INT RTN."""
+    W = draw.weights("normal_outliers", 48, 512, (7, bits, group), sigma=0.02, p=0.01, mult=10.0)
+    T = tables.int_uniform(bits)
+    z = 1 << (bits - 1)
+    c, s = rtn.quantize(W, T, group, "int")
+    # textbook asymmetric INT RTN, written with integers: q = clamp(rint(w/s) + z, 0, 2^b - 1)
+    s64 = (np.repeat(s.astype(np.float64), group, axis=1) if group else np.full(W.shape, float(s[0])))
+    r = W.astype(np.float64) / s64
+    assert not np.any(np.abs(r - np.floor(r) - 0.5) < 1e-12), "exact tie in test data"
+    q = np.clip(np.rint(r) + z, 0, (1 << bits) - 1).astype(np.int64)
+    assert np.array_equal(q, c.astype(np.int64))
+    int_deq = (q - z).astype(np.float32) * s64.astype(np.float32)
+    assert np.array_equal(oracle.dequant(c, T, s, group).view(np.uint32), int_deq.view(np.uint32))
+
+
+def test_dequant_scale_index_is_along_k():
+    # a hand case: N=2, K=256, group=128, every code 1 -> T[1]
+    T = np.array([0, 1, 2, 3], np.float16)
+    c = np.ones((2, 256), np.uint8)
+    s = np.array([[2, 3], [5, 7]], np.float16)
+    w = oracle.dequant(c, T, s, 128)
+    assert np.all(w[0, :128] == 2) and np.all(w[0, 128:] == 3)
+    assert np.all(w[1, :128] == 5) and np.all(w[1, 128:] == 7)
+
+
+# -- the product --------------------------------------------------------------
+
+def _exact(x, codes, T, s, group):
+    """sum_k x*T[c]*s in exact rationals; the fp32 product T*s is rounded as IEEE does."""
+    M, K = x.shape
+    N = codes.shape[0]
+    w = np.empty((N, K), dtype=object)
+    for n in range(N):
+        for k in range(K):
+            sv = s.reshape(-1)[0] if group == 0 else s[n, k // group]
+            # T and s are fp16, so their exact product has <= 22 significant bits
+            # and needs one rounding to fp32: do it through Fraction -> float32
+            prod = Fraction(float(T[codes[n, k]])) * Fraction(float(sv))
+            w[n, k] = Fraction(float(np.float32(float(prod))))
+    y = [[sum(Fraction(float(x[m, k])) * w[n, k] for k in range(K)) for n in range(N)]
+         for m in range(M)]
+    return y
+
+
+@pytest.mark.parametrize("bits,table,group,M,N,K", [
+    (4, "nf", 128, 3, 5, 256),
+    (3, "lloyd_max", 128, 2, 3, 384),
+    (2, "nf", 0, 1, 4, 128),
+    (4, "log", 0, 3, 2, 256),
+])
+def test_product_matches_exact_rationals(bits, table, group, M, N, K):
+    c, T, s, x = workloads.small_case(bits, table, group, M, N, K, seed=11 + bits)
+    y, B = oracle.reference(x, c, T, s, group)
+    ex = _exact(x, c, T, s, group)
+    for m in range(M):
+        for n in range(N):
+            assert abs(y[m, n] - float(ex[m][n])) <= 1e-12 * B[m, n] + 1e-300
+
+
+def test_product_is_linear_in_the_scale():
+    c, T, s, x = workloads.small_case(4, "nf", 128, 4, 33, 512, seed=3)
+    y1, _ = oracle.reference(x, c, T, s, 128)
+    y2, _ = oracle.reference(x, c, T, (s.astype(np.float32) * 4).astype(np.float16), 128)
+    assert np.array_equal(y2, 4 * y1)
+
+
+def test_one_hot_activation_decodes_single_weights():
+    c, T, s, _ = workloads.small_case(3, "lloyd_max", 128, 1, 9, 256, seed=5)
+    x = np.eye(256, dtype=np.float16)[[0, 1, 127, 128, 255]]
+    y, _ = oracle.reference(x, c, T, s, 128)
+    for m, k in enumerate([0, 1, 127, 128, 255]):
+        want = T[c[:, k]].astype(np.float32) * s[:, k // 128].astype(np.float32)
+        assert np.array_equal(y[m], want.astype(np.float64))
+
+
+def test_reference_rows_agrees_with_reference():
+    c, T, s, x = workloads.small_case(4, "int", 128, 3, 40, 256, seed=9)
+    y, B = oracle.reference(x, c, T, s, 128)
+    rows = np.array([0, 7, 39, 13])
+    yr, Br = oracle.reference_rows(x, c, T, s, 128, rows)
+    assert np.array_equal(yr, y[:, rows]) and np.array_equal(Br, B[:, rows])
+
+
+# -- acceptance ---------------------------------------------------------------
+
+def test_check_accepts_inside_and_rejects_outside_the_bound():
+    c, T, s, x = workloads.small_case(4, "nf", 128, 2, 16, 256, seed=2)
+    y, B = oracle.reference(x, c, T, s, 128)
+    bound = oracle.error_bound(B)
+    assert oracle.check(y + 0.9 * bound, y, B)[0]
+    bad = y.copy()
+    bad[1, 3] += 1.5 * bound[1, 3]
+    ok, worst = oracle.check(bad, y, B)
+    assert not ok and worst > 1.0
+    nan = y.copy()
+    nan[0, 0] = np.nan
+    assert not oracle.check(nan, y, B)[0]
+
+
+# -- planted mistakes: each must fail one of the pins above -------------------
+
+def _mutant_dequant(kind):
+    original = lutq_ref.dequant
+
+    def f(codes, lut, scales, group):
+        N, K = codes.shape
+        t = lut.astype(np.float32)[codes]
+        if kind == "group_by_row":
+            s = scales.astype(np.float32).reshape(-1)[(np.arange(N) // max(group, 1)) % scales.size]
+            return t * s[:, None]
+        if kind == "sign":
+            return -original(codes, lut, scales, group)
+        if kind == "scale_dropped":
+            return t
+        raise AssertionError(kind)
+    return f
+
+
+@pytest.mark.parametrize("kind", ["group_by_row", "sign", "scale_dropped"])
+def test_planted_dequant_mistakes_are_caught(monkeypatch, kind):
+    c, T, s, x = workloads.small_case(4, "nf", 128, 2, 3, 256, seed=21)
+    ex = _exact(x, c, T, s, 128)
+    monkeypatch.setattr(lutq_ref, "dequant", _mutant_dequant(kind))
+    y, B = oracle.reference(x, c, T, s, 128)
+    err = max(abs(y[m, n] - float(ex[m][n])) for m in range(2) for n in range(3))
+    assert err > 1e-6
+
+
+def test_planted_transpose_is_caught():
+    c, T, s, x = workloads.small_case(4, "nf", 0, 2, 2, 128, seed=22)
+    ex = _exact(x, c, T, s, 0)
+    y, _ = oracle.reference(x, c, T, s, 0)
+    assert max(abs(y.T[m, n] - float(ex[m][n])) for m in range(2) for n in range(2)) > 1e-6
