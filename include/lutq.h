@@ -1,0 +1,170 @@
+/*
+ * lutq -- weight-only LUT-quantized matrix product on AMD MI355X (gfx950).
+ *
+ *   y[m, n] = sum_k x[m, k] * T[c[n, k]] * s[n, k / group]
+ *
+ * c are b-bit codes (b = 2, 3 or 4) that index a 2^b-entry fp16 lookup table
+ * T; s is one fp16 scale per `group` consecutive weights along K, or a single
+ * scale for the whole tensor (group == 0). The product is fused with the
+ * dequantization, so only the packed codes (plus scales) stream from HBM.
+ *
+ * Sources: "FLUTE: flexible lookup table engine" abstract (weight-only
+ * quantization with the dequantization fused into the matmul; offline
+ * restructuring of the quantized matrix to cut unpacking work; a vectorized,
+ * duplicated lookup table in on-chip memory; 3-bit and non-uniform tables;
+ * group size 128, batch below 32); "LogbQuant" abstract (logarithmic tables
+ * with an adjustable base; tensor-wise granularity); "BitMoD" abstract
+ * (rescaling per-group partial sums).
+ *
+ * Conventions for every entry point:
+ *  - Device pointers are HIP device memory owned by the caller; the library
+ *    never frees them. Host pointers are marked "host".
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *    Work is enqueued on it asynchronously; a return of LUTQ_OK means
+ *    "validated and enqueued". Device faults surface at the caller's next
+ *    synchronization, as with any HIP launch.
+ *  - On any error nothing is enqueued and outputs are untouched.
+ *  - fp16 values are passed as raw IEEE binary16 bit patterns (uint16_t).
+ *  - No C++ exception crosses this boundary.
+ */
+#ifndef LUTQ_H
+#define LUTQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ------------------------------------------------------ */
+enum {
+  LUTQ_OK = 0,
+  LUTQ_EINVAL = -1,      /* null pointer, negative size, bad option value   */
+  LUTQ_EBITS = -2,       /* bits not in {2, 3, 4}                           */
+  LUTQ_EGROUP = -3,      /* group not 0 and not a multiple of 128, or K is
+                            not a multiple of group (and of 128)            */
+  LUTQ_EALIGN = -4,      /* x or packed data not 16-byte aligned, or another
+                            pointer not 2-byte aligned                      */
+  LUTQ_EMISMATCH = -5,   /* N/K differ from the descriptor; bad magic or
+                            layout version                                  */
+  LUTQ_ESIZE = -6,       /* destination buffer too small                    */
+  LUTQ_EHIP = -7,        /* a HIP runtime call failed (see lutq_last_hip_error) */
+  LUTQ_EUNSUPPORTED = -8 /* a size beyond the limits below                  */
+};
+
+/* Limits: 0 <= M; 0 <= N <= 2^24; 0 <= K <= 2^20. M above 32 is processed in
+ * slices of 32 rows (the weights are streamed once per slice). */
+#define LUTQ_MAX_N (1 << 24)
+#define LUTQ_MAX_K (1 << 20)
+
+/* ---- packed weights ------------------------------------------------------
+ * Filled by lutq_repack. The layout ("wave-block", version 1) is the offline
+ * restructuring of the FLUTE abstract, redesigned for 64-lane wavefronts:
+ *
+ *   rows are cut into tiles of 16, K into chunks of 128 codes; chunk c of
+ *   tile t is one block of 64 lane slots x (4*bits) bytes, stored at byte
+ *   offset (t * (K/128) + c) * 256 * bits. Lane slot L = 16*q + r (q = 0..3,
+ *   r = 0..15) holds the 32 codes of row 16*t + r at
+ *   k = 128*c + 32*j + 8*q + e   (j = 0..3, e = 0..7).
+ *   Within a slot, code (j, e) pairs with (j, e^1) into a pair index:
+ *     bits=4: 4 dwords; dword j, byte e/2 = code(j,e even) | code(j,e odd)<<4
+ *     bits=2: 2 dwords; dword j/2, byte e/2, nibble j%2 =
+ *             code(j,e even) | code(j,e odd)<<2
+ *     bits=3: 3 dwords (lo0, lo1, hi); the low 2 bits of each code are laid
+ *             out as bits=2 in lo0/lo1; the high bits of pair (j, e/2) sit in
+ *             byte e/2 of hi at bit offset {4, 6, 0, 2}[j] as
+ *             hi(code e even) | hi(code e odd)<<1.
+ *   Rows past N in the last tile hold code 0.
+ * One 16-row block is one coalesced 64-lane load (1 KiB at bits=4).
+ */
+#define LUTQ_MAGIC 0x5154554Cu /* "LUTQ" */
+#define LUTQ_LAYOUT_VERSION 1u
+
+typedef struct lutq_packed {
+  uint32_t magic;   /* LUTQ_MAGIC                                          */
+  uint32_t version; /* LUTQ_LAYOUT_VERSION                                 */
+  int32_t N, K;     /* weight matrix is N x K (out x in)                   */
+  int32_t bits;     /* 2, 3 or 4                                           */
+  int32_t group;    /* 0 = one scale per tensor; else a multiple of 128
+                       that divides K                                      */
+  uint64_t nbytes;  /* bytes used at data (lutq_packed_bytes)              */
+  void* data;       /* device, caller-owned, 16-byte aligned               */
+} lutq_packed_t;
+
+/* Bytes lutq_repack writes for an N x K matrix: ceil(N/16)*16 * K * bits / 8.
+ * Returns 0 for invalid arguments (bits, group, K alignment) and for N == 0
+ * or K == 0. */
+size_t lutq_packed_bytes(int N, int K, int bits, int group);
+
+/* Offline restructuring (FLUTE abstract: restructure the quantized weight
+ * matrix offline so that unpacking needs few bit operations).
+ *   codes : device, uint8 [N, K] row-major, one code per byte; bits above
+ *           `bits` are ignored (masked).
+ *   dst   : device, >= lutq_packed_bytes(N, K, bits, group) bytes, 16-byte
+ *           aligned; must not overlap `codes`.
+ *   out   : host; filled with the descriptor (data = dst) on success.
+ * Errors: LUTQ_EINVAL, LUTQ_EBITS, LUTQ_EGROUP, LUTQ_EALIGN, LUTQ_ESIZE,
+ * LUTQ_EUNSUPPORTED, LUTQ_EHIP. N == 0 or K == 0 fills the descriptor
+ * (nbytes = 0) and enqueues nothing. */
+int lutq_repack(const uint8_t* codes, int N, int K, int bits, int group,
+                void* dst, size_t dst_bytes, lutq_packed_t* out, void* stream);
+
+/* Inverse of lutq_repack, for tests: writes uint8 codes [N, K] (device,
+ * row-major) from the packed layout. Errors as lutq_repack. */
+int lutq_unpack(const lutq_packed_t* packed, uint8_t* codes_out, void* stream);
+
+/* The fused LUT-dequantize + matmul (FLUTE abstract; per-group partial sums
+ * rescaled once per group as in the BitMoD abstract):
+ *   x      : device, fp16 [M, K] row-major, 16-byte aligned.
+ *   packed : host descriptor from lutq_repack (its data stays on device).
+ *   lut    : device, fp16 [2^bits].
+ *   scales : device, fp16 [N, K/group] row-major, or [1] when group == 0.
+ *   y      : device, fp16 [M, N] row-major (output; written, never read).
+ * Accumulation is fp32; y is rounded to nearest-even fp16. The table values
+ * are used unscaled inside a group and each group's fp32 partial sum is
+ * multiplied by its scale. Results are deterministic (no float atomics).
+ * M == 0 or N == 0: nothing to do (LUTQ_OK). K == 0: y is set to zero.
+ * Errors: LUTQ_EINVAL, LUTQ_EMISMATCH, LUTQ_EALIGN, LUTQ_EUNSUPPORTED,
+ * LUTQ_EHIP. Calls may run concurrently on different streams. */
+int lutq_matmul(const uint16_t* x, const lutq_packed_t* packed, const uint16_t* lut,
+                const uint16_t* scales, uint16_t* y, int M, int N, int K, void* stream);
+
+/* Path selection for lutq_matmul_ex. */
+enum {
+  LUTQ_PATH_AUTO = 0, /* by M: GEMV for small batches, MFMA above            */
+  LUTQ_PATH_GEMV = 1, /* VALU dot2 path (any M; slices of 8 rows)            */
+  LUTQ_PATH_MFMA = 2  /* fp16 MFMA path (any M; slices of 32 rows)           */
+};
+
+typedef struct lutq_options {
+  int32_t path;   /* LUTQ_PATH_*                                              */
+  int32_t ksplit; /* workgroups per 64-row block along K; 0 = automatic.
+                     Clamped to the number of 128-code chunks.               */
+  int32_t reserved[6]; /* must be zero                                        */
+} lutq_options_t;
+
+/* lutq_matmul with explicit options (host pointer; NULL = automatic). */
+int lutq_matmul_ex(const uint16_t* x, const lutq_packed_t* packed, const uint16_t* lut,
+                   const uint16_t* scales, uint16_t* y, int M, int N, int K,
+                   const lutq_options_t* opts, void* stream);
+
+/* The path and split lutq_matmul would choose (host-side heuristic only,
+ * no device work). Writes *path and *ksplit. */
+int lutq_plan(int M, int N, int K, int bits, int* path, int* ksplit);
+
+/* Static string for a status code. */
+const char* lutq_strerror(int status);
+
+/* The last HIP error code seen by this thread (hipError_t as int). */
+int lutq_last_hip_error(void);
+
+/* Frees the library's split-K scratch buffers (per device and stream). Call
+ * only when no lutq work is in flight. */
+void lutq_shutdown(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LUTQ_H */

@@ -1,0 +1,172 @@
+"""The C ABI on the CPU: the library loads, exports every declared symbol, and
+rejects bad arguments before any HIP call (so these run without a GPU).
+Also the numpy reading of the packed layout against hand-derived bytes."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import weight_only_lut_amd as lutq
+from weight_only_lut_amd import _lib
+
+from . import layout_spec
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lutq.h")
+
+OK, EINVAL, EBITS, EGROUP, EALIGN, EMISMATCH, ESIZE, EHIP, EUNSUP = 0, -1, -2, -3, -4, -5, -6, -7, -8
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return lutq.load_library()
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(lutq_[a-z_]+)\s*\(", src)))
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = _declared()
+    assert set(names) == set(_lib.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_strerror_covers_every_code(lib):
+    for c in (OK, EINVAL, EBITS, EGROUP, EALIGN, EMISMATCH, ESIZE, EHIP, EUNSUP):
+        assert lutq.strerror(c) != "unknown lutq status"
+    assert lutq.strerror(-99) == "unknown lutq status"
+
+
+def test_packed_bytes():
+    assert lutq.packed_bytes(14336, 4096, 4, 128) == 14336 * 4096 // 2
+    assert lutq.packed_bytes(4096, 14336, 3, 128) == 4096 * 14336 * 3 // 8
+    assert lutq.packed_bytes(1000, 256, 4, 128) == 1008 * 256 // 2  # rows padded to 16
+    assert lutq.packed_bytes(16, 128, 2, 0) == 16 * 128 // 4
+    for bad in [(16, 128, 5, 128), (16, 128, 1, 128), (16, 100, 4, 0), (16, 256, 4, 64),
+                (16, 384, 4, 256), (-1, 128, 4, 128), (0, 128, 4, 128)]:
+        assert lutq.packed_bytes(*bad) == 0, bad
+
+
+def _desc(N=64, K=256, bits=4, group=128, data=0x10000):
+    d = _lib.PackedDesc()
+    d.magic, d.version = _lib.LUTQ_MAGIC, _lib.LUTQ_LAYOUT_VERSION
+    d.N, d.K, d.bits, d.group = N, K, bits, group
+    d.nbytes = lutq.packed_bytes(N, K, bits, group)
+    d.data = data
+    return d
+
+
+def test_repack_validates_before_launching(lib):
+    out = _lib.PackedDesc()
+    P = ctypes.c_void_p
+    good = dict(codes=P(0x1000), N=64, K=256, bits=4, group=128, dst=P(0x20000), nb=1 << 20)
+
+    def call(**kw):
+        a = {**good, **kw}
+        return lib.lutq_repack(a["codes"], a["N"], a["K"], a["bits"], a["group"], a["dst"],
+                               a["nb"], ctypes.byref(out), None)
+
+    assert call(bits=5) == EBITS
+    assert call(bits=1) == EBITS
+    assert call(group=64) == EGROUP
+    assert call(K=200) == EGROUP
+    assert call(K=384, group=256) == EGROUP
+    assert call(N=-1) == EINVAL
+    assert call(N=1 << 25) == EUNSUP
+    assert call(codes=P(0)) == EINVAL
+    assert call(dst=P(0)) == EINVAL
+    assert call(dst=P(0x20008)) == EALIGN
+    assert call(nb=100) == ESIZE
+    assert call(codes=P(0x20000)) == EINVAL           # overlapping buffers
+    assert lib.lutq_repack(P(0x1000), 64, 256, 4, 128, P(0x20000), 1 << 20, None, None) == EINVAL
+    # empty matrix: descriptor filled, nothing enqueued
+    assert call(N=0) == OK and out.nbytes == 0 and out.N == 0 and out.magic == _lib.LUTQ_MAGIC
+
+
+def test_matmul_validates_before_launching(lib):
+    P = ctypes.c_void_p
+    d = _desc()
+    x, lut, sc, y = P(0x1000), P(0x2000), P(0x3000), P(0x4000)
+
+    def call(desc=d, M=1, N=64, K=256, x=x, lut=lut, sc=sc, y=y, opts=None):
+        return lib.lutq_matmul_ex(x, ctypes.byref(desc) if desc is not None else None, lut, sc, y,
+                                  M, N, K, opts, None)
+
+    assert call(desc=None) == EINVAL
+    bad = _desc(); bad.magic = 0
+    assert call(desc=bad) == EMISMATCH
+    bad = _desc(); bad.version = 2
+    assert call(desc=bad) == EMISMATCH
+    bad = _desc(); bad.nbytes += 1
+    assert call(desc=bad) == EMISMATCH
+    assert call(desc=_desc(data=0x10004)) == EALIGN
+    assert call(desc=_desc(data=0)) == EINVAL
+    assert call(N=65) == EMISMATCH
+    assert call(K=128) == EMISMATCH
+    assert call(M=-1) == EINVAL
+    assert call(x=P(0)) == EINVAL
+    assert call(y=P(0)) == EINVAL
+    assert call(x=P(0x1008)) == EALIGN
+    assert call(sc=P(0x3001)) == EALIGN
+    o = _lib.Options(); o.path = 7
+    assert call(opts=ctypes.byref(o)) == EINVAL
+    o = _lib.Options(); o.ksplit = -1
+    assert call(opts=ctypes.byref(o)) == EINVAL
+    o = _lib.Options(); o.reserved[3] = 1
+    assert call(opts=ctypes.byref(o)) == EINVAL
+    # nothing to do: M == 0 (no HIP call is made)
+    assert call(M=0) == OK
+    assert lib.lutq_unpack(None, P(0x1000), None) == EINVAL
+
+
+def test_plan_switches_paths_by_batch():
+    assert lutq.plan(1, 14336, 4096, 4)[0] == "gemv"
+    assert lutq.plan(32, 28672, 8192, 4)[0] == "mfma"
+    path, ks = lutq.plan(1, 1024, 1024, 4)
+    assert 1 <= ks <= 8
+
+
+# -- the layout as documented in include/lutq.h -------------------------------
+
+def test_layout_hand_example_bits4():
+    # one row, K = 128, code k = k % 16. Slot 0 (q = 0, r = 0), k-step j covers
+    # k = 32 j + 0..7 -> codes 0..7 -> bytes 0x10 0x32 0x54 0x76.
+    codes = (np.arange(128) % 16).astype(np.uint8)[None]
+    b = layout_spec.encode(codes, 4)
+    assert b.size == 16 * 128 // 2
+    assert bytes(b[:16]) == bytes([0x10, 0x32, 0x54, 0x76] * 4)
+    # slot 16 (q = 1, r = 0): k = 32 j + 8..15 -> codes 8..15
+    assert bytes(b[16 * 16:16 * 16 + 4]) == bytes([0x98, 0xBA, 0xDC, 0xFE])
+    # slot 1 (r = 1) is a padding row
+    assert not np.any(b[16:32])
+
+
+def test_layout_hand_example_bits3():
+    # one row, K = 128, every code = 5 (binary 101: low bits 01, high bit 1)
+    codes = np.full((1, 128), 5, np.uint8)
+    w = layout_spec.encode(codes, 3)[:12].view("<u4")
+    # low planes: each nibble = 01 | 01 << 2 = 0x5, so every byte 0x55
+    assert w[0] == 0x55555555 and w[1] == 0x55555555
+    # high pairs (1 | 1 << 1 = 3) at bit offsets 4, 6, 0, 2 of every byte
+    assert w[2] == 0xFFFFFFFF
+    codes = np.zeros((1, 128), np.uint8)
+    codes[0, 32 * 1 + 2] = 4  # k-step j = 1, e = 2 (pair 1, even): high bit at byte 1, bit 6
+    w = layout_spec.encode(codes, 3)[:12].view("<u4")
+    assert w[0] == 0 and w[1] == 0 and w[2] == 1 << (8 + 6)
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+@pytest.mark.parametrize("N,K", [(1, 128), (37, 384), (64, 256), (100, 1024)])
+def test_layout_encode_decode_roundtrip(bits, N, K):
+    from synth import draw
+    c = draw.integers((N, K), 1 << bits, (31, bits, N, K))
+    b = layout_spec.encode(c, bits)
+    assert b.size == -(-N // 16) * 16 * K * bits // 8
+    assert np.array_equal(layout_spec.decode(b, N, K, bits), c)

@@ -1,0 +1,24 @@
+"""lutq: weight-only LUT-quantized matmul for AMD MI355X (gfx950).
+
+The compute lives in hand-written HIP kernels behind the C ABI of
+``liblutq.so`` (declared in ``include/lutq.h``); this package is a thin
+ctypes binding with the same names. PyTorch supplies device memory and the
+current stream only. There is no CPU fallback: if the library is missing or
+no GPU is present, the calls raise.
+"""
+
+from ._lib import (  # noqa: F401
+    LutqError,
+    Packed,
+    PATH_AUTO,
+    PATH_GEMV,
+    PATH_MFMA,
+    library_path,
+    load_library,
+    matmul,
+    packed_bytes,
+    plan,
+    repack,
+    strerror,
+    unpack,
+)

@@ -1,0 +1,189 @@
+"""ctypes binding of liblutq.so (argument marshalling only).
+
+Every function here forwards to the C entry point of the same name; tensors
+are passed as raw device pointers and the stream is PyTorch's current one.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+PATH_AUTO, PATH_GEMV, PATH_MFMA = 0, 1, 2
+_PATHS = {"auto": PATH_AUTO, "gemv": PATH_GEMV, "mfma": PATH_MFMA}
+
+LUTQ_MAGIC = 0x5154554C
+LUTQ_LAYOUT_VERSION = 1
+
+# every symbol include/lutq.h declares
+EXPORTS = (
+    "lutq_packed_bytes", "lutq_repack", "lutq_unpack", "lutq_matmul", "lutq_matmul_ex",
+    "lutq_plan", "lutq_strerror", "lutq_last_hip_error", "lutq_shutdown",
+)
+
+
+class PackedDesc(ctypes.Structure):
+    _fields_ = [
+        ("magic", ctypes.c_uint32), ("version", ctypes.c_uint32),
+        ("N", ctypes.c_int32), ("K", ctypes.c_int32),
+        ("bits", ctypes.c_int32), ("group", ctypes.c_int32),
+        ("nbytes", ctypes.c_uint64), ("data", ctypes.c_void_p),
+    ]
+
+
+class Options(ctypes.Structure):
+    _fields_ = [("path", ctypes.c_int32), ("ksplit", ctypes.c_int32),
+                ("reserved", ctypes.c_int32 * 6)]
+
+
+class LutqError(RuntimeError):
+    def __init__(self, code: int, where: str = ""):
+        self.code = code
+        msg = strerror(code)
+        if code == -7:  # LUTQ_EHIP
+            msg += f" (hipError {_lib().lutq_last_hip_error()})"
+        super().__init__(f"{where}: lutq error {code}: {msg}" if where else f"lutq error {code}: {msg}")
+
+
+_LIB = None
+
+
+def library_path() -> str:
+    return os.environ.get("LUTQ_LIBRARY", os.path.join(HERE, "liblutq.so"))
+
+
+def load_library():
+    """Load liblutq.so (built by ``weight_only_lut_amd.build``); raise if missing."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    path = library_path()
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} not found: build it with `python -m weight_only_lut_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, i32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    lib.lutq_packed_bytes.argtypes = [i32, i32, i32, i32]
+    lib.lutq_packed_bytes.restype = sz
+    lib.lutq_repack.argtypes = [vp, i32, i32, i32, i32, vp, sz, ctypes.POINTER(PackedDesc), vp]
+    lib.lutq_repack.restype = i32
+    lib.lutq_unpack.argtypes = [ctypes.POINTER(PackedDesc), vp, vp]
+    lib.lutq_unpack.restype = i32
+    lib.lutq_matmul.argtypes = [vp, ctypes.POINTER(PackedDesc), vp, vp, vp, i32, i32, i32, vp]
+    lib.lutq_matmul.restype = i32
+    lib.lutq_matmul_ex.argtypes = [vp, ctypes.POINTER(PackedDesc), vp, vp, vp, i32, i32, i32,
+                                   ctypes.POINTER(Options), vp]
+    lib.lutq_matmul_ex.restype = i32
+    lib.lutq_plan.argtypes = [i32, i32, i32, i32, ctypes.POINTER(i32), ctypes.POINTER(i32)]
+    lib.lutq_plan.restype = i32
+    lib.lutq_strerror.argtypes = [i32]
+    lib.lutq_strerror.restype = ctypes.c_char_p
+    lib.lutq_last_hip_error.argtypes = []
+    lib.lutq_last_hip_error.restype = i32
+    lib.lutq_shutdown.argtypes = []
+    lib.lutq_shutdown.restype = None
+    _LIB = lib
+    return lib
+
+
+def _lib():
+    return load_library()
+
+
+def strerror(code: int) -> str:
+    return _lib().lutq_strerror(code).decode()
+
+
+def packed_bytes(N: int, K: int, bits: int, group: int) -> int:
+    return int(_lib().lutq_packed_bytes(N, K, bits, group))
+
+
+def plan(M: int, N: int, K: int, bits: int):
+    """(path, ksplit) that lutq_matmul picks for this shape."""
+    path, ks = ctypes.c_int(0), ctypes.c_int(0)
+    rc = _lib().lutq_plan(M, N, K, bits, ctypes.byref(path), ctypes.byref(ks))
+    if rc:
+        raise LutqError(rc, "lutq_plan")
+    return {0: "auto", 1: "gemv", 2: "mfma"}[path.value], ks.value
+
+
+def _stream(device):
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _need_cuda(t, name, dtype):
+    import torch
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a CUDA (HIP) tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+class Packed:
+    """Packed weights: the device buffer plus its host descriptor."""
+
+    def __init__(self, data, desc: PackedDesc):
+        self.data = data          # torch uint8 tensor owning the device bytes
+        self.desc = desc
+
+    N = property(lambda self: self.desc.N)
+    K = property(lambda self: self.desc.K)
+    bits = property(lambda self: self.desc.bits)
+    group = property(lambda self: self.desc.group)
+    nbytes = property(lambda self: self.desc.nbytes)
+
+
+def repack(codes, bits: int, group: int) -> Packed:
+    """lutq_repack: uint8 codes [N, K] on the GPU -> Packed (wave-block layout)."""
+    import torch
+    _need_cuda(codes, "codes", torch.uint8)
+    N, K = codes.shape
+    nbytes = packed_bytes(N, K, bits, group)
+    dst = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=codes.device)
+    desc = PackedDesc()
+    rc = _lib().lutq_repack(_ptr(codes), N, K, bits, group, _ptr(dst), dst.numel(),
+                            ctypes.byref(desc), _stream(codes.device))
+    if rc:
+        raise LutqError(rc, "lutq_repack")
+    return Packed(dst, desc)
+
+
+def unpack(p: Packed):
+    """lutq_unpack: Packed -> uint8 codes [N, K] on the GPU."""
+    import torch
+    out = torch.empty((p.N, p.K), dtype=torch.uint8, device=p.data.device)
+    rc = _lib().lutq_unpack(ctypes.byref(p.desc), _ptr(out), _stream(p.data.device))
+    if rc:
+        raise LutqError(rc, "lutq_unpack")
+    return out
+
+
+def matmul(x, p: Packed, lut, scales, *, path: str = "auto", ksplit: int = 0, out=None):
+    """lutq_matmul_ex: y[M, N] = x[M, K] . dequant(p, lut, scales)^T, fp16 out."""
+    import torch
+    _need_cuda(x, "x", torch.float16)
+    _need_cuda(lut, "lut", torch.float16)
+    _need_cuda(scales, "scales", torch.float16)
+    M, K = x.shape
+    if out is None:
+        out = torch.empty((M, p.N), dtype=torch.float16, device=x.device)
+    else:
+        _need_cuda(out, "out", torch.float16)
+        if tuple(out.shape) != (M, p.N):
+            raise ValueError("out has the wrong shape")
+    opts = Options()
+    opts.path = _PATHS[path]
+    opts.ksplit = ksplit
+    rc = _lib().lutq_matmul_ex(_ptr(x), ctypes.byref(p.desc), _ptr(lut), _ptr(scales), _ptr(out),
+                               M, p.N, K, ctypes.byref(opts), _stream(x.device))
+    if rc:
+        raise LutqError(rc, "lutq_matmul")
+    return out

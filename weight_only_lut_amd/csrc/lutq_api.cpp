@@ -1,0 +1,286 @@
+// C-ABI host side of lutq: argument validation, planning, split-K scratch and
+// kernel launches. Every public function validates before touching the GPU,
+// so argument errors are reported without any HIP call.
+#include <hip/hip_runtime.h>
+
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <utility>
+
+#include "../../include/lutq.h"
+#include "lutq_internal.h"
+
+namespace {
+
+thread_local int g_last_hip = 0;
+
+int hip_fail(hipError_t e) {
+  g_last_hip = (int)e;
+  return LUTQ_EHIP;
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+int check_bits_group(int K, int bits, int group) {
+  if (bits < 2 || bits > 4) return LUTQ_EBITS;
+  if (group < 0) return LUTQ_EGROUP;
+  if (K % lutq::kChunk) return LUTQ_EGROUP;
+  if (group != 0 && (group % lutq::kChunk || K % group)) return LUTQ_EGROUP;
+  return LUTQ_OK;
+}
+
+int check_sizes(int N, int K) {
+  if (N < 0 || K < 0) return LUTQ_EINVAL;
+  if (N > LUTQ_MAX_N || K > LUTQ_MAX_K) return LUTQ_EUNSUPPORTED;
+  return LUTQ_OK;
+}
+
+int check_desc(const lutq_packed_t* p) {
+  if (!p) return LUTQ_EINVAL;
+  if (p->magic != LUTQ_MAGIC || p->version != LUTQ_LAYOUT_VERSION) return LUTQ_EMISMATCH;
+  int rc = check_sizes(p->N, p->K);
+  if (rc) return rc;
+  rc = check_bits_group(p->K, p->bits, p->group);
+  if (rc) return rc;
+  if (p->nbytes != lutq_packed_bytes(p->N, p->K, p->bits, p->group)) return LUTQ_EMISMATCH;
+  if (p->nbytes && !p->data) return LUTQ_EINVAL;
+  if (!aligned(p->data, 16)) return LUTQ_EALIGN;
+  return LUTQ_OK;
+}
+
+// Split-K scratch: one buffer per (device, stream), allocated on first need
+// and kept until lutq_shutdown. Counters start at zero (hipMemset at
+// allocation) and every launch leaves them at zero.
+struct Scratch {
+  void* base = nullptr;
+  size_t bytes = 0;
+};
+std::mutex g_mu;
+std::map<std::pair<int, void*>, Scratch> g_scratch;
+constexpr size_t kCounterBytes = 64 * 1024;  // up to 16384 row blocks
+
+int get_scratch(void* stream, size_t partial_bytes, float** partial, uint32_t** counters) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e);
+  std::lock_guard<std::mutex> lk(g_mu);
+  Scratch& s = g_scratch[{dev, stream}];
+  const size_t need = kCounterBytes + partial_bytes;
+  if (s.bytes < need) {
+    if (s.base) {
+      // the old buffer may still be in use by work queued on this stream
+      e = hipStreamSynchronize((hipStream_t)stream);
+      if (e != hipSuccess) return hip_fail(e);
+      (void)hipFree(s.base);
+      s.base = nullptr;
+      s.bytes = 0;
+    }
+    size_t bytes = need < (8u << 20) ? (8u << 20) : need;
+    e = hipMalloc(&s.base, bytes);
+    if (e != hipSuccess) return hip_fail(e);
+    e = hipMemset(s.base, 0, kCounterBytes);
+    if (e != hipSuccess) return hip_fail(e);
+    s.bytes = bytes;
+  }
+  *counters = reinterpret_cast<uint32_t*>(s.base);
+  *partial = reinterpret_cast<float*>(reinterpret_cast<char*>(s.base) + kCounterBytes);
+  return LUTQ_OK;
+}
+
+int cu_count() {
+  static int n = 0;
+  if (n == 0) {
+    int dev = 0, v = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
+      n = v;
+    else
+      n = 256;
+  }
+  return n;
+}
+
+// Batch rows above which the automatic plan switches from GEMV to MFMA.
+constexpr int kAutoGemvMaxM = 4;
+
+void plan(int M, int N, int K, int cus, int* path, int* ksplit) {
+  const int ntiles = (N + lutq::kTileRows - 1) / lutq::kTileRows;
+  const int nrb = lutq::row_blocks(ntiles);
+  const int nchunks = K / lutq::kChunk;
+  if (*path == LUTQ_PATH_AUTO) *path = (M <= kAutoGemvMaxM) ? LUTQ_PATH_GEMV : LUTQ_PATH_MFMA;
+  if (*ksplit <= 0) {
+    // keep every workgroup resident (two per CU: 64 KiB of LDS each) and
+    // spread small matrices over the whole chip
+    int k = (2 * cus) / (nrb > 0 ? nrb : 1);
+    if (k < 1) k = 1;
+    *ksplit = k;
+  }
+  if (*ksplit > nchunks) *ksplit = nchunks > 0 ? nchunks : 1;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t lutq_packed_bytes(int N, int K, int bits, int group) {
+  if (check_sizes(N, K) || check_bits_group(K, bits, group)) return 0;
+  if (N == 0 || K == 0) return 0;
+  const size_t ntiles = (size_t)(N + lutq::kTileRows - 1) / lutq::kTileRows;
+  return ntiles * lutq::kTileRows * (size_t)K * (size_t)bits / 8;
+}
+
+int lutq_repack(const uint8_t* codes, int N, int K, int bits, int group, void* dst,
+                size_t dst_bytes, lutq_packed_t* out, void* stream) {
+  if (!out) return LUTQ_EINVAL;
+  int rc = check_sizes(N, K);
+  if (rc) return rc;
+  rc = check_bits_group(K, bits, group);
+  if (rc) return rc;
+  const size_t need = lutq_packed_bytes(N, K, bits, group);
+  if (need) {
+    if (!codes || !dst) return LUTQ_EINVAL;
+    if (!aligned(dst, 16)) return LUTQ_EALIGN;
+    if (dst_bytes < need) return LUTQ_ESIZE;
+    const char* a = (const char*)codes;
+    const char* b = (const char*)dst;
+    if (a < b + need && b < a + (size_t)N * K) return LUTQ_EINVAL;  // overlap
+    hipError_t e = lutq::launch_repack(codes, (uint8_t*)dst, N, K, bits, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e);
+  }
+  lutq_packed_t d;
+  std::memset(&d, 0, sizeof d);
+  d.magic = LUTQ_MAGIC;
+  d.version = LUTQ_LAYOUT_VERSION;
+  d.N = N;
+  d.K = K;
+  d.bits = bits;
+  d.group = group;
+  d.nbytes = need;
+  d.data = need ? dst : nullptr;
+  *out = d;
+  return LUTQ_OK;
+}
+
+int lutq_unpack(const lutq_packed_t* packed, uint8_t* codes_out, void* stream) {
+  int rc = check_desc(packed);
+  if (rc) return rc;
+  if (packed->nbytes == 0) return LUTQ_OK;
+  if (!codes_out) return LUTQ_EINVAL;
+  hipError_t e = lutq::launch_unpack((const uint8_t*)packed->data, codes_out, packed->N, packed->K,
+                                     packed->bits, (hipStream_t)stream);
+  return e == hipSuccess ? LUTQ_OK : hip_fail(e);
+}
+
+int lutq_plan(int M, int N, int K, int bits, int* path, int* ksplit) {
+  if (!path || !ksplit || M < 0) return LUTQ_EINVAL;
+  int rc = check_sizes(N, K);
+  if (rc) return rc;
+  if (bits < 2 || bits > 4) return LUTQ_EBITS;
+  if (K % lutq::kChunk) return LUTQ_EGROUP;
+  *path = LUTQ_PATH_AUTO;
+  *ksplit = 0;
+  plan(M, N, K, cu_count(), path, ksplit);
+  return LUTQ_OK;
+}
+
+int lutq_matmul_ex(const uint16_t* x, const lutq_packed_t* packed, const uint16_t* lut,
+                   const uint16_t* scales, uint16_t* y, int M, int N, int K,
+                   const lutq_options_t* opts, void* stream) {
+  int rc = check_desc(packed);
+  if (rc) return rc;
+  if (M < 0 || N < 0 || K < 0) return LUTQ_EINVAL;
+  if (N != packed->N || K != packed->K) return LUTQ_EMISMATCH;
+  int path = LUTQ_PATH_AUTO, ksplit = 0;
+  if (opts) {
+    for (int i = 0; i < 6; ++i)
+      if (opts->reserved[i]) return LUTQ_EINVAL;
+    if (opts->path < LUTQ_PATH_AUTO || opts->path > LUTQ_PATH_MFMA || opts->ksplit < 0)
+      return LUTQ_EINVAL;
+    path = opts->path;
+    ksplit = opts->ksplit;
+  }
+  if (M == 0 || N == 0) return LUTQ_OK;
+  if (!y) return LUTQ_EINVAL;
+  if (!aligned(y, 2)) return LUTQ_EALIGN;
+  hipStream_t s = (hipStream_t)stream;
+  if (K == 0) {  // the empty sum; x, lut and scales are not read
+    hipError_t e = lutq::launch_fill_u16(y, (long long)M * N, 0, s);
+    return e == hipSuccess ? LUTQ_OK : hip_fail(e);
+  }
+  if (!x || !lut || !scales) return LUTQ_EINVAL;
+  if (!aligned(x, 16)) return LUTQ_EALIGN;
+  if (!aligned(lut, 2) || !aligned(scales, 2)) return LUTQ_EALIGN;
+
+  plan(M, N, K, cu_count(), &path, &ksplit);
+  const int rows_per_launch = (path == LUTQ_PATH_MFMA) ? lutq::kMfmaMaxRows : lutq::kGemvMaxRows;
+
+  lutq::MatmulParams p;
+  std::memset(&p, 0, sizeof p);
+  p.packed = (const uint8_t*)packed->data;
+  p.lut = lut;
+  p.scales = scales;
+  p.N = N;
+  p.K = K;
+  p.group = packed->group;
+  p.nchunks = K / lutq::kChunk;
+  p.ntiles = (N + lutq::kTileRows - 1) / lutq::kTileRows;
+  p.ksplit = ksplit;
+  p.cps = (p.nchunks + ksplit - 1) / ksplit;
+  if (ksplit > 1) {
+    const size_t nrb = (size_t)lutq::row_blocks(p.ntiles);
+    if (nrb * sizeof(uint32_t) > kCounterBytes) return LUTQ_EUNSUPPORTED;
+    const size_t pbytes = nrb * (size_t)ksplit * lutq::kMfmaMaxRows *
+                          (lutq::kTilesPerWg * lutq::kTileRows) * sizeof(float);
+    rc = get_scratch(stream, pbytes, &p.partial, &p.counters);
+    if (rc) return rc;
+  }
+  const int bits = packed->bits;
+  for (int m0 = 0; m0 < M; m0 += rows_per_launch) {
+    p.M = (M - m0) < rows_per_launch ? (M - m0) : rows_per_launch;
+    p.x = x + (size_t)m0 * K;
+    p.y = y + (size_t)m0 * N;
+    hipError_t e = lutq::launch_matmul(p, bits, path == LUTQ_PATH_MFMA ? lutq::kPathMfma
+                                                                       : lutq::kPathGemv, s);
+    if (e != hipSuccess) return hip_fail(e);
+  }
+  return LUTQ_OK;
+}
+
+int lutq_matmul(const uint16_t* x, const lutq_packed_t* packed, const uint16_t* lut,
+                const uint16_t* scales, uint16_t* y, int M, int N, int K, void* stream) {
+  return lutq_matmul_ex(x, packed, lut, scales, y, M, N, K, nullptr, stream);
+}
+
+const char* lutq_strerror(int status) {
+  switch (status) {
+    case LUTQ_OK: return "success";
+    case LUTQ_EINVAL: return "invalid argument (null pointer, negative size or bad option)";
+    case LUTQ_EBITS: return "bits must be 2, 3 or 4";
+    case LUTQ_EGROUP: return "group must be 0 or a multiple of 128 dividing K, and K a multiple of 128";
+    case LUTQ_EALIGN: return "misaligned pointer (x and packed data need 16 bytes, others 2)";
+    case LUTQ_EMISMATCH: return "shape or layout does not match the packed descriptor";
+    case LUTQ_ESIZE: return "destination buffer too small";
+    case LUTQ_EHIP: return "HIP runtime error";
+    case LUTQ_EUNSUPPORTED: return "size beyond the supported limits";
+    default: return "unknown lutq status";
+  }
+}
+
+int lutq_last_hip_error(void) { return g_last_hip; }
+
+void lutq_shutdown(void) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  for (auto& kv : g_scratch) {
+    if (kv.second.base) {
+      int cur = 0;
+      (void)hipGetDevice(&cur);
+      (void)hipSetDevice(kv.first.first);
+      (void)hipFree(kv.second.base);
+      (void)hipSetDevice(cur);
+    }
+  }
+  g_scratch.clear();
+}
+
+}  // extern "C"

@@ -1,0 +1,168 @@
+// Device-side building blocks shared by the lutq kernels (gfx950 only).
+//
+// Terms used throughout:
+//  tile   : 16 consecutive weight rows (output features n).
+//  chunk  : 128 consecutive codes along K.
+//  block  : one (tile, chunk) pair = 64 lane slots x (4*BITS) bytes, the unit
+//           that one wavefront loads with one coalesced load per lane.
+//  slot L : L = 16*q + r holds row 16*t + r, codes k = 128*c + 32*j + 8*q + e
+//           (j = 0..3 "k-step", e = 0..7).
+//  pair table: 256 entries of two fp16 values (T[c_even], T[c_odd]) indexed
+//           by a byte assembled from two codes, stored 64 times in LDS so
+//           that lane L always reads copy L: entry (idx, copy) lives at byte
+//           address (idx << 8) | (copy << 2), which spreads the 64 lanes of a
+//           lookup over 64 distinct banks whatever the codes are (FLUTE
+//           abstract: a vectorized, duplicated table against shared-memory
+//           bandwidth limits).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lutq {
+
+constexpr int kTileRows = 16;
+constexpr int kChunk = 128;
+constexpr int kWave = 64;
+constexpr int kPairEntries = 256;
+constexpr int kCopies = 64;
+constexpr int kTableWords = kPairEntries * kCopies;  // 16384 dwords = 64 KiB
+
+typedef _Float16 f16;
+typedef f16 f16x2 __attribute__((ext_vector_type(2)));
+typedef f16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Bytes of one lane slot and number of dwords it spans.
+template <int BITS> struct Slot {
+  static constexpr int kBytes = 4 * BITS;
+  static constexpr int kDwords = BITS;
+};
+
+// Codes of one lane slot in registers.
+template <int BITS> struct SlotRegs { uint32_t d[BITS]; };
+
+template <int BITS>
+__device__ __forceinline__ SlotRegs<BITS> load_slot(const uint8_t* p) {
+  SlotRegs<BITS> r;
+  if constexpr (BITS == 4) {
+    u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    r.d[0] = v.x; r.d[1] = v.y; r.d[2] = v.z; r.d[3] = v.w;
+  } else if constexpr (BITS == 3) {
+    u32x3 v = __builtin_nontemporal_load(reinterpret_cast<const u32x3*>(p));
+    r.d[0] = v.x; r.d[1] = v.y; r.d[2] = v.z;
+  } else {
+    u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+    r.d[0] = v.x; r.d[1] = v.y;
+  }
+  return r;
+}
+
+// The four pair-index bytes of k-step j (one byte per pair e/2 = 0..3).
+// Only the bits a table index uses are meaningful; the pair table repeats its
+// entries over the unused high bits, so no masking is needed here.
+template <int BITS>
+__device__ __forceinline__ uint32_t step_indices(const SlotRegs<BITS>& s, int j) {
+  if constexpr (BITS == 4) {
+    return s.d[j];
+  } else if constexpr (BITS == 2) {
+    const uint32_t w = s.d[j >> 1];
+    return (j & 1) ? (w >> 4) : w;
+  } else {
+    // low 2-bit planes as nibbles (as BITS == 2), high bits from word 2
+    const uint32_t lo = s.d[j >> 1];
+    const uint32_t l = (j & 1) ? (lo >> 4) : lo;
+    const uint32_t h = s.d[2];
+    uint32_t hs;
+    switch (j) {
+      case 0: hs = h; break;
+      case 1: hs = h >> 2; break;
+      case 2: hs = h << 4; break;
+      default: hs = h << 2; break;
+    }
+    // bits 0-3 of each byte from the low planes, bits 4-7 from the high plane
+    return (l & 0x0F0F0F0Fu) | (hs & 0xF0F0F0F0u);  // one v_bfi_b32
+  }
+}
+
+// LDS byte address of pair-table entry (byte `i` of `idx4`, copy = lane):
+// v_perm puts the index byte in bits 8-15 and the lane byte (lane*4) in bits
+// 0-7 -- one VALU op per lookup.
+__device__ __forceinline__ uint32_t pair_addr(uint32_t idx4, uint32_t lane_byte, int i) {
+  const uint32_t sel = 0x0C0C0000u | ((4u + (uint32_t)i) << 8);
+  return __builtin_amdgcn_perm(idx4, lane_byte, sel);
+}
+
+__device__ __forceinline__ uint32_t lds_load(const uint32_t* table, uint32_t byte_addr) {
+  return *reinterpret_cast<const uint32_t*>(reinterpret_cast<const char*>(table) + byte_addr);
+}
+
+// Decode the two codes of a pair index for table building.
+template <int BITS>
+__device__ __forceinline__ void pair_codes(uint32_t idx, uint32_t& c0, uint32_t& c1) {
+  if constexpr (BITS == 4) {
+    c0 = idx & 15u; c1 = (idx >> 4) & 15u;
+  } else if constexpr (BITS == 2) {
+    c0 = idx & 3u; c1 = (idx >> 2) & 3u;
+  } else {
+    c0 = (idx & 3u) | (((idx >> 4) & 1u) << 2);
+    c1 = ((idx >> 2) & 3u) | (((idx >> 5) & 1u) << 2);
+  }
+}
+
+// Fill the duplicated pair table. Every thread of the block takes part; the
+// caller issues a barrier before the first lookup.
+template <int BITS>
+__device__ __forceinline__ void build_pair_table(uint32_t* table, const uint16_t* lut,
+                                                 int tid, int nthreads) {
+  // thread -> (entry, run of copies); each run is written as 16-byte stores
+  const int runs_per_entry = (kPairEntries * kCopies / 4) / kPairEntries;  // 16 quads
+  for (int w = tid; w < kPairEntries * runs_per_entry; w += nthreads) {
+    const uint32_t idx = (uint32_t)w / runs_per_entry;
+    const int run = w % runs_per_entry;
+    uint32_t c0, c1;
+    pair_codes<BITS>(idx, c0, c1);
+    const uint32_t v = (uint32_t)lut[c0] | ((uint32_t)lut[c1] << 16);
+    u32x4 q = {v, v, v, v};
+    *reinterpret_cast<u32x4*>(table + idx * kCopies + run * 4) = q;
+  }
+}
+
+// DPP row_newbcast:n -- every lane of each 16-lane row reads lane n of that
+// row. `n` must fold to a constant after unrolling.
+__device__ __forceinline__ uint32_t row_newbcast(uint32_t v, int n) {
+  switch (n) {
+    case 0: return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x150, 0xF, 0xF, false);
+    case 1: return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x151, 0xF, 0xF, false);
+    case 2: return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x152, 0xF, 0xF, false);
+    case 3: return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x153, 0xF, 0xF, false);
+    case 4: return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x154, 0xF, 0xF, false);
+    case 5: return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x155, 0xF, 0xF, false);
+    case 6: return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x156, 0xF, 0xF, false);
+    case 7: return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x157, 0xF, 0xF, false);
+    case 8: return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x158, 0xF, 0xF, false);
+    case 9: return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x159, 0xF, 0xF, false);
+    case 10: return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x15a, 0xF, 0xF, false);
+    case 11: return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x15b, 0xF, 0xF, false);
+    case 12: return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x15c, 0xF, 0xF, false);
+    case 13: return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x15d, 0xF, 0xF, false);
+    case 14: return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x15e, 0xF, 0xF, false);
+    case 15: return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x15f, 0xF, 0xF, false);
+    default: return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x15f, 0xF, 0xF, false);
+  }
+}
+
+__device__ __forceinline__ f16x2 as_f16x2(uint32_t v) { return __builtin_bit_cast(f16x2, v); }
+
+__device__ __forceinline__ uint16_t f32_to_f16_bits(float f) {
+  return __builtin_bit_cast(uint16_t, (f16)f);  // round to nearest even
+}
+
+__device__ __forceinline__ float f16_bits_to_f32(uint16_t h) {
+  return (float)__builtin_bit_cast(f16, h);
+}
+
+}  // namespace lutq

@@ -1,0 +1,55 @@
+// Internal interface between the C-ABI host code and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <algorithm>
+
+#include "lutq_device.h"
+
+namespace lutq {
+
+// Fixed workgroup shape of the matmul kernels: 8 waves split the K range of
+// a block of `tiles_per_wg` 16-row tiles.
+constexpr int kWaves = 8;
+constexpr int kThreads = kWaves * kWave;
+
+struct MatmulParams {
+  const uint16_t* x;      // fp16 [M, K] (this launch's slice of rows)
+  const uint8_t* packed;  // wave-block layout
+  const uint16_t* lut;    // fp16 [2^bits]
+  const uint16_t* scales; // fp16 [N, K/group] or [1]
+  uint16_t* y;            // fp16 [M, N] (this launch's slice of rows)
+  float* partial;         // split-K partial sums, or null when ksplit == 1
+  uint32_t* counters;     // split-K arrival counters (zero between launches)
+  int M;                  // rows of x in this launch (<= the kernel's row capacity)
+  int N, K, group;        // group == 0: one scale per tensor
+  int nchunks, ntiles;
+  int ksplit;             // workgroups per row block along K
+  int cps;                // chunks per split
+};
+
+enum Path { kPathGemv = 1, kPathMfma = 2 };
+
+// Rows of x one launch of each path handles.
+constexpr int kGemvMaxRows = 8;
+constexpr int kMfmaMaxRows = 32;
+
+// Tiles (16 rows each) per workgroup.
+constexpr int kTilesPerWg = 4;
+
+// Number of 64-row blocks for N rows.
+inline int row_blocks(int ntiles) { return (ntiles + kTilesPerWg - 1) / kTilesPerWg; }
+
+hipError_t launch_repack(const uint8_t* codes, uint8_t* dst, int N, int K, int bits,
+                         hipStream_t s);
+hipError_t launch_unpack(const uint8_t* src, uint8_t* codes, int N, int K, int bits,
+                         hipStream_t s);
+hipError_t launch_fill_u16(uint16_t* p, long long n, uint16_t v, hipStream_t s);
+
+// One launch over rows [0, p.M) of x; p.M <= kGemvMaxRows (GEMV) or
+// kMfmaMaxRows (MFMA).
+hipError_t launch_matmul(const MatmulParams& p, int bits, int path, hipStream_t s);
+
+}  // namespace lutq
