@@ -1,0 +1,299 @@
+"""Benchmark of the fused LUT-dequantize + matmul on one MI355X.
+
+Headline step: one lutq_matmul call on the Llama-3-8B MLP up-projection shape
+(N = 14336, K = 4096), 4-bit uniform (INT) table, one fp16 scale per 128
+weights, batch M = 1 -- the HBM-bound GEMV. Weights are "cold": every call
+reads a different copy of the packed matrix, and the copies together exceed
+the 256 MB Infinity Cache, so the bytes come from HBM. Also measured in the
+same run (reported beside the headline):
+
+- the same call with one warm copy (Infinity-Cache resident);
+- batch 32 on the Llama-70B-shaped log table (N = 28672, K = 8192,
+  tensor-wise scale): TFLOP/s against the fp16 MFMA peak;
+- the CPU oracle on a bounded sample of the headline workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--sweep]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 MFMA, published
+CACHE_BYTES = 256 << 20        # Infinity Cache (MALL)
+COLD_SET_BYTES = 2 * CACHE_BYTES
+
+
+def algorithmic_bytes(M, N, K, bits, group):
+    """Bytes the method must move: packed codes + scales + x + y + table."""
+    scales = N * (K // group) * 2 if group else 2
+    return N * K * bits // 8 + scales + M * K * 2 + M * N * 2 + (1 << bits) * 2
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+class Case:
+    """Device-resident inputs of one workload matrix at batch M."""
+
+    def __init__(self, lutq, torch, wname, mat, M, cold=True):
+        import numpy as np
+
+        from synth import workloads
+        w = workloads.WORKLOADS[wname]
+        self.w, self.M = w, M
+        _, m = w.matrix(mat)
+        self.N, self.K = m.N, m.K
+        t0 = time.time()
+        c, T, s = workloads.quantized(w, mat)
+        x = workloads.activations(w, M, mat)
+        log(f"[bench] {wname}/{m.name} inputs generated in {time.time() - t0:.1f}s")
+        d = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+        P = lutq.repack(d(c), w.bits, w.group)
+        self.packed = [P]
+        if cold:
+            ncopy = max(2, -(-COLD_SET_BYTES // P.nbytes))
+            from weight_only_lut_amd._lib import Packed, PackedDesc
+            for _ in range(ncopy - 1):
+                data = P.data.clone()
+                desc = PackedDesc.from_buffer_copy(P.desc)
+                desc.data = data.data_ptr()
+                self.packed.append(Packed(data, desc))
+        self.x, self.lut, self.scales = d(x), d(T), d(s)
+        self.y = torch.empty((M, self.N), dtype=torch.float16, device="cuda")
+        self.bytes = algorithmic_bytes(M, self.N, self.K, w.bits, w.group)
+        self.flops = 2 * M * self.N * self.K
+        self.host = (c, T, s, x)
+        torch.cuda.synchronize()
+
+    def call(self, lutq, i):
+        lutq.matmul(self.x, self.packed[i % len(self.packed)], self.lut, self.scales, out=self.y)
+
+
+def time_case(lutq, torch, case, steps, warmup):
+    """Average microseconds per call over `steps` back-to-back calls.
+
+    The calls are captured once in a HIP graph and replayed, so host-side
+    launch cost stays outside the timed region; HIP events are recorded on the
+    stream the kernels run on. Median of three replays.
+    """
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        for i in range(warmup):
+            case.call(lutq, i)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        for i in range(steps):
+            case.call(lutq, i)
+    with torch.cuda.stream(stream):
+        graph.replay()
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = []
+    with torch.cuda.stream(stream):  # replay() launches on the current stream
+        for _ in range(3):
+            start.record()
+            graph.replay()
+            stop.record()
+            torch.cuda.synchronize()
+            reps.append(start.elapsed_time(stop) * 1e3 / steps)
+    return sorted(reps)[1]
+
+
+def cpu_baseline(case, budget_s=15.0):
+    """The oracle as it stands (unpack + dequant + fp64 matmul) on the host cores."""
+    import numpy as np
+
+    import oracle
+    c, T, s, x = case.host
+    w = case.w
+    packed = oracle.pack_codes(c, w.bits)   # the oracle's own format; untimed
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # threadpoolctl missing
+        blas = int(os.environ.get("OMP_NUM_THREADS", "1"))
+    cores = len(os.sched_getaffinity(0))
+    times = []
+    t_all = time.time()
+    while time.time() - t_all < budget_s or len(times) < 3:
+        t0 = time.time()
+        codes = oracle.unpack_codes(packed, case.N, case.K, w.bits)
+        oracle.reference(x, codes, T, s, w.group)
+        times.append(time.time() - t0)
+        if len(times) >= 50:
+            break
+    med = float(np.median(times))
+    return {
+        "value": case.bytes / med / 1e9,
+        "unit": "GB/s",
+        "cores": min(cores, blas) if blas > 1 else 1,
+        "host_cores": cores,
+        "blas_threads": blas,
+        "kind": "oracle",
+        "us_per_call": med * 1e6,
+        "sample": f"{w.name} N={case.N} K={case.K} M={case.M}: whole matrix, canonical unpack + "
+                  f"fp32 dequant + fp64 matmul (numpy), median of {len(times)} runs",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-batch32", action="store_true")
+    ap.add_argument("--sweep", action="store_true", help="also time every workload (stderr)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "runs on one GPU only: --gpus above 1 is not supported "
+                                   "(the matmul would shard along N, with no communication, but "
+                                   "only the one-GPU kernel is built)"}))
+        sys.exit(2)
+
+    import torch
+
+    import weight_only_lut_amd as lutq
+    lutq.load_library()
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU")
+
+    # ---- headline: batch-1 4-bit g128 GEMV, cold weights ------------------
+    head = Case(lutq, torch, "int4_up_proj", None, 1, cold=True)
+    path, ksplit = lutq.plan(1, head.N, head.K, 4)
+    log(f"[bench] headline: {len(head.packed)} rotating copies, path={path}, ksplit={ksplit}")
+    region_us = time_case(lutq, torch, head, args.steps, args.warmup)
+    warm = Case.__new__(Case)
+    warm.__dict__.update(head.__dict__)
+    warm.packed = head.packed[:1]
+    w_region_us = time_case(lutq, torch, warm, args.steps, args.warmup)
+    log(f"[bench] headline cold: {region_us:.2f} us/call; warm: {w_region_us:.2f} us/call")
+
+    value = head.bytes / (region_us * 1e-6) / 1e9
+    achieved = value
+    traffic = load_traffic("int4_up_proj")
+
+    extra = {
+        "us_per_call": round(region_us, 3),
+        "bits_read_per_weight": round(head.bytes * 8 / (head.N * head.K), 4),
+        "warm": {"us_per_call": round(w_region_us, 3),
+                 "effective_GBps": round(head.bytes / (w_region_us * 1e-6) / 1e9, 1)},
+        "path": path, "ksplit": ksplit,
+    }
+
+    # ---- batch 32: log table, Llama-70B up-projection shape ---------------
+    if not args.no_batch32:
+        b32 = Case(lutq, torch, "log4_70b", None, 32, cold=True)
+        p32 = lutq.plan(32, b32.N, b32.K, 4)
+        k_us = time_case(lutq, torch, b32, max(20, args.steps // 4), args.warmup)
+        warm32 = Case.__new__(Case)
+        warm32.__dict__.update(b32.__dict__)
+        warm32.packed = b32.packed[:1]
+        wk_us = time_case(lutq, torch, warm32, max(20, args.steps // 4), args.warmup)
+        tf = b32.flops / (k_us * 1e-6) / 1e12
+        extra["batch32"] = {
+            "workload": "log4_70b", "N": b32.N, "K": b32.K, "M": 32, "path": p32[0],
+            "us_per_call": round(k_us, 3),
+            "TFLOPs": round(tf, 1), "mfma_frac": round(tf / MFMA_F16_PEAK_TFLOPS, 4),
+            "effective_GBps": round(b32.bytes / (k_us * 1e-6) / 1e9, 1),
+            "warm": {"us_per_call": round(wk_us, 3),
+                     "TFLOPs": round(b32.flops / (wk_us * 1e-6) / 1e12, 1),
+                     "mfma_frac": round(b32.flops / (wk_us * 1e-6) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4)},
+        }
+        log(f"[bench] batch32 cold {k_us:.2f} us = {tf:.1f} TFLOP/s; warm {wk_us:.2f} us")
+        del b32, warm32
+        torch.cuda.empty_cache()
+
+    if args.sweep:
+        extra["sweep"] = sweep(lutq, torch, args)
+
+    cpu = None if args.no_cpu_baseline else cpu_baseline(head)
+
+    out = {
+        "metric": "batch-1 4-bit g128 GEMV us + effective GB/s (% HBM peak); batch-32 TFLOP/s",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(region_us / 1e3, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": "int4_up_proj", "N": head.N, "K": head.K, "M": 1, "bits": 4,
+                   "group": 128, "table": "int", "weights": f"cold, {len(head.packed)} rotating copies"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic},
+        "cpu_baseline": cpu,
+        "extra": extra,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def sweep(lutq, torch, args):
+    """Every workload matrix at every batch size, both paths and the automatic
+    plan, cold weights; one JSON row per case on stderr."""
+    from synth import workloads
+    rows = []
+    for wname, w in workloads.WORKLOADS.items():
+        for m in w.matrices:
+            base = Case(lutq, torch, wname, m.name, max(w.batches), cold=True)
+            for M in w.batches:
+                case = Case.__new__(Case)
+                case.__dict__.update(base.__dict__)
+                case.M = M
+                case.x = base.x[:M].contiguous()
+                case.y = torch.empty((M, base.N), dtype=torch.float16, device="cuda")
+                case.bytes = algorithmic_bytes(M, base.N, base.K, w.bits, w.group)
+                case.flops = 2 * M * base.N * base.K
+                for path in ("auto", "gemv", "mfma"):
+                    def call(lutq_, i, case=case, path=path):
+                        lutq_.matmul(case.x, case.packed[i % len(case.packed)], case.lut,
+                                     case.scales, out=case.y, path=path)
+                    case.call = call
+                    us = time_case(lutq, torch, case, max(20, args.steps // 4), args.warmup)
+                    row = {"workload": wname, "matrix": m.name, "N": base.N, "K": base.K,
+                           "M": M, "path": path, "us": round(us, 3),
+                           "GBps": round(case.bytes / (us * 1e-6) / 1e9, 1),
+                           "TFLOPs": round(case.flops / (us * 1e-6) / 1e12, 2)}
+                    if path == "auto":
+                        row["plan"] = lutq.plan(M, base.N, base.K, w.bits)
+                    log("[sweep] " + json.dumps(row))
+                    rows.append(row)
+            del base
+            torch.cuda.empty_cache()
+    return rows
+
+
+def load_traffic(workload):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"matmul_kernel_{workload}_counters.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path))
+        from weight_only_lut_amd.build import source_digest
+        if rec.get("source_digest") != source_digest():
+            return None
+        return rec.get("traffic_bytes_per_launch")
+    except Exception:
+        return None
+
+
+if __name__ == "__main__":
+    main()

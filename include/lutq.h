@@ -44,8 +44,9 @@ enum {
   LUTQ_EBITS = -2,       /* bits not in {2, 3, 4}                           */
   LUTQ_EGROUP = -3,      /* group not 0 and not a multiple of 128, or K is
                             not a multiple of group (and of 128)            */
-  LUTQ_EALIGN = -4,      /* x or packed data not 16-byte aligned, or another
-                            pointer not 2-byte aligned                      */
+  LUTQ_EALIGN = -4,      /* x or packed data not 16-byte aligned, lut not
+                            4-byte aligned, or another pointer not 2-byte
+                            aligned                                         */
   LUTQ_EMISMATCH = -5,   /* N/K differ from the descriptor; bad magic or
                             layout version                                  */
   LUTQ_ESIZE = -6,       /* destination buffer too small                    */
@@ -53,10 +54,13 @@ enum {
   LUTQ_EUNSUPPORTED = -8 /* a size beyond the limits below                  */
 };
 
-/* Limits: 0 <= M; 0 <= N <= 2^24; 0 <= K <= 2^20. M above 32 is processed in
- * slices of 32 rows (the weights are streamed once per slice). */
+/* Limits: 0 <= M; 0 <= N <= 2^24; 0 <= K <= 2^20; N*K <= 2^36 (32 GiB of
+ * 4-bit codes). Batches above the per-launch capacity of a path (8 rows for
+ * GEMV, 32 for MFMA) are processed in slices; the weights are streamed once
+ * per slice. */
 #define LUTQ_MAX_N (1 << 24)
 #define LUTQ_MAX_K (1 << 20)
+#define LUTQ_MAX_NK (1LL << 36)
 
 /* ---- packed weights ------------------------------------------------------
  * Filled by lutq_repack. The layout ("wave-block", version 1) is the offline
@@ -118,7 +122,7 @@ int lutq_unpack(const lutq_packed_t* packed, uint8_t* codes_out, void* stream);
  * rescaled once per group as in the BitMoD abstract):
  *   x      : device, fp16 [M, K] row-major, 16-byte aligned.
  *   packed : host descriptor from lutq_repack (its data stays on device).
- *   lut    : device, fp16 [2^bits].
+ *   lut    : device, fp16 [2^bits], 4-byte aligned.
  *   scales : device, fp16 [N, K/group] row-major, or [1] when group == 0.
  *   y      : device, fp16 [M, N] row-major (output; written, never read).
  * Accumulation is fp32; y is rounded to nearest-even fp16. The table values

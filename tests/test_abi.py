@@ -115,6 +115,7 @@ def test_matmul_validates_before_launching(lib):
     assert call(y=P(0)) == EINVAL
     assert call(x=P(0x1008)) == EALIGN
     assert call(sc=P(0x3001)) == EALIGN
+    assert call(lut=P(0x2002)) == EALIGN     # the table is read as 4-byte words
     o = _lib.Options(); o.path = 7
     assert call(opts=ctypes.byref(o)) == EINVAL
     o = _lib.Options(); o.ksplit = -1

@@ -56,5 +56,15 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+def source_digest() -> str:
+    """SHA-256 over the library sources (to tell whether a stored profile is current)."""
+    import hashlib
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv))

@@ -33,6 +33,7 @@ int check_bits_group(int K, int bits, int group) {
 int check_sizes(int N, int K) {
   if (N < 0 || K < 0) return LUTQ_EINVAL;
   if (N > LUTQ_MAX_N || K > LUTQ_MAX_K) return LUTQ_EUNSUPPORTED;
+  if ((long long)N * K > LUTQ_MAX_NK) return LUTQ_EUNSUPPORTED;
   return LUTQ_OK;
 }
 
@@ -105,15 +106,17 @@ int cu_count() {
 constexpr int kAutoGemvMaxM = 4;
 
 void plan(int M, int N, int K, int cus, int* path, int* ksplit) {
-  const int ntiles = (N + lutq::kTileRows - 1) / lutq::kTileRows;
-  const int nrb = lutq::row_blocks(ntiles);
   const int nchunks = K / lutq::kChunk;
   if (*path == LUTQ_PATH_AUTO) *path = (M <= kAutoGemvMaxM) ? LUTQ_PATH_GEMV : LUTQ_PATH_MFMA;
+  const int kpath = *path == LUTQ_PATH_MFMA ? lutq::kPathMfma : lutq::kPathGemv;
+  const int rows = lutq::rows_per_workgroup(kpath);
+  const int nrb = (N + rows - 1) / rows;
   if (*ksplit <= 0) {
-    // keep every workgroup resident (two per CU: 64 KiB of LDS each) and
-    // spread small matrices over the whole chip
-    int k = (2 * cus) / (nrb > 0 ? nrb : 1);
-    if (k < 1) k = 1;
+    // Split K across workgroups only when the matrix has too few row blocks
+    // to give every CU work: the split costs a second pass over fp32
+    // partials and an arrival counter per row block.
+    int k = 1;
+    if (nrb > 0 && 2 * nrb <= cus) k = cus / nrb;
     *ksplit = k;
   }
   if (*ksplit > nchunks) *ksplit = nchunks > 0 ? nchunks : 1;
@@ -210,7 +213,7 @@ int lutq_matmul_ex(const uint16_t* x, const lutq_packed_t* packed, const uint16_
   }
   if (!x || !lut || !scales) return LUTQ_EINVAL;
   if (!aligned(x, 16)) return LUTQ_EALIGN;
-  if (!aligned(lut, 2) || !aligned(scales, 2)) return LUTQ_EALIGN;
+  if (!aligned(lut, 4) || !aligned(scales, 2)) return LUTQ_EALIGN;
 
   plan(M, N, K, cu_count(), &path, &ksplit);
   const int rows_per_launch = (path == LUTQ_PATH_MFMA) ? lutq::kMfmaMaxRows : lutq::kGemvMaxRows;
@@ -228,10 +231,11 @@ int lutq_matmul_ex(const uint16_t* x, const lutq_packed_t* packed, const uint16_
   p.ksplit = ksplit;
   p.cps = (p.nchunks + ksplit - 1) / ksplit;
   if (ksplit > 1) {
-    const size_t nrb = (size_t)lutq::row_blocks(p.ntiles);
+    const int rows = lutq::rows_per_workgroup(path == LUTQ_PATH_MFMA ? lutq::kPathMfma
+                                                                     : lutq::kPathGemv);
+    const size_t nrb = (size_t)(N + rows - 1) / rows;
     if (nrb * sizeof(uint32_t) > kCounterBytes) return LUTQ_EUNSUPPORTED;
-    const size_t pbytes = nrb * (size_t)ksplit * lutq::kMfmaMaxRows *
-                          (lutq::kTilesPerWg * lutq::kTileRows) * sizeof(float);
+    const size_t pbytes = nrb * (size_t)ksplit * lutq::kMfmaMaxRows * rows * sizeof(float);
     rc = get_scratch(stream, pbytes, &p.partial, &p.counters);
     if (rc) return rc;
   }
@@ -258,7 +262,7 @@ const char* lutq_strerror(int status) {
     case LUTQ_EINVAL: return "invalid argument (null pointer, negative size or bad option)";
     case LUTQ_EBITS: return "bits must be 2, 3 or 4";
     case LUTQ_EGROUP: return "group must be 0 or a multiple of 128 dividing K, and K a multiple of 128";
-    case LUTQ_EALIGN: return "misaligned pointer (x and packed data need 16 bytes, others 2)";
+    case LUTQ_EALIGN: return "misaligned pointer (x and packed data need 16 bytes, lut 4, others 2)";
     case LUTQ_EMISMATCH: return "shape or layout does not match the packed descriptor";
     case LUTQ_ESIZE: return "destination buffer too small";
     case LUTQ_EHIP: return "HIP runtime error";

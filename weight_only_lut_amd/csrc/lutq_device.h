@@ -19,6 +19,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <utility>
+
 namespace lutq {
 
 constexpr int kTileRows = 16;
@@ -113,22 +115,49 @@ __device__ __forceinline__ void pair_codes(uint32_t idx, uint32_t& c0, uint32_t&
   }
 }
 
-// Fill the duplicated pair table. Every thread of the block takes part; the
-// caller issues a barrier before the first lookup.
+// T[lane mod 2^BITS] (fp16 bits in the low half) for every lane. The table
+// is read with uniform loads (the compiler issues them as scalar loads) and
+// spread to lanes with selects; `lut` must be 4-byte aligned.
 template <int BITS>
-__device__ __forceinline__ void build_pair_table(uint32_t* table, const uint16_t* lut,
-                                                 int tid, int nthreads) {
-  // thread -> (entry, run of copies); each run is written as 16-byte stores
-  const int runs_per_entry = (kPairEntries * kCopies / 4) / kPairEntries;  // 16 quads
-  for (int w = tid; w < kPairEntries * runs_per_entry; w += nthreads) {
-    const uint32_t idx = (uint32_t)w / runs_per_entry;
-    const int run = w % runs_per_entry;
-    uint32_t c0, c1;
-    pair_codes<BITS>(idx, c0, c1);
-    const uint32_t v = (uint32_t)lut[c0] | ((uint32_t)lut[c1] << 16);
-    u32x4 q = {v, v, v, v};
-    *reinterpret_cast<u32x4*>(table + idx * kCopies + run * 4) = q;
-  }
+__device__ __forceinline__ uint32_t lut_to_lanes(const uint16_t* lut, int lane) {
+  constexpr int kWords = (1 << BITS) / 2;
+  const uint32_t* w = reinterpret_cast<const uint32_t*>(lut);
+  uint32_t words[kWords];
+#pragma unroll
+  for (int i = 0; i < kWords; ++i) words[i] = __builtin_amdgcn_readfirstlane(w[i]);
+  const int e = lane & ((1 << BITS) - 1);
+  uint32_t v = words[0];
+#pragma unroll
+  for (int i = 1; i < kWords; ++i) v = (e >> 1) == i ? words[i] : v;
+  return (e & 1) ? (v >> 16) : (v & 0xFFFFu);
+}
+
+// Fill the duplicated pair table. `lut_lane` holds T[lane] in lanes
+// 0..2^BITS-1 of every wave; entries are gathered with cross-lane reads.
+// THREADS / 256 threads share an entry: each computes the entry's value once
+// and writes its share of the 64 copies as 16-byte stores. Store k of a
+// thread goes to chunk (k + entry) mod C of its share, so the 64 lanes of a
+// store instruction cover all 64 banks evenly (4 dwords per bank, the
+// minimum for 16-byte stores) instead of piling onto two bank groups. The
+// caller issues a barrier before the first lookup.
+template <int BITS, int THREADS>
+__device__ __forceinline__ void build_pair_table(uint32_t* table, uint32_t lut_lane, int tid) {
+  static_assert(THREADS % kPairEntries == 0, "whole threads per entry");
+  constexpr int kPerEntry = THREADS / kPairEntries;   // threads per entry
+  constexpr int kCopiesPer = kCopies / kPerEntry;      // copies each thread writes
+  constexpr int C = kCopiesPer / 4;                    // 16-byte stores per thread
+  static_assert(kCopiesPer % 4 == 0 && (C & (C - 1)) == 0, "power-of-two 16-byte stores");
+  const uint32_t idx = (uint32_t)tid / kPerEntry;
+  const uint32_t part = (uint32_t)tid % kPerEntry;
+  uint32_t c0, c1;
+  pair_codes<BITS>(idx, c0, c1);
+  const uint32_t v0 = (uint32_t)__shfl((int)lut_lane, (int)c0) & 0xFFFFu;
+  const uint32_t v1 = (uint32_t)__shfl((int)lut_lane, (int)c1) & 0xFFFFu;
+  const uint32_t v = v0 | (v1 << 16);
+  const u32x4 q = {v, v, v, v};
+  u32x4* dst = reinterpret_cast<u32x4*>(table + idx * kCopies + part * kCopiesPer);
+#pragma unroll
+  for (int k = 0; k < C; ++k) dst[(k + idx) & (C - 1)] = q;
 }
 
 // DPP row_newbcast:n -- every lane of each 16-lane row reads lane n of that
@@ -153,6 +182,16 @@ __device__ __forceinline__ uint32_t row_newbcast(uint32_t v, int n) {
     case 15: return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x15f, 0xF, 0xF, false);
     default: return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x15f, 0xF, 0xF, false);
   }
+}
+
+// Calls f(std::integral_constant<int, I>{}) for I = 0 .. N-1 (unrolled).
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
 __device__ __forceinline__ f16x2 as_f16x2(uint32_t v) { return __builtin_bit_cast(f16x2, v); }

@@ -10,11 +10,6 @@
 
 namespace lutq {
 
-// Fixed workgroup shape of the matmul kernels: 8 waves split the K range of
-// a block of `tiles_per_wg` 16-row tiles.
-constexpr int kWaves = 8;
-constexpr int kThreads = kWaves * kWave;
-
 struct MatmulParams {
   const uint16_t* x;      // fp16 [M, K] (this launch's slice of rows)
   const uint8_t* packed;  // wave-block layout
@@ -36,11 +31,8 @@ enum Path { kPathGemv = 1, kPathMfma = 2 };
 constexpr int kGemvMaxRows = 8;
 constexpr int kMfmaMaxRows = 32;
 
-// Tiles (16 rows each) per workgroup.
-constexpr int kTilesPerWg = 4;
-
-// Number of 64-row blocks for N rows.
-inline int row_blocks(int ntiles) { return (ntiles + kTilesPerWg - 1) / kTilesPerWg; }
+// Output rows one matmul workgroup covers on a path (a multiple of 16).
+int rows_per_workgroup(int path);
 
 hipError_t launch_repack(const uint8_t* codes, uint8_t* dst, int N, int K, int bits,
                          hipStream_t s);

@@ -11,7 +11,7 @@
 // Workgroup: 8 waves; the block covers 4 tiles (64 rows) and a range of
 // 128-code chunks, dealt to the waves round-robin. Each wave streams the four
 // 1 KiB (at 4 bits) blocks of a chunk with one coalesced load per lane,
-// prefetching PF chunks ahead; codes, scales and activations of a chunk are
+// keeping several chunks in flight; codes, scales and activations of a chunk are
 // loaded together so the in-order load counter never waits on a prefetch.
 //
 // Two compute policies share that skeleton:
@@ -31,15 +31,23 @@
 
 namespace lutq {
 
-template <int BITS, bool MFMA, int MROWS, bool GROUPED>
-__global__ __launch_bounds__(kThreads) void matmul_kernel(const MatmulParams p) {
-  constexpr int TPW = kTilesPerWg;
+// BITS: code width; MFMA: compute policy; MROWS: batch rows per launch;
+// GROUPED: per-group (else per-tensor) scales; PF: register slots of the load
+// pipeline (PF - 1 chunks in flight while one is computed);
+// TPW: 16-row tiles per wave (and per workgroup); WAVES: waves per workgroup,
+// which split the K range; OCC: waves per SIMD the register budget targets.
+template <int BITS, bool MFMA, int MROWS, bool GROUPED, int PF, int TPW, int WAVES, int OCC>
+__global__ __launch_bounds__(WAVES * kWave) __attribute__((amdgpu_waves_per_eu(OCC)))
+void matmul_kernel(const MatmulParams p) {
+  constexpr int kThreads = WAVES * kWave;
+  constexpr int kWaves = WAVES;
   constexpr int ROWS = TPW * kTileRows;
-  constexpr int PF = 2;
   constexpr int MT = MFMA ? MROWS / 16 : 1;
   constexpr int SLOT = 4 * BITS;
   constexpr int BLOCK = kWave * SLOT;
+  static_assert(PF >= 2, "at least one chunk in flight while another is computed");
   static_assert(kWaves * ROWS * MROWS <= kTableWords, "reduction buffer exceeds LDS table");
+  static_assert(kThreads >= kPairEntries, "table build needs one thread per entry");
 
   __shared__ __attribute__((aligned(16))) uint32_t table[kTableWords];
   __shared__ int arrive_last;
@@ -50,64 +58,81 @@ __global__ __launch_bounds__(kThreads) void matmul_kernel(const MatmulParams p) 
   const int r = lane & 15, q = lane >> 4;
   const uint32_t lane_byte = (uint32_t)lane << 2;
 
+  // The table values, one per lane (lanes >= 2^BITS repeat the table).
+  // Read with wave-uniform (scalar) loads: they do not queue behind the
+  // vector loads of the code stream, so the LDS table is ready early.
+  const uint32_t lut_lane = lut_to_lanes<BITS>(p.lut, lane);
+
   const int rb = blockIdx.x / p.ksplit;
   const int ks = blockIdx.x - rb * p.ksplit;
   const int c_begin = ks * p.cps;
   const int c_end = min(p.nchunks, c_begin + p.cps);
   const int span = max(0, c_end - c_begin);
+  // this wave's chunks: cw, cw + WAVES, cw + 2 WAVES, ... (nmine of them)
+  const int cw = c_begin + wave;
   const int nmine = span > wave ? (span - wave + kWaves - 1) / kWaves : 0;
+  // Every step of the pipeline issues the same loads, so the in-order load
+  // counter can be waited on precisely: steps past the wave's last chunk
+  // re-read a valid chunk of this block and contribute with weight 0.
+  const int c_last = min(p.nchunks - 1, max(c_begin, c_end - 1));
+  const int niter = (nmine + PF - 1) / PF * PF;
   const int tile0 = rb * TPW;
-  const int ntl = min(TPW, p.ntiles - tile0);
   const int cpg = GROUPED ? p.group / kChunk : 1;       // chunks per group
   const int gpr = GROUPED ? p.K / p.group : 0;          // groups per row
 
+  // Tiles past the end of the matrix (in the last row block) re-read the
+  // last tile: the loads stay in bounds and the compute stays branch-free;
+  // their rows are >= N and are never stored. Bases are wave-uniform
+  // (SGPRs); per-lane parts are 32-bit byte offsets.
   const uint8_t* tbase[TPW];
-  size_t srow[TPW];
+  uint32_t sboff[TPW];
 #pragma unroll
   for (int t = 0; t < TPW; ++t) {
-    tbase[t] = p.packed + (size_t)(tile0 + t) * p.nchunks * BLOCK + lane * SLOT;
-    srow[t] = (size_t)min(p.N - 1, (tile0 + t) * kTileRows + r) * gpr;
+    const int tile = min(tile0 + t, p.ntiles - 1);
+    tbase[t] = p.packed + (size_t)tile * p.nchunks * BLOCK;
+    sboff[t] = 2u * (uint32_t)min(p.N - 1, (tile0 + t) * kTileRows + r) * (uint32_t)gpr;
   }
+  const uint32_t lane_off = (uint32_t)lane * SLOT;
 
-  // activation offsets of this lane within a chunk
+  // Activation rows past M re-read row M-1 (never stored), again to keep
+  // the inner loop free of branches.
   // GEMV: lane 16q + 4j + i holds the pair x[128c + 32j + 8q + 2i .. +1]
-  const int gx_off = 32 * (r >> 2) + 8 * q + 2 * (r & 3);
+  const uint32_t gx_boff = 2u * (32 * (r >> 2) + 8 * q + 2 * (r & 3));
   // MFMA: lane (row r, quarter q) holds x[row][128c + 32j + 8q .. +7]
-  const int ax_off = 8 * q;
+  uint32_t aboff[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+    aboff[mt] = 2u * ((uint32_t)min(mt * 16 + r, p.M - 1) * (uint32_t)p.K + 8 * q);
 
   SlotRegs<BITS> cbuf[PF][TPW];
   uint16_t sbuf[PF][TPW];
   uint32_t xbuf[PF][MFMA ? 1 : MROWS];
   u32x4 abuf[PF][MT][MFMA ? 4 : 1];
 
+  auto chunk = [&](int i) { return min(cw + i * kWaves, c_last); };
+
   auto issue = [&](auto S, int c) {
     constexpr int s = decltype(S)::value;
+    const int gidx = cpg == 1 ? c : c / cpg;
+    const char* sbase = reinterpret_cast<const char*>(p.scales + gidx);
 #pragma unroll
     for (int t = 0; t < TPW; ++t) {
-      if (t < ntl) {
-        cbuf[s][t] = load_slot<BITS>(tbase[t] + (size_t)c * BLOCK);
-        if constexpr (GROUPED) sbuf[s][t] = p.scales[srow[t] + c / cpg];
-      }
+      cbuf[s][t] = load_slot<BITS>(tbase[t] + (size_t)c * BLOCK + lane_off);
+      if constexpr (GROUPED) sbuf[s][t] = *reinterpret_cast<const uint16_t*>(sbase + sboff[t]);
     }
+    const char* xc = reinterpret_cast<const char*>(p.x + (size_t)c * kChunk);
     if constexpr (!MFMA) {
 #pragma unroll
-      for (int m = 0; m < MROWS; ++m)
-        xbuf[s][m] = (m < p.M)
-            ? *reinterpret_cast<const uint32_t*>(p.x + (size_t)m * p.K + (size_t)c * kChunk + gx_off)
-            : 0u;
+      for (int m = 0; m < MROWS; ++m) {
+        const char* xm = xc + (size_t)min(m, p.M - 1) * p.K * 2;  // uniform
+        xbuf[s][m] = *reinterpret_cast<const uint32_t*>(xm + gx_boff);
+      }
     } else {
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        const int row = mt * 16 + r;
+      for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          u32x4 v = {0u, 0u, 0u, 0u};
-          if (row < p.M)
-            v = *reinterpret_cast<const u32x4*>(p.x + (size_t)row * p.K + (size_t)c * kChunk +
-                                                 32 * j + ax_off);
-          abuf[s][mt][j] = v;
-        }
-      }
+        for (int j = 0; j < 4; ++j)
+          abuf[s][mt][j] = *reinterpret_cast<const u32x4*>(xc + 64 * j + aboff[mt]);
     }
   };
 
@@ -121,9 +146,14 @@ __global__ __launch_bounds__(kThreads) void matmul_kernel(const MatmulParams p) 
     for (int mt = 0; mt < MT; ++mt) macc[t][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  auto compute = [&](auto S, int c) {
+  // One chunk (128 codes) of every tile; `weight` is 1 for the wave's real
+  // chunks and 0 for pipeline padding steps.
+  auto compute = [&](auto S, float weight) {
     constexpr int s = decltype(S)::value;
-    (void)c;
+    float sc[TPW];
+#pragma unroll
+    for (int t = 0; t < TPW; ++t)
+      sc[t] = GROUPED ? weight * f16_bits_to_f32(sbuf[s][t]) : weight;
     if constexpr (!MFMA) {
       // k-step outer, tile inner: each activation broadcast serves all tiles
       float cs[TPW][MROWS];
@@ -135,7 +165,7 @@ __global__ __launch_bounds__(kThreads) void matmul_kernel(const MatmulParams p) 
       for (int j = 0; j < 4; ++j) {
         uint32_t idx4[TPW];
 #pragma unroll
-        for (int t = 0; t < TPW; ++t) idx4[t] = t < ntl ? step_indices<BITS>(cbuf[s][t], j) : 0u;
+        for (int t = 0; t < TPW; ++t) idx4[t] = step_indices<BITS>(cbuf[s][t], j);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           // row_newbcast:(4j+i): every lane of a 16-lane row reads lane 4j+i of that row
@@ -144,7 +174,6 @@ __global__ __launch_bounds__(kThreads) void matmul_kernel(const MatmulParams p) 
           for (int m = 0; m < MROWS; ++m) xv[m] = row_newbcast(xbuf[s][m], 4 * j + i);
 #pragma unroll
           for (int t = 0; t < TPW; ++t) {
-            if (t >= ntl) continue;
             const uint32_t pr = lds_load(table, pair_addr(idx4[t], lane_byte, i));
 #pragma unroll
             for (int m = 0; m < MROWS; ++m)
@@ -153,21 +182,12 @@ __global__ __launch_bounds__(kThreads) void matmul_kernel(const MatmulParams p) 
         }
       }
 #pragma unroll
-      for (int t = 0; t < TPW; ++t) {
-        if (t >= ntl) continue;
-        if constexpr (GROUPED) {
-          const float sc = f16_bits_to_f32(sbuf[s][t]);
+      for (int t = 0; t < TPW; ++t)
 #pragma unroll
-          for (int m = 0; m < MROWS; ++m) gacc[t][m] = __builtin_fmaf(sc, cs[t][m], gacc[t][m]);
-        } else {
-#pragma unroll
-          for (int m = 0; m < MROWS; ++m) gacc[t][m] += cs[t][m];
-        }
-      }
+        for (int m = 0; m < MROWS; ++m) gacc[t][m] = __builtin_fmaf(sc[t], cs[t][m], gacc[t][m]);
     } else {
 #pragma unroll
       for (int t = 0; t < TPW; ++t) {
-        if (t >= ntl) continue;
         f32x4 cg[MT];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -181,43 +201,33 @@ __global__ __launch_bounds__(kThreads) void matmul_kernel(const MatmulParams p) 
 #pragma unroll
           for (int mt = 0; mt < MT; ++mt) {
             const f16x8 a = __builtin_bit_cast(f16x8, abuf[s][mt][j]);
-            if constexpr (GROUPED) {
-              cg[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                  a, b, j == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : cg[mt], 0, 0, 0);
-            } else {
-              macc[t][mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, macc[t][mt], 0, 0, 0);
-            }
+            cg[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                a, b, j == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : cg[mt], 0, 0, 0);
           }
         }
-        if constexpr (GROUPED) {
-          const float sc = f16_bits_to_f32(sbuf[s][t]);
 #pragma unroll
-          for (int mt = 0; mt < MT; ++mt)
+        for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) macc[t][mt][e] = __builtin_fmaf(sc, cg[mt][e], macc[t][mt][e]);
-        }
+          for (int e = 0; e < 4; ++e) macc[t][mt][e] = __builtin_fmaf(sc[t], cg[mt][e], macc[t][mt][e]);
       }
     }
   };
 
-  using S0 = std::integral_constant<int, 0>;
-  using S1 = std::integral_constant<int, 1>;
-  static_assert(PF == 2, "pipeline written for two stages");
+  // Software pipeline: PF register slots; the load of step i + PF - 1 is
+  // issued before step i is computed, so PF - 1 chunks are in flight during
+  // every compute step.
+  static_for<PF - 1>([&](auto S) { issue(S, chunk(decltype(S)::value)); });
 
-  const int cw = c_begin + wave;  // this wave's chunks: cw, cw + 8, cw + 16, ...
-  if (nmine > 0) issue(S0{}, cw);
-  if (nmine > 1) issue(S1{}, cw + kWaves);
-
-  build_pair_table<BITS>(table, p.lut, tid, kThreads);
+  build_pair_table<BITS, kThreads>(table, lut_lane, tid);
   __syncthreads();
 
-  for (int i0 = 0; i0 < nmine; i0 += PF) {
-    compute(S0{}, cw + i0 * kWaves);
-    if (i0 + 2 < nmine) issue(S0{}, cw + (i0 + 2) * kWaves);
-    if (i0 + 1 < nmine) {
-      compute(S1{}, cw + (i0 + 1) * kWaves);
-      if (i0 + 3 < nmine) issue(S1{}, cw + (i0 + 3) * kWaves);
-    }
+  for (int i0 = 0; i0 < niter; i0 += PF) {
+    static_for<PF>([&](auto S) {
+      constexpr int s = decltype(S)::value;
+      const int i = i0 + s;
+      issue(std::integral_constant<int, (s + PF - 1) % PF>{}, chunk(i + PF - 1));
+      compute(S, i < nmine ? 1.f : 0.f);
+    });
   }
 
   // ---- combine the waves (fixed order) ------------------------------------
@@ -262,16 +272,21 @@ __global__ __launch_bounds__(kThreads) void matmul_kernel(const MatmulParams p) 
   if (p.ksplit == 1) return;
 
   // ---- split-K: the last workgroup of this row block sums the splits ------
-  __threadfence();
+  // Partials are written and read with agent-scope atomics, which go to the
+  // device-coherent level of the memory system and so are seen across XCDs
+  // without writing back or invalidating whole L2 caches (the cost of an
+  // agent-scope fence). Each thread waits for its partial stores to be
+  // acknowledged before the barrier; only then does one thread bump the
+  // row block's arrival counter.
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (tid == 0) {
     const uint32_t old =
-        __hip_atomic_fetch_add(p.counters + rb, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_fetch_add(p.counters + rb, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     arrive_last = (old == (uint32_t)(p.ksplit - 1));
   }
   __syncthreads();
   if (!arrive_last) return;
-  __threadfence();
   for (int it = tid; it < items; it += kThreads) {
     const int m = it / ROWS, row = it - m * ROWS;
     const int n = tile0 * kTileRows + row;
@@ -284,14 +299,48 @@ __global__ __launch_bounds__(kThreads) void matmul_kernel(const MatmulParams p) 
   if (tid == 0) __hip_atomic_store(p.counters + rb, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Kernel shapes (overridable at build time for tuning).
+#ifndef LUTQ_GEMV_TPW
+#define LUTQ_GEMV_TPW 2
+#endif
+#ifndef LUTQ_GEMV_WAVES
+#define LUTQ_GEMV_WAVES 8
+#endif
+#ifndef LUTQ_GEMV_PF
+#define LUTQ_GEMV_PF 2
+#endif
+#ifndef LUTQ_GEMV_OCC
+#define LUTQ_GEMV_OCC 4
+#endif
+#ifndef LUTQ_MFMA_TPW
+#define LUTQ_MFMA_TPW 4
+#endif
+#ifndef LUTQ_MFMA_WAVES
+#define LUTQ_MFMA_WAVES 4
+#endif
+#ifndef LUTQ_MFMA_PF
+#define LUTQ_MFMA_PF 2
+#endif
+#ifndef LUTQ_MFMA_OCC
+#define LUTQ_MFMA_OCC 2
+#endif
+
+int rows_per_workgroup(int path) {
+  return (path == kPathMfma ? LUTQ_MFMA_TPW : LUTQ_GEMV_TPW) * kTileRows;
+}
+
 template <int BITS, bool MFMA, int MROWS>
 static hipError_t launch_t(const MatmulParams& p, hipStream_t s) {
-  const int nrb = row_blocks(p.ntiles);
+  constexpr int PF = MFMA ? LUTQ_MFMA_PF : LUTQ_GEMV_PF;
+  constexpr int TPW = MFMA ? LUTQ_MFMA_TPW : LUTQ_GEMV_TPW;
+  constexpr int WAVES = MFMA ? LUTQ_MFMA_WAVES : LUTQ_GEMV_WAVES;
+  constexpr int OCC = MFMA ? LUTQ_MFMA_OCC : LUTQ_GEMV_OCC;
+  const int nrb = (p.ntiles + TPW - 1) / TPW;
   const dim3 grid((unsigned)nrb * (unsigned)p.ksplit);
   if (p.group != 0)
-    matmul_kernel<BITS, MFMA, MROWS, true><<<grid, kThreads, 0, s>>>(p);
+    matmul_kernel<BITS, MFMA, MROWS, true, PF, TPW, WAVES, OCC><<<grid, WAVES * kWave, 0, s>>>(p);
   else
-    matmul_kernel<BITS, MFMA, MROWS, false><<<grid, kThreads, 0, s>>>(p);
+    matmul_kernel<BITS, MFMA, MROWS, false, PF, TPW, WAVES, OCC><<<grid, WAVES * kWave, 0, s>>>(p);
   return hipGetLastError();
 }
 
