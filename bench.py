@@ -155,7 +155,15 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-batch32", action="store_true")
     ap.add_argument("--sweep", action="store_true", help="also time every workload (stderr)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 256 MiB device copy (for scaling memory counters)")
+    ap.add_argument("--summarize-profile", nargs=3, metavar=("KERNEL_TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
+                    help="write profiles/ summaries from rocprofv3 output and exit")
+    ap.add_argument("--profile-command", default="", help="command line recorded in the summary")
     args = ap.parse_args()
+    if args.summarize_profile:
+        summarize_profile(*args.summarize_profile, command=args.profile_command)
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "runs on one GPU only: --gpus above 1 is not supported "
                                    "(the matmul would shard along N, with no communication, but "
@@ -218,6 +226,9 @@ def main():
     if args.sweep:
         extra["sweep"] = sweep(lutq, torch, args)
 
+    if args.copy_calibration:
+        copy_calibration(torch)
+
     cpu = None if args.no_cpu_baseline else cpu_baseline(head)
 
     out = {
@@ -279,10 +290,98 @@ def sweep(lutq, torch, args):
     return rows
 
 
+COPY_BYTES = 256 << 20
+
+
+def copy_calibration(torch):
+    """A plain streaming kernel that reads COPY_BYTES and writes COPY_BYTES
+    once (an elementwise negation, easy to pick out of a trace by name): the
+    reference for scaling FETCH_SIZE / WRITE_SIZE."""
+    a = torch.ones(COPY_BYTES // 2, dtype=torch.float16, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(3):
+        torch.neg(a, out=b)
+    torch.cuda.synchronize()
+
+
+HEADLINE_KERNEL = "matmul_kernel<4, false, 1, true"   # 4-bit, GEMV, batch 1, grouped scales
+BATCH32_KERNEL = "matmul_kernel<4, true, 32, false"   # 4-bit, MFMA, batch 32, tensor scale
+
+
+def _read_csv(path):
+    import csv
+    with open(path) as f:
+        return list(csv.DictReader(f))
+
+
+def _find(dirpath, suffix):
+    for root, _, files in os.walk(dirpath):
+        for f in files:
+            if f.endswith(suffix):
+                return os.path.join(root, f)
+    raise FileNotFoundError(f"no *{suffix} under {dirpath}")
+
+
+def _counter_per_dispatch(dirpath, counter, name_part):
+    import statistics
+    per = {}
+    for r in _read_csv(_find(dirpath, "counter_collection.csv")):
+        if name_part in r["Kernel_Name"] and r["Counter_Name"] == counter:
+            per[r["Dispatch_Id"]] = per.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+    return statistics.median(per.values()) if per else None, len(per)
+
+
+def summarize_profile(kt_dir, fetch_dir, write_dir, command=""):
+    """profiles/*: kernel durations (rocprofv3 --kernel-trace --stats) and HBM
+    traffic per launch (FETCH_SIZE, WRITE_SIZE in KiB, scaled by what the same
+    counters read for the COPY_BYTES copy)."""
+    from weight_only_lut_amd.build import source_digest
+    stats = _read_csv(_find(kt_dir, "kernel_stats.csv"))
+    rows = [r for r in stats if "lutq::" in r["Name"] or "copy" in r["Name"].lower()]
+    copy_name = "neg_kernel"
+    f_copy, n1 = _counter_per_dispatch(fetch_dir, "FETCH_SIZE", copy_name)
+    w_copy, n2 = _counter_per_dispatch(write_dir, "WRITE_SIZE", copy_name)
+    f_scale = COPY_BYTES / (f_copy * 1024) if f_copy else None
+    w_scale = COPY_BYTES / (w_copy * 1024) if w_copy else None
+    out = {"source_digest": source_digest(), "copy_bytes": COPY_BYTES,
+           "fetch_scale": f_scale, "write_scale": w_scale, "kernels": {}}
+    for label, part in (("int4_up_proj", HEADLINE_KERNEL), ("log4_70b_batch32", BATCH32_KERNEL)):
+        f, nf = _counter_per_dispatch(fetch_dir, "FETCH_SIZE", part)
+        w, nw = _counter_per_dispatch(write_dir, "WRITE_SIZE", part)
+        dur = [r for r in stats if part in r["Name"]]
+        rec = {"kernel": part, "fetch_kib_raw": f, "write_kib_raw": w, "dispatches": [nf, nw],
+               "avg_duration_us": float(dur[0]["AverageNs"]) / 1e3 if dur else None}
+        if f is not None and w is not None and f_scale and w_scale:
+            rec["traffic_bytes_per_launch"] = round(f * 1024 * f_scale + w * 1024 * w_scale)
+        out["kernels"][label] = rec
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    with open(os.path.join(ROOT, "profiles", "matmul_kernel_counters.json"), "w") as fh:
+        json.dump(out, fh, indent=1)
+    lines = ["# lutq matmul kernels: rocprofv3 summary", "",
+             f"Source digest of weight_only_lut_amd/csrc: `{out['source_digest']}`", "",
+             "Command:", "", "```", command or "(not recorded)", "```", "",
+             "## Kernel durations (rocprofv3 --kernel-trace --stats)", "",
+             "| kernel | calls | average us | min us | max us |", "|---|---|---|---|---|"]
+    for r in rows:
+        lines.append(f"| `{r['Name'][:110]}` | {r['Calls']} | {float(r['AverageNs'])/1e3:.3f} | "
+                     f"{float(r['MinNs'])/1e3:.3f} | {float(r['MaxNs'])/1e3:.3f} |")
+    lines += ["", "## HBM traffic per launch (rocprofv3 --pmc FETCH_SIZE, then WRITE_SIZE)", "",
+              f"Calibration: a {COPY_BYTES >> 20} MiB device copy reads FETCH_SIZE = {f_copy} KiB and "
+              f"WRITE_SIZE = {w_copy} KiB per dispatch; scale factors {f_scale} (fetch) and "
+              f"{w_scale} (write) turn counter KiB into bytes.", "",
+              "| workload | raw FETCH KiB | raw WRITE KiB | scaled bytes / launch |", "|---|---|---|---|"]
+    for label, rec in out["kernels"].items():
+        lines.append(f"| {label} | {rec['fetch_kib_raw']} | {rec['write_kib_raw']} | "
+                     f"{rec.get('traffic_bytes_per_launch')} |")
+    with open(os.path.join(ROOT, "profiles", "matmul_kernel_int4_up_proj_log4_70b.md"), "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print(json.dumps(out, indent=1))
+
+
 def load_traffic(workload):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it
     was taken on the current kernel source; else None."""
-    path = os.path.join(ROOT, "profiles", f"matmul_kernel_{workload}_counters.json")
+    path = os.path.join(ROOT, "profiles", "matmul_kernel_counters.json")
     if not os.path.exists(path):
         return None
     try:
@@ -290,8 +389,8 @@ def load_traffic(workload):
         from weight_only_lut_amd.build import source_digest
         if rec.get("source_digest") != source_digest():
             return None
-        return rec.get("traffic_bytes_per_launch")
-    except Exception:
+        return rec["kernels"][workload].get("traffic_bytes_per_launch")
+    except (OSError, KeyError, ValueError):
         return None
 
 
