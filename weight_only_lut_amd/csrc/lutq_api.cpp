@@ -103,7 +103,7 @@ int cu_count() {
 }
 
 // Batch rows above which the automatic plan switches from GEMV to MFMA.
-constexpr int kAutoGemvMaxM = 4;
+constexpr int kAutoGemvMaxM = 2;
 
 void plan(int M, int N, int K, int cus, int* path, int* ksplit) {
   const int nchunks = K / lutq::kChunk;

@@ -46,10 +46,17 @@ void matmul_kernel(const MatmulParams p) {
   constexpr int SLOT = 4 * BITS;
   constexpr int BLOCK = kWave * SLOT;
   static_assert(PF >= 2, "at least one chunk in flight while another is computed");
-  static_assert(kWaves * ROWS * MROWS <= kTableWords, "reduction buffer exceeds LDS table");
+  // Cross-wave reduction buffer (reuses the table's LDS): [wave][m][row] with
+  // a row pitch of ROWS + 4, so that the MFMA accumulator stores (lanes r, q
+  // -> rows r, batch rows 4q + e) and the row-contiguous final reads both
+  // spread over distinct banks.
+  constexpr int RP = ROWS + 4;
+  static_assert(ROWS % 16 == 0, "pitch rule assumes whole tiles");
+  constexpr int kRedWords = kWaves * MROWS * RP;
+  constexpr int kLdsWords = kRedWords > kTableWords ? kRedWords : kTableWords;
   static_assert(kThreads >= kPairEntries, "table build needs one thread per entry");
 
-  __shared__ __attribute__((aligned(16))) uint32_t table[kTableWords];
+  __shared__ __attribute__((aligned(16))) uint32_t table[kLdsWords];
   __shared__ int arrive_last;
 
   const int tid = threadIdx.x;
@@ -73,7 +80,7 @@ void matmul_kernel(const MatmulParams p) {
   const int nmine = span > wave ? (span - wave + kWaves - 1) / kWaves : 0;
   // Every step of the pipeline issues the same loads, so the in-order load
   // counter can be waited on precisely: steps past the wave's last chunk
-  // re-read a valid chunk of this block and contribute with weight 0.
+  // re-read a valid chunk of this block and are not computed.
   const int c_last = min(p.nchunks - 1, max(c_begin, c_end - 1));
   const int niter = (nmine + PF - 1) / PF * PF;
   const int tile0 = rb * TPW;
@@ -146,14 +153,9 @@ void matmul_kernel(const MatmulParams p) {
     for (int mt = 0; mt < MT; ++mt) macc[t][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  // One chunk (128 codes) of every tile; `weight` is 1 for the wave's real
-  // chunks and 0 for pipeline padding steps.
-  auto compute = [&](auto S, float weight) {
+  // One chunk (128 codes) of every tile.
+  auto compute = [&](auto S) {
     constexpr int s = decltype(S)::value;
-    float sc[TPW];
-#pragma unroll
-    for (int t = 0; t < TPW; ++t)
-      sc[t] = GROUPED ? weight * f16_bits_to_f32(sbuf[s][t]) : weight;
     if constexpr (!MFMA) {
       // k-step outer, tile inner: each activation broadcast serves all tiles
       float cs[TPW][MROWS];
@@ -182,15 +184,23 @@ void matmul_kernel(const MatmulParams p) {
         }
       }
 #pragma unroll
-      for (int t = 0; t < TPW; ++t)
+      for (int t = 0; t < TPW; ++t) {
+        if constexpr (GROUPED) {
+          const float sc = f16_bits_to_f32(sbuf[s][t]);
 #pragma unroll
-        for (int m = 0; m < MROWS; ++m) gacc[t][m] = __builtin_fmaf(sc[t], cs[t][m], gacc[t][m]);
+          for (int m = 0; m < MROWS; ++m) gacc[t][m] = __builtin_fmaf(sc, cs[t][m], gacc[t][m]);
+        } else {
+#pragma unroll
+          for (int m = 0; m < MROWS; ++m) gacc[t][m] += cs[t][m];
+        }
+      }
     } else {
 #pragma unroll
       for (int t = 0; t < TPW; ++t) {
         f32x4 cg[MT];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
+          // the decoded pairs of k-step j are the B operand
           const uint32_t idx4 = step_indices<BITS>(cbuf[s][t], j);
           u32x4 bq;
           bq.x = lds_load(table, pair_addr(idx4, lane_byte, 0));
@@ -201,21 +211,30 @@ void matmul_kernel(const MatmulParams p) {
 #pragma unroll
           for (int mt = 0; mt < MT; ++mt) {
             const f16x8 a = __builtin_bit_cast(f16x8, abuf[s][mt][j]);
-            cg[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                a, b, j == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : cg[mt], 0, 0, 0);
+            if constexpr (GROUPED) {
+              // the group's partial sum starts from zero and is rescaled below
+              cg[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                  a, b, j == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : cg[mt], 0, 0, 0);
+            } else {
+              macc[t][mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, macc[t][mt], 0, 0, 0);
+            }
           }
         }
+        if constexpr (GROUPED) {
+          const float sc = f16_bits_to_f32(sbuf[s][t]);
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
+          for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) macc[t][mt][e] = __builtin_fmaf(sc[t], cg[mt][e], macc[t][mt][e]);
+            for (int e = 0; e < 4; ++e) macc[t][mt][e] = __builtin_fmaf(sc, cg[mt][e], macc[t][mt][e]);
+        }
       }
     }
   };
 
   // Software pipeline: PF register slots; the load of step i + PF - 1 is
   // issued before step i is computed, so PF - 1 chunks are in flight during
-  // every compute step.
+  // every compute step. Loads are unconditional (see c_last); the compute of
+  // padding steps is skipped with a wave-uniform branch.
   static_for<PF - 1>([&](auto S) { issue(S, chunk(decltype(S)::value)); });
 
   build_pair_table<BITS, kThreads>(table, lut_lane, tid);
@@ -226,13 +245,13 @@ void matmul_kernel(const MatmulParams p) {
       constexpr int s = decltype(S)::value;
       const int i = i0 + s;
       issue(std::integral_constant<int, (s + PF - 1) % PF>{}, chunk(i + PF - 1));
-      compute(S, i < nmine ? 1.f : 0.f);
+      if (i < nmine) compute(S);
     });
   }
 
   // ---- combine the waves (fixed order) ------------------------------------
   __syncthreads();  // every wave is done with the table; reuse it
-  float* red = reinterpret_cast<float*>(table);  // [kWaves][ROWS][MROWS]
+  float* red = reinterpret_cast<float*>(table);  // [kWaves][MROWS][RP]
 #pragma unroll
   for (int t = 0; t < TPW; ++t) {
     if constexpr (!MFMA) {
@@ -241,14 +260,14 @@ void matmul_kernel(const MatmulParams p) {
         float v = gacc[t][m];
         v += __shfl_xor(v, 16);
         v += __shfl_xor(v, 32);
-        if (q == 0) red[(wave * ROWS + t * kTileRows + r) * MROWS + m] = v;
+        if (q == 0) red[(wave * MROWS + m) * RP + t * kTileRows + r] = v;
       }
     } else {
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          red[(wave * ROWS + t * kTileRows + r) * MROWS + mt * 16 + 4 * q + e] = macc[t][mt][e];
+          red[(wave * MROWS + mt * 16 + 4 * q + e) * RP + t * kTileRows + r] = macc[t][mt][e];
     }
   }
   __syncthreads();
@@ -259,7 +278,7 @@ void matmul_kernel(const MatmulParams p) {
     const int m = it / ROWS, row = it - m * ROWS;
     float v = 0.f;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) v += red[(w * ROWS + row) * MROWS + m];
+    for (int w = 0; w < kWaves; ++w) v += red[(w * MROWS + m) * RP + row];
     v *= tscale;
     const int n = tile0 * kTileRows + row;
     if (p.ksplit == 1) {
@@ -334,7 +353,9 @@ static hipError_t launch_t(const MatmulParams& p, hipStream_t s) {
   constexpr int PF = MFMA ? LUTQ_MFMA_PF : LUTQ_GEMV_PF;
   constexpr int TPW = MFMA ? LUTQ_MFMA_TPW : LUTQ_GEMV_TPW;
   constexpr int WAVES = MFMA ? LUTQ_MFMA_WAVES : LUTQ_GEMV_WAVES;
-  constexpr int OCC = MFMA ? LUTQ_MFMA_OCC : LUTQ_GEMV_OCC;
+  // GEMV with 4 or 8 batch rows needs more registers than the occupancy
+  // target of the 1-2 row kernels allows.
+  constexpr int OCC = MFMA ? LUTQ_MFMA_OCC : (MROWS <= 2 ? LUTQ_GEMV_OCC : 2);
   const int nrb = (p.ntiles + TPW - 1) / TPW;
   const dim3 grid((unsigned)nrb * (unsigned)p.ksplit);
   if (p.group != 0)
