@@ -179,8 +179,8 @@ def main():
 
     # ---- headline: batch-1 4-bit g128 GEMV, cold weights ------------------
     head = Case(lutq, torch, "int4_up_proj", None, 1, cold=True)
-    path, ksplit = lutq.plan(1, head.N, head.K, 4)
-    log(f"[bench] headline: {len(head.packed)} rotating copies, path={path}, ksplit={ksplit}")
+    hplan = lutq.plan(1, head.N, head.K, 4)
+    log(f"[bench] headline: {len(head.packed)} rotating copies, plan={hplan}")
     region_us = time_case(lutq, torch, head, args.steps, args.warmup)
     warm = Case.__new__(Case)
     warm.__dict__.update(head.__dict__)
@@ -197,7 +197,7 @@ def main():
         "bits_read_per_weight": round(head.bytes * 8 / (head.N * head.K), 4),
         "warm": {"us_per_call": round(w_region_us, 3),
                  "effective_GBps": round(head.bytes / (w_region_us * 1e-6) / 1e9, 1)},
-        "path": path, "ksplit": ksplit,
+        "plan": hplan,
     }
 
     # ---- batch 32: log table, Llama-70B up-projection shape ---------------
@@ -211,7 +211,7 @@ def main():
         wk_us = time_case(lutq, torch, warm32, max(20, args.steps // 4), args.warmup)
         tf = b32.flops / (k_us * 1e-6) / 1e12
         extra["batch32"] = {
-            "workload": "log4_70b", "N": b32.N, "K": b32.K, "M": 32, "path": p32[0],
+            "workload": "log4_70b", "N": b32.N, "K": b32.K, "M": 32, "plan": p32,
             "us_per_call": round(k_us, 3),
             "TFLOPs": round(tf, 1), "mfma_frac": round(tf / MFMA_F16_PEAK_TFLOPS, 4),
             "effective_GBps": round(b32.bytes / (k_us * 1e-6) / 1e9, 1),
@@ -256,8 +256,9 @@ def main():
 
 
 def sweep(lutq, torch, args):
-    """Every workload matrix at every batch size, both paths and the automatic
-    plan, cold weights; one JSON row per case on stderr."""
+    """Every workload matrix at every batch size, the automatic plan and each
+    kernel shape of both paths (GEMV up to 8 batch rows), cold weights; one
+    JSON row per case on stderr."""
     from synth import workloads
     rows = []
     for wname, w in workloads.WORKLOADS.items():
@@ -271,14 +272,17 @@ def sweep(lutq, torch, args):
                 case.y = torch.empty((M, base.N), dtype=torch.float16, device="cuda")
                 case.bytes = algorithmic_bytes(M, base.N, base.K, w.bits, w.group)
                 case.flops = 2 * M * base.N * base.K
-                for path in ("auto", "gemv", "mfma"):
-                    def call(lutq_, i, case=case, path=path):
+                shapes = [("auto", 0)] + [("mfma", t) for t in (2, 4, 8)]
+                if M <= 8:
+                    shapes += [("gemv", t) for t in (1, 2)]
+                for path, tiles in shapes:
+                    def call(lutq_, i, case=case, path=path, tiles=tiles):
                         lutq_.matmul(case.x, case.packed[i % len(case.packed)], case.lut,
-                                     case.scales, out=case.y, path=path)
+                                     case.scales, out=case.y, path=path, tiles=tiles)
                     case.call = call
                     us = time_case(lutq, torch, case, max(20, args.steps // 4), args.warmup)
                     row = {"workload": wname, "matrix": m.name, "N": base.N, "K": base.K,
-                           "M": M, "path": path, "us": round(us, 3),
+                           "M": M, "path": path, "tiles": tiles, "us": round(us, 3),
                            "GBps": round(case.bytes / (us * 1e-6) / 1e9, 1),
                            "TFLOPs": round(case.flops / (us * 1e-6) / 1e12, 2)}
                     if path == "auto":

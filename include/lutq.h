@@ -143,9 +143,13 @@ enum {
 
 typedef struct lutq_options {
   int32_t path;   /* LUTQ_PATH_*                                              */
-  int32_t ksplit; /* workgroups per 64-row block along K; 0 = automatic.
+  int32_t ksplit; /* workgroups per row block along K; 0 = automatic.
                      Clamped to the number of 128-code chunks.               */
-  int32_t reserved[6]; /* must be zero                                        */
+  int32_t tiles;  /* 16-row output tiles per wave (the workgroup covers
+                     16 * tiles rows); 0 = automatic. Needs an explicit
+                     path: GEMV takes 1 or 2, MFMA 2, 4 or 8; anything
+                     else gives LUTQ_EINVAL.                                 */
+  int32_t reserved[5]; /* must be zero                                        */
 } lutq_options_t;
 
 /* lutq_matmul with explicit options (host pointer; NULL = automatic). */
@@ -153,9 +157,12 @@ int lutq_matmul_ex(const uint16_t* x, const lutq_packed_t* packed, const uint16_
                    const uint16_t* scales, uint16_t* y, int M, int N, int K,
                    const lutq_options_t* opts, void* stream);
 
-/* The path and split lutq_matmul would choose (host-side heuristic only,
- * no device work). Writes *path and *ksplit. */
-int lutq_plan(int M, int N, int K, int bits, int* path, int* ksplit);
+/* The options lutq_matmul_ex resolves for this call (host-side heuristic
+ * only, no device work): `req` (host, may be NULL = all automatic) is
+ * validated as in lutq_matmul_ex and its automatic fields are filled in;
+ * the result goes to `out` (host). With several batch slices the shape is
+ * the one of the first slice, and all slices use it. */
+int lutq_plan(int M, int N, int K, int bits, const lutq_options_t* req, lutq_options_t* out);
 
 /* Static string for a status code. */
 const char* lutq_strerror(int status);

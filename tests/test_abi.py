@@ -122,16 +122,41 @@ def test_matmul_validates_before_launching(lib):
     assert call(opts=ctypes.byref(o)) == EINVAL
     o = _lib.Options(); o.reserved[3] = 1
     assert call(opts=ctypes.byref(o)) == EINVAL
+    for path, tiles in [(0, 2), (1, 8), (1, 4), (2, 1), (2, 3), (1, -1)]:
+        o = _lib.Options(); o.path, o.tiles = path, tiles
+        assert call(opts=ctypes.byref(o)) == EINVAL, (path, tiles)
     # nothing to do: M == 0 (no HIP call is made)
     assert call(M=0) == OK
     assert lib.lutq_unpack(None, P(0x1000), None) == EINVAL
 
 
 def test_plan_switches_paths_by_batch():
-    assert lutq.plan(1, 14336, 4096, 4)[0] == "gemv"
-    assert lutq.plan(32, 28672, 8192, 4)[0] == "mfma"
-    path, ks = lutq.plan(1, 1024, 1024, 4)
-    assert 1 <= ks <= 8
+    assert lutq.plan(1, 14336, 4096, 4)["path"] == "gemv"
+    assert lutq.plan(2, 14336, 4096, 4)["path"] == "gemv"
+    assert lutq.plan(3, 14336, 4096, 4)["path"] == "mfma"
+    assert lutq.plan(32, 28672, 8192, 4)["path"] == "mfma"
+
+
+def test_plan_shapes_and_split():
+    # Without a GPU the device is taken to have 256 compute units.
+    # Batch 32 on a wide matrix: 8 tiles per wave, no split.
+    assert lutq.plan(32, 28672, 8192, 4) == {"path": "mfma", "ksplit": 1, "tiles": 8}
+    # A batch slice of 16 rows keeps 4 tiles per wave.
+    assert lutq.plan(16, 28672, 8192, 4)["tiles"] == 4
+    # Narrow matrices: 2 tiles per wave, and K split until the row blocks
+    # cover the device (1024 rows = 32 blocks of 32 rows -> 8 splits).
+    assert lutq.plan(8, 1024, 4096, 4) == {"path": "mfma", "ksplit": 8, "tiles": 2}
+    # GEMV: 2 tiles per wave only when that still gives 2 row blocks per CU
+    assert lutq.plan(1, 14336, 4096, 4) == {"path": "gemv", "ksplit": 1, "tiles": 2}
+    assert lutq.plan(1, 4096, 4096, 4) == {"path": "gemv", "ksplit": 1, "tiles": 1}
+    assert lutq.plan(1, 1024, 4096, 4) == {"path": "gemv", "ksplit": 4, "tiles": 1}
+    # the split never exceeds the number of 128-code chunks
+    assert lutq.plan(1, 16, 256, 4)["ksplit"] == 2
+    # explicit fields are kept
+    assert lutq.plan(1, 14336, 4096, 4, path="mfma", tiles=8, ksplit=3) == \
+        {"path": "mfma", "ksplit": 3, "tiles": 8}
+    with pytest.raises(lutq.LutqError):
+        lutq.plan(1, 14336, 4096, 4, path="gemv", tiles=8)
 
 
 # -- the layout as documented in include/lutq.h -------------------------------

@@ -119,6 +119,33 @@ def test_parity_random(lutq, bits, table, group, N, K, M, path):
     assert_close(y, x, c, T, s, group)
 
 
+SHAPES = [("gemv", 1), ("gemv", 2), ("mfma", 2), ("mfma", 4), ("mfma", 8)]
+
+
+@pytest.mark.parametrize("path,tiles", SHAPES)
+@pytest.mark.parametrize("bits,table,group", [(4, "nf", 128), (3, "lloyd_max", 0), (2, "int", 256)])
+@pytest.mark.parametrize("M", [1, 5, 16, 32, 45])
+@pytest.mark.parametrize("ksplit", [1, 3])
+def test_parity_every_shape(lutq, path, tiles, bits, table, group, M, ksplit):
+    # 293 rows = 19 tiles: at 8 tiles per wave two full row blocks and a
+    # ragged third (3 tiles, the last one 5 rows); 45 batch rows = a full
+    # slice plus a ragged one on either path.
+    N, K = 293, 768
+    c, T, s, x = workloads.small_case(bits, table, group, M, N, K, seed=300 + bits + M)
+    y = run(lutq, c, T, s, x, bits, group, path=path, tiles=tiles, ksplit=ksplit)
+    assert_close(y, x, c, T, s, group)
+
+
+@pytest.mark.parametrize("path,tiles", SHAPES)
+def test_one_hot_every_shape(lutq, path, tiles):
+    N, K = 150, 256
+    c, T, s, _ = workloads.small_case(3, "lloyd_max", 128, 1, N, K, seed=60)
+    x = np.eye(K, dtype=np.float16)
+    y = run(lutq, c, T, s, x, 3, 128, path=path, tiles=tiles)
+    want = (T[c].astype(np.float32) * s[:, np.arange(K) // 128].astype(np.float32)).astype(np.float16)
+    assert np.array_equal(y.view(np.uint16), want.T.view(np.uint16))
+
+
 @pytest.mark.parametrize("ksplit", [1, 2, 3, 7, 100])
 @pytest.mark.parametrize("path", ["gemv", "mfma"])
 def test_parity_forced_k_splits(lutq, ksplit, path):

@@ -35,7 +35,7 @@ class PackedDesc(ctypes.Structure):
 
 class Options(ctypes.Structure):
     _fields_ = [("path", ctypes.c_int32), ("ksplit", ctypes.c_int32),
-                ("reserved", ctypes.c_int32 * 6)]
+                ("tiles", ctypes.c_int32), ("reserved", ctypes.c_int32 * 5)]
 
 
 class LutqError(RuntimeError):
@@ -75,7 +75,7 @@ def load_library():
     lib.lutq_matmul_ex.argtypes = [vp, ctypes.POINTER(PackedDesc), vp, vp, vp, i32, i32, i32,
                                    ctypes.POINTER(Options), vp]
     lib.lutq_matmul_ex.restype = i32
-    lib.lutq_plan.argtypes = [i32, i32, i32, i32, ctypes.POINTER(i32), ctypes.POINTER(i32)]
+    lib.lutq_plan.argtypes = [i32, i32, i32, i32, ctypes.POINTER(Options), ctypes.POINTER(Options)]
     lib.lutq_plan.restype = i32
     lib.lutq_strerror.argtypes = [i32]
     lib.lutq_strerror.restype = ctypes.c_char_p
@@ -99,13 +99,23 @@ def packed_bytes(N: int, K: int, bits: int, group: int) -> int:
     return int(_lib().lutq_packed_bytes(N, K, bits, group))
 
 
-def plan(M: int, N: int, K: int, bits: int):
-    """(path, ksplit) that lutq_matmul picks for this shape."""
-    path, ks = ctypes.c_int(0), ctypes.c_int(0)
-    rc = _lib().lutq_plan(M, N, K, bits, ctypes.byref(path), ctypes.byref(ks))
+def _options(path: str, ksplit: int, tiles: int) -> Options:
+    o = Options()
+    o.path = _PATHS[path]
+    o.ksplit = ksplit
+    o.tiles = tiles
+    return o
+
+
+def plan(M: int, N: int, K: int, bits: int, *, path: str = "auto", ksplit: int = 0,
+         tiles: int = 0) -> dict:
+    """lutq_plan: the options lutq_matmul_ex resolves for this call, as
+    {"path": "gemv" | "mfma", "ksplit": int, "tiles": int}."""
+    req, out = _options(path, ksplit, tiles), Options()
+    rc = _lib().lutq_plan(M, N, K, bits, ctypes.byref(req), ctypes.byref(out))
     if rc:
         raise LutqError(rc, "lutq_plan")
-    return {0: "auto", 1: "gemv", 2: "mfma"}[path.value], ks.value
+    return {"path": {1: "gemv", 2: "mfma"}[out.path], "ksplit": out.ksplit, "tiles": out.tiles}
 
 
 def _stream(device):
@@ -166,7 +176,8 @@ def unpack(p: Packed):
     return out
 
 
-def matmul(x, p: Packed, lut, scales, *, path: str = "auto", ksplit: int = 0, out=None):
+def matmul(x, p: Packed, lut, scales, *, path: str = "auto", ksplit: int = 0, tiles: int = 0,
+           out=None):
     """lutq_matmul_ex: y[M, N] = x[M, K] . dequant(p, lut, scales)^T, fp16 out."""
     import torch
     _need_cuda(x, "x", torch.float16)
@@ -179,9 +190,7 @@ def matmul(x, p: Packed, lut, scales, *, path: str = "auto", ksplit: int = 0, ou
         _need_cuda(out, "out", torch.float16)
         if tuple(out.shape) != (M, p.N):
             raise ValueError("out has the wrong shape")
-    opts = Options()
-    opts.path = _PATHS[path]
-    opts.ksplit = ksplit
+    opts = _options(path, ksplit, tiles)
     rc = _lib().lutq_matmul_ex(_ptr(x), ctypes.byref(p.desc), _ptr(lut), _ptr(scales), _ptr(out),
                                M, p.N, K, ctypes.byref(opts), _stream(x.device))
     if rc:

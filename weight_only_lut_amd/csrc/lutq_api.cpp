@@ -105,21 +105,49 @@ int cu_count() {
 // Batch rows above which the automatic plan switches from GEMV to MFMA.
 constexpr int kAutoGemvMaxM = 2;
 
-void plan(int M, int N, int K, int cus, int* path, int* ksplit) {
+int rows_per_launch(int path) {
+  return path == LUTQ_PATH_MFMA ? lutq::kMfmaMaxRows : lutq::kGemvMaxRows;
+}
+
+int kernel_path(int path) { return path == LUTQ_PATH_MFMA ? lutq::kPathMfma : lutq::kPathGemv; }
+
+// Checks the caller's options (NULL = all automatic) and copies them to *o.
+int read_options(const lutq_options_t* opts, lutq_options_t* o) {
+  std::memset(o, 0, sizeof *o);
+  if (!opts) return LUTQ_OK;
+  for (int i = 0; i < 5; ++i)
+    if (opts->reserved[i]) return LUTQ_EINVAL;
+  if (opts->path < LUTQ_PATH_AUTO || opts->path > LUTQ_PATH_MFMA || opts->ksplit < 0 ||
+      opts->tiles < 0)
+    return LUTQ_EINVAL;
+  if (opts->tiles &&
+      (opts->path == LUTQ_PATH_AUTO || !lutq::tiles_supported(kernel_path(opts->path), opts->tiles)))
+    return LUTQ_EINVAL;
+  *o = *opts;
+  return LUTQ_OK;
+}
+
+// Fills the automatic fields of *o (checked by read_options) for an
+// M x N x K product (M, N, K > 0).
+void plan(int M, int N, int K, int cus, lutq_options_t* o) {
   const int nchunks = K / lutq::kChunk;
-  if (*path == LUTQ_PATH_AUTO) *path = (M <= kAutoGemvMaxM) ? LUTQ_PATH_GEMV : LUTQ_PATH_MFMA;
-  const int kpath = *path == LUTQ_PATH_MFMA ? lutq::kPathMfma : lutq::kPathGemv;
-  const int rows = lutq::rows_per_workgroup(kpath);
-  const int nrb = (N + rows - 1) / rows;
-  if (*ksplit <= 0) {
+  if (o->path == LUTQ_PATH_AUTO) o->path = (M <= kAutoGemvMaxM) ? LUTQ_PATH_GEMV : LUTQ_PATH_MFMA;
+  const int kpath = kernel_path(o->path);
+  const int ntiles = (N + lutq::kTileRows - 1) / lutq::kTileRows;
+  if (o->tiles == 0) {
+    const int rl = rows_per_launch(o->path);
+    o->tiles = lutq::pick_tiles(kpath, M < rl ? M : rl, ntiles, cus);
+  }
+  const int nrb = (ntiles + o->tiles - 1) / o->tiles;
+  if (o->ksplit == 0) {
     // Split K across workgroups only when the matrix has too few row blocks
     // to give every CU work: the split costs a second pass over fp32
     // partials and an arrival counter per row block.
     int k = 1;
-    if (nrb > 0 && 2 * nrb <= cus) k = cus / nrb;
-    *ksplit = k;
+    if (2 * nrb <= cus) k = cus / nrb;
+    o->ksplit = k;
   }
-  if (*ksplit > nchunks) *ksplit = nchunks > 0 ? nchunks : 1;
+  if (o->ksplit > nchunks) o->ksplit = nchunks > 0 ? nchunks : 1;
 }
 
 }  // namespace
@@ -175,15 +203,17 @@ int lutq_unpack(const lutq_packed_t* packed, uint8_t* codes_out, void* stream) {
   return e == hipSuccess ? LUTQ_OK : hip_fail(e);
 }
 
-int lutq_plan(int M, int N, int K, int bits, int* path, int* ksplit) {
-  if (!path || !ksplit || M < 0) return LUTQ_EINVAL;
+int lutq_plan(int M, int N, int K, int bits, const lutq_options_t* req, lutq_options_t* out) {
+  if (!out || M < 0) return LUTQ_EINVAL;
   int rc = check_sizes(N, K);
   if (rc) return rc;
   if (bits < 2 || bits > 4) return LUTQ_EBITS;
   if (K % lutq::kChunk) return LUTQ_EGROUP;
-  *path = LUTQ_PATH_AUTO;
-  *ksplit = 0;
-  plan(M, N, K, cu_count(), path, ksplit);
+  lutq_options_t o;
+  rc = read_options(req, &o);
+  if (rc) return rc;
+  plan(M > 0 ? M : 1, N > 0 ? N : 1, K > 0 ? K : lutq::kChunk, cu_count(), &o);
+  *out = o;
   return LUTQ_OK;
 }
 
@@ -194,15 +224,9 @@ int lutq_matmul_ex(const uint16_t* x, const lutq_packed_t* packed, const uint16_
   if (rc) return rc;
   if (M < 0 || N < 0 || K < 0) return LUTQ_EINVAL;
   if (N != packed->N || K != packed->K) return LUTQ_EMISMATCH;
-  int path = LUTQ_PATH_AUTO, ksplit = 0;
-  if (opts) {
-    for (int i = 0; i < 6; ++i)
-      if (opts->reserved[i]) return LUTQ_EINVAL;
-    if (opts->path < LUTQ_PATH_AUTO || opts->path > LUTQ_PATH_MFMA || opts->ksplit < 0)
-      return LUTQ_EINVAL;
-    path = opts->path;
-    ksplit = opts->ksplit;
-  }
+  lutq_options_t o;
+  rc = read_options(opts, &o);
+  if (rc) return rc;
   if (M == 0 || N == 0) return LUTQ_OK;
   if (!y) return LUTQ_EINVAL;
   if (!aligned(y, 2)) return LUTQ_EALIGN;
@@ -215,8 +239,10 @@ int lutq_matmul_ex(const uint16_t* x, const lutq_packed_t* packed, const uint16_
   if (!aligned(x, 16)) return LUTQ_EALIGN;
   if (!aligned(lut, 4) || !aligned(scales, 2)) return LUTQ_EALIGN;
 
-  plan(M, N, K, cu_count(), &path, &ksplit);
-  const int rows_per_launch = (path == LUTQ_PATH_MFMA) ? lutq::kMfmaMaxRows : lutq::kGemvMaxRows;
+  plan(M, N, K, cu_count(), &o);
+  const int path = kernel_path(o.path);
+  const int ksplit = o.ksplit;
+  const int rl = rows_per_launch(o.path);
 
   lutq::MatmulParams p;
   std::memset(&p, 0, sizeof p);
@@ -231,21 +257,19 @@ int lutq_matmul_ex(const uint16_t* x, const lutq_packed_t* packed, const uint16_
   p.ksplit = ksplit;
   p.cps = (p.nchunks + ksplit - 1) / ksplit;
   if (ksplit > 1) {
-    const int rows = lutq::rows_per_workgroup(path == LUTQ_PATH_MFMA ? lutq::kPathMfma
-                                                                     : lutq::kPathGemv);
-    const size_t nrb = (size_t)(N + rows - 1) / rows;
+    const size_t nrb = (size_t)(p.ntiles + o.tiles - 1) / o.tiles;
     if (nrb * sizeof(uint32_t) > kCounterBytes) return LUTQ_EUNSUPPORTED;
-    const size_t pbytes = nrb * (size_t)ksplit * lutq::kMfmaMaxRows * rows * sizeof(float);
+    const size_t rows = (size_t)o.tiles * lutq::kTileRows;
+    const size_t pbytes = nrb * (size_t)ksplit * rl * rows * sizeof(float);
     rc = get_scratch(stream, pbytes, &p.partial, &p.counters);
     if (rc) return rc;
   }
   const int bits = packed->bits;
-  for (int m0 = 0; m0 < M; m0 += rows_per_launch) {
-    p.M = (M - m0) < rows_per_launch ? (M - m0) : rows_per_launch;
+  for (int m0 = 0; m0 < M; m0 += rl) {
+    p.M = (M - m0) < rl ? (M - m0) : rl;
     p.x = x + (size_t)m0 * K;
     p.y = y + (size_t)m0 * N;
-    hipError_t e = lutq::launch_matmul(p, bits, path == LUTQ_PATH_MFMA ? lutq::kPathMfma
-                                                                       : lutq::kPathGemv, s);
+    hipError_t e = lutq::launch_matmul(p, bits, path, o.tiles, s);
     if (e != hipSuccess) return hip_fail(e);
   }
   return LUTQ_OK;

@@ -31,8 +31,15 @@ enum Path { kPathGemv = 1, kPathMfma = 2 };
 constexpr int kGemvMaxRows = 8;
 constexpr int kMfmaMaxRows = 32;
 
-// Output rows one matmul workgroup covers on a path (a multiple of 16).
-int rows_per_workgroup(int path);
+// Shapes of the matmul workgroup compiled for each path, as the number of
+// 16-row output tiles each wave covers (every wave of a workgroup covers the
+// same tiles and takes its own K chunks). Wider shapes share each activation
+// fragment across more tiles; narrower ones give small matrices more
+// workgroups.
+bool tiles_supported(int path, int tiles);
+// The shape the automatic plan picks for a launch of `mrows` batch rows over
+// `ntiles` tiles on a device with `cus` compute units.
+int pick_tiles(int path, int mrows, int ntiles, int cus);
 
 hipError_t launch_repack(const uint8_t* codes, uint8_t* dst, int N, int K, int bits,
                          hipStream_t s);
@@ -41,7 +48,7 @@ hipError_t launch_unpack(const uint8_t* src, uint8_t* codes, int N, int K, int b
 hipError_t launch_fill_u16(uint16_t* p, long long n, uint16_t v, hipStream_t s);
 
 // One launch over rows [0, p.M) of x; p.M <= kGemvMaxRows (GEMV) or
-// kMfmaMaxRows (MFMA).
-hipError_t launch_matmul(const MatmulParams& p, int bits, int path, hipStream_t s);
+// kMfmaMaxRows (MFMA); `tiles` passes tiles_supported(path, tiles).
+hipError_t launch_matmul(const MatmulParams& p, int bits, int path, int tiles, hipStream_t s);
 
 }  // namespace lutq

@@ -318,70 +318,79 @@ void matmul_kernel(const MatmulParams p) {
   if (tid == 0) __hip_atomic_store(p.counters + rb, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Kernel shapes (overridable at build time for tuning).
-#ifndef LUTQ_GEMV_TPW
-#define LUTQ_GEMV_TPW 2
-#endif
-#ifndef LUTQ_GEMV_WAVES
-#define LUTQ_GEMV_WAVES 8
-#endif
-#ifndef LUTQ_GEMV_PF
-#define LUTQ_GEMV_PF 2
-#endif
-#ifndef LUTQ_GEMV_OCC
-#define LUTQ_GEMV_OCC 4
-#endif
-#ifndef LUTQ_MFMA_TPW
-#define LUTQ_MFMA_TPW 4
-#endif
-#ifndef LUTQ_MFMA_WAVES
-#define LUTQ_MFMA_WAVES 4
-#endif
-#ifndef LUTQ_MFMA_PF
-#define LUTQ_MFMA_PF 2
-#endif
-#ifndef LUTQ_MFMA_OCC
-#define LUTQ_MFMA_OCC 2
-#endif
+// Kernel shapes. GEMV: 8 waves, each covering 1 or 2 tiles. MFMA: 8 tiles
+// per wave with 4 waves (batch 32 on wide matrices: each activation fragment
+// feeds 8 tiles), 4 tiles with 4 waves, or 2 tiles with 8 waves (narrow
+// matrices, which need many workgroups to fill the device).
+constexpr int kPf = 2;
 
-int rows_per_workgroup(int path) {
-  return (path == kPathMfma ? LUTQ_MFMA_TPW : LUTQ_GEMV_TPW) * kTileRows;
+bool tiles_supported(int path, int tiles) {
+  if (path == kPathMfma) return tiles == 2 || tiles == 4 || tiles == 8;
+  return tiles == 1 || tiles == 2;
 }
 
-template <int BITS, bool MFMA, int MROWS>
+// Measured on MI355X over the Llama-3-8B and Llama-70B projection shapes: the
+// widest shape that still gives most CUs a workgroup wins, except that 8
+// tiles only pay at 32 batch rows.
+int pick_tiles(int path, int mrows, int ntiles, int cus) {
+  if (path != kPathMfma) return ntiles >= 2 * cus ? 2 : 1;
+  if (mrows > 16 && ntiles >= 6 * cus) return 8;
+  if (ntiles >= 2 * cus) return 4;
+  return 2;
+}
+
+template <int BITS, bool MFMA, int MROWS, int TPW, int WAVES, int OCC>
 static hipError_t launch_t(const MatmulParams& p, hipStream_t s) {
-  constexpr int PF = MFMA ? LUTQ_MFMA_PF : LUTQ_GEMV_PF;
-  constexpr int TPW = MFMA ? LUTQ_MFMA_TPW : LUTQ_GEMV_TPW;
-  constexpr int WAVES = MFMA ? LUTQ_MFMA_WAVES : LUTQ_GEMV_WAVES;
-  // GEMV with 4 or 8 batch rows needs more registers than the occupancy
-  // target of the 1-2 row kernels allows.
-  constexpr int OCC = MFMA ? LUTQ_MFMA_OCC : (MROWS <= 2 ? LUTQ_GEMV_OCC : 2);
   const int nrb = (p.ntiles + TPW - 1) / TPW;
   const dim3 grid((unsigned)nrb * (unsigned)p.ksplit);
+  // Grouped scales at 32 batch rows x 8 tiles need more than the 256
+  // registers of two waves per SIMD; this shape runs on few enough
+  // workgroups that one wave per SIMD costs little.
+  constexpr int OCC_G = (MFMA && MROWS == 32 && TPW == 8) ? 1 : OCC;
   if (p.group != 0)
-    matmul_kernel<BITS, MFMA, MROWS, true, PF, TPW, WAVES, OCC><<<grid, WAVES * kWave, 0, s>>>(p);
+    matmul_kernel<BITS, MFMA, MROWS, true, kPf, TPW, WAVES, OCC_G><<<grid, WAVES * kWave, 0, s>>>(p);
   else
-    matmul_kernel<BITS, MFMA, MROWS, false, PF, TPW, WAVES, OCC><<<grid, WAVES * kWave, 0, s>>>(p);
+    matmul_kernel<BITS, MFMA, MROWS, false, kPf, TPW, WAVES, OCC><<<grid, WAVES * kWave, 0, s>>>(p);
   return hipGetLastError();
 }
 
-template <int BITS>
-static hipError_t launch_bits(const MatmulParams& p, int path, hipStream_t s) {
-  if (path == kPathMfma) {
-    if (p.M <= 16) return launch_t<BITS, true, 16>(p, s);
-    return launch_t<BITS, true, 32>(p, s);
+template <int BITS, int MROWS>
+static hipError_t launch_mfma(const MatmulParams& p, int tiles, hipStream_t s) {
+  switch (tiles) {
+    case 8: return launch_t<BITS, true, MROWS, 8, 4, 2>(p, s);
+    case 4: return launch_t<BITS, true, MROWS, 4, 4, 2>(p, s);
+    default: return launch_t<BITS, true, MROWS, 2, 8, 2>(p, s);
   }
-  if (p.M <= 1) return launch_t<BITS, false, 1>(p, s);
-  if (p.M <= 2) return launch_t<BITS, false, 2>(p, s);
-  if (p.M <= 4) return launch_t<BITS, false, 4>(p, s);
-  return launch_t<BITS, false, 8>(p, s);
 }
 
-hipError_t launch_matmul(const MatmulParams& p, int bits, int path, hipStream_t s) {
+// GEMV with 4 or 8 batch rows needs more registers than the occupancy target
+// of the 1-2 row kernels allows.
+template <int BITS, int MROWS>
+static hipError_t launch_gemv(const MatmulParams& p, int tiles, hipStream_t s) {
+  constexpr int OCC = MROWS <= 2 ? 4 : 2;
+  switch (tiles) {
+    case 1: return launch_t<BITS, false, MROWS, 1, 8, OCC>(p, s);
+    default: return launch_t<BITS, false, MROWS, 2, 8, OCC>(p, s);
+  }
+}
+
+template <int BITS>
+static hipError_t launch_bits(const MatmulParams& p, int path, int tiles, hipStream_t s) {
+  if (path == kPathMfma) {
+    if (p.M <= 16) return launch_mfma<BITS, 16>(p, tiles, s);
+    return launch_mfma<BITS, 32>(p, tiles, s);
+  }
+  if (p.M <= 1) return launch_gemv<BITS, 1>(p, tiles, s);
+  if (p.M <= 2) return launch_gemv<BITS, 2>(p, tiles, s);
+  if (p.M <= 4) return launch_gemv<BITS, 4>(p, tiles, s);
+  return launch_gemv<BITS, 8>(p, tiles, s);
+}
+
+hipError_t launch_matmul(const MatmulParams& p, int bits, int path, int tiles, hipStream_t s) {
   switch (bits) {
-    case 2: return launch_bits<2>(p, path, s);
-    case 3: return launch_bits<3>(p, path, s);
-    default: return launch_bits<4>(p, path, s);
+    case 2: return launch_bits<2>(p, path, tiles, s);
+    case 3: return launch_bits<3>(p, path, tiles, s);
+    default: return launch_bits<4>(p, path, tiles, s);
   }
 }
 
