@@ -29,6 +29,13 @@ constexpr int kWave = 64;
 constexpr int kPairEntries = 256;
 constexpr int kCopies = 64;
 constexpr int kTableWords = kPairEntries * kCopies;  // 16384 dwords = 64 KiB
+// Word 3 of a raw (unstructured, stride 0) buffer resource on gfx9-family
+// GPUs: 32-bit data format, no swizzle; offsets are bytes, range-checked
+// against the record count.
+constexpr int kBufferRsrcWord3 = 0x00020000;
+// A buffer offset past any record count this library builds (x slices are
+// at most 32 rows x 2^20 fp16 = 64 MiB, plus chunk offsets below 2^22).
+constexpr uint32_t kOutOfRange = 0x80000000u;
 
 typedef _Float16 f16;
 typedef f16 f16x2 __attribute__((ext_vector_type(2)));
@@ -160,29 +167,36 @@ __device__ __forceinline__ void build_pair_table(uint32_t* table, uint32_t lut_l
   for (int k = 0; k < C; ++k) dst[(k + idx) & (C - 1)] = q;
 }
 
-// DPP row_newbcast:n -- every lane of each 16-lane row reads lane n of that
-// row. `n` must fold to a constant after unrolling.
-__device__ __forceinline__ uint32_t row_newbcast(uint32_t v, int n) {
-  switch (n) {
-    case 0: return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x150, 0xF, 0xF, false);
-    case 1: return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x151, 0xF, 0xF, false);
-    case 2: return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x152, 0xF, 0xF, false);
-    case 3: return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x153, 0xF, 0xF, false);
-    case 4: return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x154, 0xF, 0xF, false);
-    case 5: return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x155, 0xF, 0xF, false);
-    case 6: return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x156, 0xF, 0xF, false);
-    case 7: return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x157, 0xF, 0xF, false);
-    case 8: return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x158, 0xF, 0xF, false);
-    case 9: return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x159, 0xF, 0xF, false);
-    case 10: return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x15a, 0xF, 0xF, false);
-    case 11: return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x15b, 0xF, 0xF, false);
-    case 12: return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x15c, 0xF, 0xF, false);
-    case 13: return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x15d, 0xF, 0xF, false);
-    case 14: return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x15e, 0xF, 0xF, false);
-    case 15: return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x15f, 0xF, 0xF, false);
-    default: return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x15f, 0xF, 0xF, false);
+// acc += dot(x from lane 4j+i of this lane's 16-lane row, p_i), i = 0..3, in
+// that order: four v_dot2c_f32_f16 whose DPP row_newbcast reads the
+// activation pair straight from the broadcasting lane, so no separate
+// broadcast move is issued. `j` must fold to a constant.
+// The compiler inserts no wait states around inline assembly, so the block
+// carries its own: s_nop 1 before (a DPP read of a VGPR needs 2 after a
+// VALU write of it), s_nop 3 after (measured on gfx950: a plain VALU read
+// of a v_dot2c_f32_f16_dpp result within 2 wait states sees the value from
+// before the block; 3 suffice, 4 are given). DPP dots chained on one
+// accumulator need none between them.
+#define LUTQ_DOT2_BCAST4(A, B, C, D)                                                 \
+  asm("s_nop 1\n\t"                                                                 \
+      "v_dot2c_f32_f16_dpp %0, %1, %2 row_newbcast:" #A " row_mask:0xf bank_mask:0xf\n\t" \
+      "v_dot2c_f32_f16_dpp %0, %1, %3 row_newbcast:" #B " row_mask:0xf bank_mask:0xf\n\t" \
+      "v_dot2c_f32_f16_dpp %0, %1, %4 row_newbcast:" #C " row_mask:0xf bank_mask:0xf\n\t" \
+      "v_dot2c_f32_f16_dpp %0, %1, %5 row_newbcast:" #D " row_mask:0xf bank_mask:0xf\n\t" \
+      "s_nop 3"                                                                      \
+      : "+v"(acc)                                                                    \
+      : "v"(x), "v"(p0), "v"(p1), "v"(p2), "v"(p3))
+__device__ __forceinline__ float dot2_bcast4(float acc, uint32_t x, uint32_t p0, uint32_t p1,
+                                             uint32_t p2, uint32_t p3, int j) {
+  switch (j) {
+    case 0: LUTQ_DOT2_BCAST4(0, 1, 2, 3); break;
+    case 1: LUTQ_DOT2_BCAST4(4, 5, 6, 7); break;
+    case 2: LUTQ_DOT2_BCAST4(8, 9, 10, 11); break;
+    default: LUTQ_DOT2_BCAST4(12, 13, 14, 15); break;
   }
+  return acc;
 }
+#undef LUTQ_DOT2_BCAST4
 
 // Calls f(std::integral_constant<int, I>{}) for I = 0 .. N-1 (unrolled).
 template <typename F, int... I>

@@ -105,11 +105,17 @@ void matmul_kernel(const MatmulParams p) {
   // the inner loop free of branches.
   // GEMV: lane 16q + 4j + i holds the pair x[128c + 32j + 8q + 2i .. +1]
   const uint32_t gx_boff = 2u * (32 * (r >> 2) + 8 * q + 2 * (r & 3));
-  // MFMA: lane (row r, quarter q) holds x[row][128c + 32j + 8q .. +7]
+  // MFMA: lane (row r, quarter q) holds x[row][128c + 32j + 8q .. +7]. The
+  // activations are read through a buffer resource covering the M rows of
+  // this launch; rows at or past M get an offset beyond it, which the
+  // hardware answers with zeros without touching memory.
+  const __amdgpu_buffer_rsrc_t xrsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(p.x), 0, 2 * p.M * p.K, kBufferRsrcWord3);
   uint32_t aboff[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
-    aboff[mt] = 2u * ((uint32_t)min(mt * 16 + r, p.M - 1) * (uint32_t)p.K + 8 * q);
+    aboff[mt] = mt * 16 + r < p.M ? 2u * ((uint32_t)(mt * 16 + r) * (uint32_t)p.K + 8 * q)
+                                  : kOutOfRange;
 
   SlotRegs<BITS> cbuf[PF][TPW];
   uint16_t sbuf[PF][TPW];
@@ -135,11 +141,13 @@ void matmul_kernel(const MatmulParams p) {
         xbuf[s][m] = *reinterpret_cast<const uint32_t*>(xm + gx_boff);
       }
     } else {
+      const uint32_t cb = (uint32_t)c * (2 * kChunk);
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          abuf[s][mt][j] = *reinterpret_cast<const u32x4*>(xc + 64 * j + aboff[mt]);
+          abuf[s][mt][j] = __builtin_bit_cast(
+              u32x4, __builtin_amdgcn_raw_buffer_load_b128(xrsrc, aboff[mt] + cb + 64 * j, 0, 0));
     }
   };
 
@@ -169,18 +177,14 @@ void matmul_kernel(const MatmulParams p) {
 #pragma unroll
         for (int t = 0; t < TPW; ++t) idx4[t] = step_indices<BITS>(cbuf[s][t], j);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          // row_newbcast:(4j+i): every lane of a 16-lane row reads lane 4j+i of that row
-          uint32_t xv[MROWS];
+        for (int t = 0; t < TPW; ++t) {
+          uint32_t pr[4];
 #pragma unroll
-          for (int m = 0; m < MROWS; ++m) xv[m] = row_newbcast(xbuf[s][m], 4 * j + i);
+          for (int i = 0; i < 4; ++i) pr[i] = lds_load(table, pair_addr(idx4[t], lane_byte, i));
+          // pair i of k-step j meets the activations of lane 4j+i of the row
 #pragma unroll
-          for (int t = 0; t < TPW; ++t) {
-            const uint32_t pr = lds_load(table, pair_addr(idx4[t], lane_byte, i));
-#pragma unroll
-            for (int m = 0; m < MROWS; ++m)
-              cs[t][m] = __builtin_amdgcn_fdot2(as_f16x2(xv[m]), as_f16x2(pr), cs[t][m], false);
-          }
+          for (int m = 0; m < MROWS; ++m)
+            cs[t][m] = dot2_bcast4(cs[t][m], xbuf[s][m], pr[0], pr[1], pr[2], pr[3], j);
         }
       }
 #pragma unroll
