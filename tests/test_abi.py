@@ -131,10 +131,17 @@ def test_matmul_validates_before_launching(lib):
 
 
 def test_plan_switches_paths_by_batch():
+    # Without a GPU the device is taken to have 256 compute units.
+    # wide matrices (>= 512 tiles): GEMV for one row only
     assert lutq.plan(1, 14336, 4096, 4)["path"] == "gemv"
-    assert lutq.plan(2, 14336, 4096, 4)["path"] == "gemv"
-    assert lutq.plan(3, 14336, 4096, 4)["path"] == "mfma"
+    assert lutq.plan(2, 14336, 4096, 4)["path"] == "mfma"
     assert lutq.plan(32, 28672, 8192, 4)["path"] == "mfma"
+    # 4096 rows = 256 tiles: GEMV up to 4 rows
+    assert lutq.plan(4, 4096, 14336, 3)["path"] == "gemv"
+    assert lutq.plan(5, 4096, 14336, 3)["path"] == "mfma"
+    # 1024 rows = 64 tiles: GEMV up to 8 rows
+    assert lutq.plan(8, 1024, 4096, 4)["path"] == "gemv"
+    assert lutq.plan(9, 1024, 4096, 4)["path"] == "mfma"
 
 
 def test_plan_shapes_and_split():
@@ -145,7 +152,7 @@ def test_plan_shapes_and_split():
     assert lutq.plan(16, 28672, 8192, 4)["tiles"] == 4
     # Narrow matrices: 2 tiles per wave, and K split until the row blocks
     # cover the device (1024 rows = 32 blocks of 32 rows -> 8 splits).
-    assert lutq.plan(8, 1024, 4096, 4) == {"path": "mfma", "ksplit": 8, "tiles": 2}
+    assert lutq.plan(16, 1024, 4096, 4) == {"path": "mfma", "ksplit": 8, "tiles": 2}
     # GEMV: 2 tiles per wave only when that still gives 2 row blocks per CU
     assert lutq.plan(1, 14336, 4096, 4) == {"path": "gemv", "ksplit": 1, "tiles": 2}
     assert lutq.plan(1, 4096, 4096, 4) == {"path": "gemv", "ksplit": 1, "tiles": 1}

@@ -102,9 +102,6 @@ int cu_count() {
   return n;
 }
 
-// Batch rows above which the automatic plan switches from GEMV to MFMA.
-constexpr int kAutoGemvMaxM = 2;
-
 int rows_per_launch(int path) {
   return path == LUTQ_PATH_MFMA ? lutq::kMfmaMaxRows : lutq::kGemvMaxRows;
 }
@@ -131,9 +128,16 @@ int read_options(const lutq_options_t* opts, lutq_options_t* o) {
 // M x N x K product (M, N, K > 0).
 void plan(int M, int N, int K, int cus, lutq_options_t* o) {
   const int nchunks = K / lutq::kChunk;
-  if (o->path == LUTQ_PATH_AUTO) o->path = (M <= kAutoGemvMaxM) ? LUTQ_PATH_GEMV : LUTQ_PATH_MFMA;
-  const int kpath = kernel_path(o->path);
   const int ntiles = (N + lutq::kTileRows - 1) / lutq::kTileRows;
+  if (o->path == LUTQ_PATH_AUTO) {
+    // Batch rows up to which GEMV beats MFMA (measured on MI355X over the
+    // Llama projection shapes): on wide matrices MFMA wins from 2 rows; on
+    // narrow ones, which run GEMV at one tile per wave, GEMV keeps up to 4
+    // rows, and up to 8 when there are at most half as many tiles as CUs.
+    const int gemv_max = ntiles >= 2 * cus ? 1 : (2 * ntiles <= cus ? 8 : 4);
+    o->path = M <= gemv_max ? LUTQ_PATH_GEMV : LUTQ_PATH_MFMA;
+  }
+  const int kpath = kernel_path(o->path);
   if (o->tiles == 0) {
     const int rl = rows_per_launch(o->path);
     o->tiles = lutq::pick_tiles(kpath, M < rl ? M : rl, ntiles, cus);

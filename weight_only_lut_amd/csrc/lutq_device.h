@@ -33,9 +33,12 @@ constexpr int kTableWords = kPairEntries * kCopies;  // 16384 dwords = 64 KiB
 // GPUs: 32-bit data format, no swizzle; offsets are bytes, range-checked
 // against the record count.
 constexpr int kBufferRsrcWord3 = 0x00020000;
-// A buffer offset past any record count this library builds (x slices are
-// at most 32 rows x 2^20 fp16 = 64 MiB, plus chunk offsets below 2^22).
+// Buffer offsets past the record count of every resource the kernels build
+// (each spans at most 64 MiB): kOutOfRange marks a pipeline step past the
+// wave's last chunk, kRowOutOfRange a batch row past M. Either may be added
+// to the other and to an in-resource offset without wrapping 32 bits.
 constexpr uint32_t kOutOfRange = 0x80000000u;
+constexpr uint32_t kRowOutOfRange = 0x40000000u;
 
 typedef _Float16 f16;
 typedef f16 f16x2 __attribute__((ext_vector_type(2)));
@@ -54,17 +57,28 @@ template <int BITS> struct Slot {
 // Codes of one lane slot in registers.
 template <int BITS> struct SlotRegs { uint32_t d[BITS]; };
 
+// A raw buffer resource over `bytes` bytes at `base`. Loads through it at
+// an offset at or past `bytes` return zeros without a memory access.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes,
+                                           kBufferRsrcWord3);
+}
+
+// Cache policy of the code stream: nontemporal (read once).
+constexpr int kNontemporal = 2;
+
+// One lane slot of codes at byte offset `off` of the resource.
 template <int BITS>
-__device__ __forceinline__ SlotRegs<BITS> load_slot(const uint8_t* p) {
+__device__ __forceinline__ SlotRegs<BITS> load_slot(__amdgpu_buffer_rsrc_t rs, uint32_t off) {
   SlotRegs<BITS> r;
   if constexpr (BITS == 4) {
-    u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    const u32x4 v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, kNontemporal));
     r.d[0] = v.x; r.d[1] = v.y; r.d[2] = v.z; r.d[3] = v.w;
   } else if constexpr (BITS == 3) {
-    u32x3 v = __builtin_nontemporal_load(reinterpret_cast<const u32x3*>(p));
+    const u32x3 v = __builtin_bit_cast(u32x3, __builtin_amdgcn_raw_buffer_load_b96(rs, off, 0, kNontemporal));
     r.d[0] = v.x; r.d[1] = v.y; r.d[2] = v.z;
   } else {
-    u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+    const u32x2 v = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, off, 0, kNontemporal));
     r.d[0] = v.x; r.d[1] = v.y;
   }
   return r;

@@ -78,76 +78,86 @@ void matmul_kernel(const MatmulParams p) {
   // this wave's chunks: cw, cw + WAVES, cw + 2 WAVES, ... (nmine of them)
   const int cw = c_begin + wave;
   const int nmine = span > wave ? (span - wave + kWaves - 1) / kWaves : 0;
-  // Every step of the pipeline issues the same loads, so the in-order load
-  // counter can be waited on precisely: steps past the wave's last chunk
-  // re-read a valid chunk of this block and are not computed.
-  const int c_last = min(p.nchunks - 1, max(c_begin, c_end - 1));
   const int niter = (nmine + PF - 1) / PF * PF;
   const int tile0 = rb * TPW;
   const int cpg = GROUPED ? p.group / kChunk : 1;       // chunks per group
   const int gpr = GROUPED ? p.K / p.group : 0;          // groups per row
 
-  // Tiles past the end of the matrix (in the last row block) re-read the
-  // last tile: the loads stay in bounds and the compute stays branch-free;
-  // their rows are >= N and are never stored. Bases are wave-uniform
-  // (SGPRs); per-lane parts are 32-bit byte offsets.
-  const uint8_t* tbase[TPW];
-  uint32_t sboff[TPW];
-#pragma unroll
-  for (int t = 0; t < TPW; ++t) {
-    const int tile = min(tile0 + t, p.ntiles - 1);
-    tbase[t] = p.packed + (size_t)tile * p.nchunks * BLOCK;
-    sboff[t] = 2u * (uint32_t)min(p.N - 1, (tile0 + t) * kTileRows + r) * (uint32_t)gpr;
-  }
+  // Every pipeline step issues the same loads, so the in-order load counter
+  // is waited on exactly. The loads go through raw buffer resources that
+  // cover exactly this workgroup's data; steps past the wave's last chunk
+  // use an out-of-range offset, and tiles and rows past the end of the
+  // matrix or batch fall outside the resource, so they read zeros without
+  // a memory access. Their results are never stored.
+  const int tiles_here = min(TPW, p.ntiles - tile0);
+  const uint32_t tile_bytes = (uint32_t)p.nchunks * BLOCK;
+  const __amdgpu_buffer_rsrc_t crsrc =
+      make_rsrc(p.packed + (size_t)tile0 * tile_bytes, (uint32_t)tiles_here * tile_bytes);
   const uint32_t lane_off = (uint32_t)lane * SLOT;
+  uint32_t coff[TPW];
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) coff[t] = (uint32_t)t * tile_bytes + lane_off;
 
-  // Activation rows past M re-read row M-1 (never stored), again to keep
-  // the inner loop free of branches.
-  // GEMV: lane 16q + 4j + i holds the pair x[128c + 32j + 8q + 2i .. +1]
-  const uint32_t gx_boff = 2u * (32 * (r >> 2) + 8 * q + 2 * (r & 3));
-  // MFMA: lane (row r, quarter q) holds x[row][128c + 32j + 8q .. +7]. The
-  // activations are read through a buffer resource covering the M rows of
-  // this launch; rows at or past M get an offset beyond it, which the
-  // hardware answers with zeros without touching memory.
-  const __amdgpu_buffer_rsrc_t xrsrc = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t*>(p.x), 0, 2 * p.M * p.K, kBufferRsrcWord3);
+  // scales of this block's rows: [rows][groups]; lane row = 16 t + r
+  const int row0 = tile0 * kTileRows;
+  const uint32_t rows_here = (uint32_t)min(ROWS, p.N - row0);
+  const __amdgpu_buffer_rsrc_t srsrc =
+      make_rsrc(p.scales + (size_t)row0 * gpr, GROUPED ? rows_here * (uint32_t)gpr * 2u : 0u);
+  uint32_t soff[TPW];
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) soff[t] = 2u * (uint32_t)(t * kTileRows + r) * (uint32_t)gpr;
+
+  // activations of this launch's M rows
+  const __amdgpu_buffer_rsrc_t xrsrc =
+      make_rsrc(p.x, 2u * (uint32_t)p.M * (uint32_t)p.K);
+  // GEMV: lane 16q + 4j + i holds the pair x[m][128c + 32j + 8q + 2i .. +1]
+  uint32_t xoff[MFMA ? 1 : MROWS];
+  if constexpr (!MFMA) {
+    const uint32_t gx_boff = 2u * (32 * (r >> 2) + 8 * q + 2 * (r & 3));
+#pragma unroll
+    for (int m = 0; m < MROWS; ++m)
+      xoff[m] = m < p.M ? 2u * (uint32_t)m * (uint32_t)p.K + gx_boff : kRowOutOfRange;
+  }
+  // MFMA: lane (row r, quarter q) holds x[row][128c + 32j + 8q .. +7]
   uint32_t aboff[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
     aboff[mt] = mt * 16 + r < p.M ? 2u * ((uint32_t)(mt * 16 + r) * (uint32_t)p.K + 8 * q)
-                                  : kOutOfRange;
+                                  : kRowOutOfRange;
 
   SlotRegs<BITS> cbuf[PF][TPW];
   uint16_t sbuf[PF][TPW];
   uint32_t xbuf[PF][MFMA ? 1 : MROWS];
   u32x4 abuf[PF][MT][MFMA ? 4 : 1];
 
-  auto chunk = [&](int i) { return min(cw + i * kWaves, c_last); };
+  // chunk of pipeline step i, or -1 past the wave's last chunk
+  auto chunk = [&](int i) { return i < nmine ? cw + i * kWaves : -1; };
 
   auto issue = [&](auto S, int c) {
     constexpr int s = decltype(S)::value;
-    const int gidx = cpg == 1 ? c : c / cpg;
-    const char* sbase = reinterpret_cast<const char*>(p.scales + gidx);
+    const bool live = c >= 0;  // wave-uniform
+    const uint32_t cb = live ? (uint32_t)c * BLOCK : kOutOfRange;
+    uint32_t sb = kOutOfRange;
+    if constexpr (GROUPED)
+      if (live) sb = 2u * (cpg == 1 ? (uint32_t)c : (uint32_t)c / (uint32_t)cpg);
 #pragma unroll
     for (int t = 0; t < TPW; ++t) {
-      cbuf[s][t] = load_slot<BITS>(tbase[t] + (size_t)c * BLOCK + lane_off);
-      if constexpr (GROUPED) sbuf[s][t] = *reinterpret_cast<const uint16_t*>(sbase + sboff[t]);
+      cbuf[s][t] = load_slot<BITS>(crsrc, coff[t] + cb);
+      if constexpr (GROUPED)
+        sbuf[s][t] = __builtin_amdgcn_raw_buffer_load_b16(srsrc, soff[t] + sb, 0, 0);
     }
-    const char* xc = reinterpret_cast<const char*>(p.x + (size_t)c * kChunk);
+    const uint32_t xb = live ? (uint32_t)c * (2 * kChunk) : kOutOfRange;
     if constexpr (!MFMA) {
 #pragma unroll
-      for (int m = 0; m < MROWS; ++m) {
-        const char* xm = xc + (size_t)min(m, p.M - 1) * p.K * 2;  // uniform
-        xbuf[s][m] = *reinterpret_cast<const uint32_t*>(xm + gx_boff);
-      }
+      for (int m = 0; m < MROWS; ++m)
+        xbuf[s][m] = __builtin_amdgcn_raw_buffer_load_b32(xrsrc, xoff[m] + xb, 0, 0);
     } else {
-      const uint32_t cb = (uint32_t)c * (2 * kChunk);
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
           abuf[s][mt][j] = __builtin_bit_cast(
-              u32x4, __builtin_amdgcn_raw_buffer_load_b128(xrsrc, aboff[mt] + cb + 64 * j, 0, 0));
+              u32x4, __builtin_amdgcn_raw_buffer_load_b128(xrsrc, aboff[mt] + xb + 64 * j, 0, 0));
     }
   };
 
