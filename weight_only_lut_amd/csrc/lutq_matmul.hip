@@ -78,7 +78,13 @@ void matmul_kernel(const MatmulParams p) {
   // this wave's chunks: cw, cw + WAVES, cw + 2 WAVES, ... (nmine of them)
   const int cw = c_begin + wave;
   const int nmine = span > wave ? (span - wave + kWaves - 1) / kWaves : 0;
-  const int niter = (nmine + PF - 1) / PF * PF;
+  // Scales come in batches of SB steps (see below); the pipeline loop is
+  // unrolled over U steps, a multiple of both PF and SB, so register slots
+  // and batch positions are compile-time constants.
+  constexpr int SB = 4;
+  constexpr int U = PF % SB == 0 ? PF : (SB % PF == 0 ? SB : PF * SB);
+  static_assert(U == PF || U == 2 * PF, "the loop tail below covers one slot round");
+  const int nsteps = (nmine + PF - 1) / PF * PF;
   const int tile0 = rb * TPW;
   const int cpg = GROUPED ? p.group / kChunk : 1;       // chunks per group
   const int gpr = GROUPED ? p.K / p.group : 0;          // groups per row
@@ -98,7 +104,11 @@ void matmul_kernel(const MatmulParams p) {
 #pragma unroll
   for (int t = 0; t < TPW; ++t) coff[t] = (uint32_t)t * tile_bytes + lane_off;
 
-  // scales of this block's rows: [rows][groups]; lane row = 16 t + r
+  // Scales of this block's rows, [rows][groups]. One 2-byte load per tile
+  // fetches a batch of SB = 4 steps: lane (q, r) takes row 16t + r at the
+  // group of step 4b + q. Each step then hands its lane row to all four lane
+  // rows with ds_bpermute, so a step costs no scale load of its own (a
+  // per-step load touches 16 cache lines, one per row, for 32 bytes).
   const int row0 = tile0 * kTileRows;
   const uint32_t rows_here = (uint32_t)min(ROWS, p.N - row0);
   const __amdgpu_buffer_rsrc_t srsrc =
@@ -126,26 +136,19 @@ void matmul_kernel(const MatmulParams p) {
                                   : kRowOutOfRange;
 
   SlotRegs<BITS> cbuf[PF][TPW];
-  uint16_t sbuf[PF][TPW];
+  uint32_t scur[TPW], snext[TPW];  // scale batches: in use, in flight
   uint32_t xbuf[PF][MFMA ? 1 : MROWS];
   u32x4 abuf[PF][MT][MFMA ? 4 : 1];
 
   // chunk of pipeline step i, or -1 past the wave's last chunk
   auto chunk = [&](int i) { return i < nmine ? cw + i * kWaves : -1; };
 
-  auto issue = [&](auto S, int c) {
+  auto issue = [&](auto S, int c) __attribute__((always_inline)) {
     constexpr int s = decltype(S)::value;
     const bool live = c >= 0;  // wave-uniform
     const uint32_t cb = live ? (uint32_t)c * BLOCK : kOutOfRange;
-    uint32_t sb = kOutOfRange;
-    if constexpr (GROUPED)
-      if (live) sb = 2u * (cpg == 1 ? (uint32_t)c : (uint32_t)c / (uint32_t)cpg);
 #pragma unroll
-    for (int t = 0; t < TPW; ++t) {
-      cbuf[s][t] = load_slot<BITS>(crsrc, coff[t] + cb);
-      if constexpr (GROUPED)
-        sbuf[s][t] = __builtin_amdgcn_raw_buffer_load_b16(srsrc, soff[t] + sb, 0, 0);
-    }
+    for (int t = 0; t < TPW; ++t) cbuf[s][t] = load_slot<BITS>(crsrc, coff[t] + cb);
     const uint32_t xb = live ? (uint32_t)c * (2 * kChunk) : kOutOfRange;
     if constexpr (!MFMA) {
 #pragma unroll
@@ -161,6 +164,21 @@ void matmul_kernel(const MatmulParams p) {
     }
   };
 
+  // the scale batch of steps i0 .. i0 + SB - 1 into snext
+  auto issue_scales = [&](int i0) __attribute__((always_inline)) {
+    const int c = chunk(i0 + q);  // per lane
+    uint32_t sb = kOutOfRange;
+    if (c >= 0) sb = 2u * (cpg == 1 ? (uint32_t)c : (uint32_t)c / (uint32_t)cpg);
+#pragma unroll
+    for (int t = 0; t < TPW; ++t)
+      snext[t] = __builtin_amdgcn_raw_buffer_load_b16(srsrc, soff[t] + sb, 0, 0);
+  };
+  // the scale of this lane's row at step position u (0 .. SB-1) of the batch
+  auto step_scale = [&](int t, int u) __attribute__((always_inline)) {
+    const int v = __builtin_amdgcn_ds_bpermute((16 * u + r) * 4, (int)scur[t]);
+    return f16_bits_to_f32((uint16_t)v);
+  };
+
   float gacc[TPW][MFMA ? 1 : MROWS];
   f32x4 macc[TPW][MT];
 #pragma unroll
@@ -172,8 +190,9 @@ void matmul_kernel(const MatmulParams p) {
   }
 
   // One chunk (128 codes) of every tile.
-  auto compute = [&](auto S) {
+  auto compute = [&](auto S, auto B) __attribute__((always_inline)) {
     constexpr int s = decltype(S)::value;
+    constexpr int u = decltype(B)::value;  // position in the scale batch
     if constexpr (!MFMA) {
       // k-step outer, tile inner: each activation broadcast serves all tiles
       float cs[TPW][MROWS];
@@ -200,7 +219,7 @@ void matmul_kernel(const MatmulParams p) {
 #pragma unroll
       for (int t = 0; t < TPW; ++t) {
         if constexpr (GROUPED) {
-          const float sc = f16_bits_to_f32(sbuf[s][t]);
+          const float sc = step_scale(t, u);
 #pragma unroll
           for (int m = 0; m < MROWS; ++m) gacc[t][m] = __builtin_fmaf(sc, cs[t][m], gacc[t][m]);
         } else {
@@ -235,7 +254,7 @@ void matmul_kernel(const MatmulParams p) {
           }
         }
         if constexpr (GROUPED) {
-          const float sc = f16_bits_to_f32(sbuf[s][t]);
+          const float sc = step_scale(t, u);
 #pragma unroll
           for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -247,20 +266,38 @@ void matmul_kernel(const MatmulParams p) {
 
   // Software pipeline: PF register slots; the load of step i + PF - 1 is
   // issued before step i is computed, so PF - 1 chunks are in flight during
-  // every compute step. Loads are unconditional (see c_last); the compute of
-  // padding steps is skipped with a wave-uniform branch.
+  // every compute step, and the scale batch of steps i + SB .. i + 2SB - 1 is
+  // issued when step i opens a batch. Within the loop every step issues the
+  // same loads (those past the wave's last chunk read nothing); the loop
+  // ends with the wave's last chunk.
+  if constexpr (GROUPED) issue_scales(0);
   static_for<PF - 1>([&](auto S) { issue(S, chunk(decltype(S)::value)); });
 
   build_pair_table<BITS, kThreads>(table, lut_lane, tid);
   __syncthreads();
 
-  for (int i0 = 0; i0 < niter; i0 += PF) {
-    static_for<PF>([&](auto S) {
-      constexpr int s = decltype(S)::value;
-      const int i = i0 + s;
-      issue(std::integral_constant<int, (s + PF - 1) % PF>{}, chunk(i + PF - 1));
-      if (i < nmine) compute(S);
-    });
+  // One step at position u of a U-step group starting at i0. Steps past the
+  // wave's last chunk (at most PF - 1) issue loads that read nothing and
+  // skip the compute; keeping the issue unconditional keeps the in-order
+  // load counter the same on every path, so its waits stay exact.
+  // (always inlined: an outlined copy would move the register arrays it
+  // captures into scratch memory)
+  auto step = [&](auto S, int i0) __attribute__((always_inline)) {
+    constexpr int u = decltype(S)::value;
+    const int i = i0 + u;
+    if constexpr (GROUPED && u % SB == 0) {
+#pragma unroll
+      for (int t = 0; t < TPW; ++t) scur[t] = snext[t];
+      issue_scales(i + SB);
+    }
+    issue(std::integral_constant<int, (u + PF - 1) % PF>{}, chunk(i + PF - 1));
+    if (i < nmine)
+      compute(std::integral_constant<int, u % PF>{}, std::integral_constant<int, u % SB>{});
+  };
+  int i0 = 0;
+  for (; i0 + U <= nsteps; i0 += U) static_for<U>([&](auto S) { step(S, i0); });
+  if constexpr (U > PF) {
+    if (i0 < nsteps) static_for<PF>([&](auto S) { step(S, i0); });
   }
 
   // ---- combine the waves (fixed order) ------------------------------------
