@@ -154,6 +154,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-batch32", action="store_true")
+    ap.add_argument("--no-warm", action="store_true",
+                    help="skip the Infinity-Cache-warm repeats (so a kernel trace holds cold calls only)")
     ap.add_argument("--sweep", action="store_true", help="also time every workload (stderr)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy (for scaling memory counters)")
@@ -182,11 +184,13 @@ def main():
     hplan = lutq.plan(1, head.N, head.K, 4)
     log(f"[bench] headline: {len(head.packed)} rotating copies, plan={hplan}")
     region_us = time_case(lutq, torch, head, args.steps, args.warmup)
-    warm = Case.__new__(Case)
-    warm.__dict__.update(head.__dict__)
-    warm.packed = head.packed[:1]
-    w_region_us = time_case(lutq, torch, warm, args.steps, args.warmup)
-    log(f"[bench] headline cold: {region_us:.2f} us/call; warm: {w_region_us:.2f} us/call")
+    w_region_us = None
+    if not args.no_warm:
+        warm = Case.__new__(Case)
+        warm.__dict__.update(head.__dict__)
+        warm.packed = head.packed[:1]
+        w_region_us = time_case(lutq, torch, warm, args.steps, args.warmup)
+    log(f"[bench] headline cold: {region_us:.2f} us/call; warm: {w_region_us} us/call")
 
     value = head.bytes / (region_us * 1e-6) / 1e9
     achieved = value
@@ -195,8 +199,9 @@ def main():
     extra = {
         "us_per_call": round(region_us, 3),
         "bits_read_per_weight": round(head.bytes * 8 / (head.N * head.K), 4),
-        "warm": {"us_per_call": round(w_region_us, 3),
-                 "effective_GBps": round(head.bytes / (w_region_us * 1e-6) / 1e9, 1)},
+        "warm": None if w_region_us is None else {
+            "us_per_call": round(w_region_us, 3),
+            "effective_GBps": round(head.bytes / (w_region_us * 1e-6) / 1e9, 1)},
         "plan": hplan,
     }
 
@@ -205,22 +210,26 @@ def main():
         b32 = Case(lutq, torch, "log4_70b", None, 32, cold=True)
         p32 = lutq.plan(32, b32.N, b32.K, 4)
         k_us = time_case(lutq, torch, b32, max(20, args.steps // 4), args.warmup)
-        warm32 = Case.__new__(Case)
-        warm32.__dict__.update(b32.__dict__)
-        warm32.packed = b32.packed[:1]
-        wk_us = time_case(lutq, torch, warm32, max(20, args.steps // 4), args.warmup)
+        wk_us = None
+        if not args.no_warm:
+            warm32 = Case.__new__(Case)
+            warm32.__dict__.update(b32.__dict__)
+            warm32.packed = b32.packed[:1]
+            wk_us = time_case(lutq, torch, warm32, max(20, args.steps // 4), args.warmup)
+            del warm32
         tf = b32.flops / (k_us * 1e-6) / 1e12
         extra["batch32"] = {
             "workload": "log4_70b", "N": b32.N, "K": b32.K, "M": 32, "plan": p32,
             "us_per_call": round(k_us, 3),
             "TFLOPs": round(tf, 1), "mfma_frac": round(tf / MFMA_F16_PEAK_TFLOPS, 4),
             "effective_GBps": round(b32.bytes / (k_us * 1e-6) / 1e9, 1),
-            "warm": {"us_per_call": round(wk_us, 3),
-                     "TFLOPs": round(b32.flops / (wk_us * 1e-6) / 1e12, 1),
-                     "mfma_frac": round(b32.flops / (wk_us * 1e-6) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4)},
+            "warm": None if wk_us is None else {
+                "us_per_call": round(wk_us, 3),
+                "TFLOPs": round(b32.flops / (wk_us * 1e-6) / 1e12, 1),
+                "mfma_frac": round(b32.flops / (wk_us * 1e-6) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4)},
         }
-        log(f"[bench] batch32 cold {k_us:.2f} us = {tf:.1f} TFLOP/s; warm {wk_us:.2f} us")
-        del b32, warm32
+        log(f"[bench] batch32 cold {k_us:.2f} us = {tf:.1f} TFLOP/s; warm {wk_us} us")
+        del b32
         torch.cuda.empty_cache()
 
     if args.sweep:
