@@ -29,6 +29,7 @@
 // order, so results are deterministic.
 #include "lutq_internal.h"
 
+
 namespace lutq {
 
 // BITS: code width; MFMA: compute policy; MROWS: batch rows per launch;
@@ -82,7 +83,7 @@ void matmul_kernel(const MatmulParams p) {
   // unrolled over U steps, a multiple of both PF and SB, so register slots
   // and batch positions are compile-time constants.
   constexpr int SB = 4;
-  constexpr int U = PF % SB == 0 ? PF : (SB % PF == 0 ? SB : PF * SB);
+  constexpr int U = !GROUPED || PF % SB == 0 ? PF : (SB % PF == 0 ? SB : PF * SB);
   static_assert(U == PF || U == 2 * PF, "the loop tail below covers one slot round");
   const int nsteps = (nmine + PF - 1) / PF * PF;
   const int tile0 = rb * TPW;
@@ -146,9 +147,9 @@ void matmul_kernel(const MatmulParams p) {
   auto issue = [&](auto S, int c) __attribute__((always_inline)) {
     constexpr int s = decltype(S)::value;
     const bool live = c >= 0;  // wave-uniform
-    const uint32_t cb = live ? (uint32_t)c * BLOCK : kOutOfRange;
-#pragma unroll
-    for (int t = 0; t < TPW; ++t) cbuf[s][t] = load_slot<BITS>(crsrc, coff[t] + cb);
+    // Activations first, then the codes tile by tile: the load counter
+    // drains in issue order, so tile t can be computed as soon as its own
+    // codes have landed, while the later tiles' codes are still in flight.
     const uint32_t xb = live ? (uint32_t)c * (2 * kChunk) : kOutOfRange;
     if constexpr (!MFMA) {
 #pragma unroll
@@ -162,6 +163,9 @@ void matmul_kernel(const MatmulParams p) {
           abuf[s][mt][j] = __builtin_bit_cast(
               u32x4, __builtin_amdgcn_raw_buffer_load_b128(xrsrc, aboff[mt] + xb + 64 * j, 0, 0));
     }
+    const uint32_t cb = live ? (uint32_t)c * BLOCK : kOutOfRange;
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) cbuf[s][t] = load_slot<BITS>(crsrc, coff[t] + cb);
   };
 
   // the scale batch of steps i0 .. i0 + SB - 1 into snext
@@ -228,19 +232,30 @@ void matmul_kernel(const MatmulParams p) {
         }
       }
     } else {
+      // The decoded pairs of k-step j are the B operand. The lookups of tile
+      // t + 1 are issued before the MFMAs of tile t, so the LDS latency hides
+      // behind them even with a single wave per SIMD.
+      u32x4 bq[2][4];
+      auto lookup = [&](int t, u32x4(&dst)[4]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t idx4 = step_indices<BITS>(cbuf[s][t], j);
+          dst[j].x = lds_load(table, pair_addr(idx4, lane_byte, 0));
+          dst[j].y = lds_load(table, pair_addr(idx4, lane_byte, 1));
+          dst[j].z = lds_load(table, pair_addr(idx4, lane_byte, 2));
+          dst[j].w = lds_load(table, pair_addr(idx4, lane_byte, 3));
+        }
+      };
+      lookup(0, bq[0]);
 #pragma unroll
       for (int t = 0; t < TPW; ++t) {
+        if (t + 1 < TPW) lookup(t + 1, bq[(t + 1) & 1]);
+        // keep the scheduler from sinking those lookups below the MFMAs
+        __builtin_amdgcn_sched_barrier(0);
         f32x4 cg[MT];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          // the decoded pairs of k-step j are the B operand
-          const uint32_t idx4 = step_indices<BITS>(cbuf[s][t], j);
-          u32x4 bq;
-          bq.x = lds_load(table, pair_addr(idx4, lane_byte, 0));
-          bq.y = lds_load(table, pair_addr(idx4, lane_byte, 1));
-          bq.z = lds_load(table, pair_addr(idx4, lane_byte, 2));
-          bq.w = lds_load(table, pair_addr(idx4, lane_byte, 3));
-          const f16x8 b = __builtin_bit_cast(f16x8, bq);
+          const f16x8 b = __builtin_bit_cast(f16x8, bq[t & 1][j]);
 #pragma unroll
           for (int mt = 0; mt < MT; ++mt) {
             const f16x8 a = __builtin_bit_cast(f16x8, abuf[s][mt][j]);
