@@ -80,11 +80,12 @@ class Case:
 
 
 def time_case(lutq, torch, case, steps, warmup):
-    """Average microseconds per call over `steps` back-to-back calls.
+    """Average microseconds per call over exactly `steps` back-to-back calls.
 
-    The calls are captured once in a HIP graph and replayed, so host-side
-    launch cost stays outside the timed region; HIP events are recorded on the
-    stream the kernels run on. Median of three replays.
+    `warmup` eager calls, then the `steps` calls are captured in a HIP graph,
+    replayed once untimed, and replayed once more between HIP events recorded
+    on the stream the kernels run on (host-side launch cost stays outside the
+    timed region), with a device synchronization on both sides.
     """
     stream = torch.cuda.Stream()
     with torch.cuda.stream(stream):
@@ -99,15 +100,12 @@ def time_case(lutq, torch, case, steps, warmup):
         graph.replay()
     torch.cuda.synchronize()
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    reps = []
     with torch.cuda.stream(stream):  # replay() launches on the current stream
-        for _ in range(3):
-            start.record()
-            graph.replay()
-            stop.record()
-            torch.cuda.synchronize()
-            reps.append(start.elapsed_time(stop) * 1e3 / steps)
-    return sorted(reps)[1]
+        start.record()
+        graph.replay()
+        stop.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(stop) * 1e3 / steps
 
 
 def cpu_baseline(case, budget_s=15.0):
