@@ -192,7 +192,7 @@ def main():
 
     value = head.bytes / (region_us * 1e-6) / 1e9
     achieved = value
-    traffic = load_traffic("int4_up_proj")
+    traffic = load_traffic("int4_up_proj", hplan)
 
     extra = {
         "us_per_call": round(region_us, 3),
@@ -356,12 +356,19 @@ def summarize_profile(kt_dir, fetch_dir, write_dir, command=""):
     w_scale = COPY_BYTES / (w_copy * 1024) if w_copy else None
     out = {"source_digest": source_digest(), "copy_bytes": COPY_BYTES,
            "fetch_scale": f_scale, "write_scale": w_scale, "kernels": {}}
-    for label, part in (("int4_up_proj", HEADLINE_KERNEL), ("log4_70b_batch32", BATCH32_KERNEL)):
+    import weight_only_lut_amd as lutq
+    from synth import workloads
+    lutq.load_library()
+    for label, part, wname, M in (("int4_up_proj", HEADLINE_KERNEL, "int4_up_proj", 1),
+                                  ("log4_70b_batch32", BATCH32_KERNEL, "log4_70b", 32)):
         f, nf = _counter_per_dispatch(fetch_dir, "FETCH_SIZE", part)
         w, nw = _counter_per_dispatch(write_dir, "WRITE_SIZE", part)
         dur = [r for r in stats if part in r["Name"]]
+        wl = workloads.WORKLOADS[wname]
+        mat = wl.matrices[0]
         rec = {"kernel": part, "fetch_kib_raw": f, "write_kib_raw": w, "dispatches": [nf, nw],
-               "avg_duration_us": float(dur[0]["AverageNs"]) / 1e3 if dur else None}
+               "avg_duration_us": float(dur[0]["AverageNs"]) / 1e3 if dur else None,
+               "plan": lutq.plan(M, mat.N, mat.K, wl.bits)}
         if f is not None and w is not None and f_scale and w_scale:
             rec["traffic_bytes_per_launch"] = round(f * 1024 * f_scale + w * 1024 * w_scale)
         out["kernels"][label] = rec
@@ -389,9 +396,9 @@ def summarize_profile(kt_dir, fetch_dir, write_dir, command=""):
     print(json.dumps(out, indent=1))
 
 
-def load_traffic(workload):
+def load_traffic(workload, plan):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it
-    was taken on the current kernel source; else None."""
+    was taken on the current kernel source and with the same plan; else None."""
     path = os.path.join(ROOT, "profiles", "matmul_kernel_counters.json")
     if not os.path.exists(path):
         return None
@@ -400,7 +407,10 @@ def load_traffic(workload):
         from weight_only_lut_amd.build import source_digest
         if rec.get("source_digest") != source_digest():
             return None
-        return rec["kernels"][workload].get("traffic_bytes_per_launch")
+        k = rec["kernels"][workload]
+        if k.get("plan") != plan:
+            return None
+        return k.get("traffic_bytes_per_launch")
     except (OSError, KeyError, ValueError):
         return None
 

@@ -136,32 +136,42 @@ def test_plan_switches_paths_by_batch():
     assert lutq.plan(1, 14336, 4096, 4)["path"] == "gemv"
     assert lutq.plan(2, 14336, 4096, 4)["path"] == "mfma"
     assert lutq.plan(32, 28672, 8192, 4)["path"] == "mfma"
-    # 4096 rows = 256 tiles: GEMV up to 4 rows
-    assert lutq.plan(4, 4096, 14336, 3)["path"] == "gemv"
-    assert lutq.plan(5, 4096, 14336, 3)["path"] == "mfma"
-    # 1024 rows = 64 tiles: GEMV up to 8 rows
-    assert lutq.plan(8, 1024, 4096, 4)["path"] == "gemv"
-    assert lutq.plan(9, 1024, 4096, 4)["path"] == "mfma"
+    # narrow, short K: GEMV up to 4 rows
+    assert lutq.plan(4, 4096, 4096, 3)["path"] == "gemv"
+    assert lutq.plan(5, 4096, 4096, 3)["path"] == "mfma"
+    assert lutq.plan(4, 1024, 4096, 4)["path"] == "gemv"
+    assert lutq.plan(8, 1024, 4096, 4)["path"] == "mfma"
+    # narrow, long K (>= 8192): GEMV up to 2 rows
+    assert lutq.plan(2, 4096, 14336, 3)["path"] == "gemv"
+    assert lutq.plan(3, 4096, 14336, 3)["path"] == "mfma"
 
 
 def test_plan_shapes_and_split():
-    # Without a GPU the device is taken to have 256 compute units.
     # Batch 32 on a wide matrix: 8 tiles per wave, no split.
     assert lutq.plan(32, 28672, 8192, 4) == {"path": "mfma", "ksplit": 1, "tiles": 8}
     # A batch slice of 16 rows keeps 4 tiles per wave.
     assert lutq.plan(16, 28672, 8192, 4)["tiles"] == 4
-    # Narrow matrices: 2 tiles per wave, and K split until the row blocks
-    # cover the device (1024 rows = 32 blocks of 32 rows -> 8 splits).
-    assert lutq.plan(16, 1024, 4096, 4) == {"path": "mfma", "ksplit": 8, "tiles": 2}
     # GEMV: 2 tiles per wave only when that still gives 2 row blocks per CU
     assert lutq.plan(1, 14336, 4096, 4) == {"path": "gemv", "ksplit": 1, "tiles": 2}
     assert lutq.plan(1, 4096, 4096, 4) == {"path": "gemv", "ksplit": 1, "tiles": 1}
-    assert lutq.plan(1, 1024, 4096, 4) == {"path": "gemv", "ksplit": 4, "tiles": 1}
-    # the split never exceeds the number of 128-code chunks
-    assert lutq.plan(1, 16, 256, 4)["ksplit"] == 2
-    # explicit fields are kept
+    # GEMV: a short K is never split, however few the row blocks
+    assert lutq.plan(1, 1024, 4096, 4) == {"path": "gemv", "ksplit": 1, "tiles": 1}
+    # GEMV, long K on fewer row blocks than CUs: split until the CUs are
+    # covered, keeping >= 32 chunks per split
+    assert lutq.plan(1, 16, 1 << 20, 4)["ksplit"] == 256
+    assert lutq.plan(1, 16, 16384, 4)["ksplit"] == 4
+    assert lutq.plan(2, 4096, 14336, 3) == {"path": "gemv", "ksplit": 1, "tiles": 1}
+    # MFMA: split once the row blocks cover at most half the CUs, from 9
+    # batch rows or on a long K (1024 rows = 32 blocks of 32 -> 8;
+    # 4096 rows = 128 blocks -> 2)
+    assert lutq.plan(16, 1024, 4096, 4) == {"path": "mfma", "ksplit": 8, "tiles": 2}
+    assert lutq.plan(8, 1024, 4096, 4) == {"path": "mfma", "ksplit": 1, "tiles": 2}
+    assert lutq.plan(4, 4096, 14336, 3) == {"path": "mfma", "ksplit": 2, "tiles": 2}
+    assert lutq.plan(32, 14336, 4096, 4) == {"path": "mfma", "ksplit": 1, "tiles": 4}
+    # explicit fields are kept (the split is clamped to the chunk count)
     assert lutq.plan(1, 14336, 4096, 4, path="mfma", tiles=8, ksplit=3) == \
         {"path": "mfma", "ksplit": 3, "tiles": 8}
+    assert lutq.plan(1, 16, 256, 4, ksplit=100)["ksplit"] == 2
     with pytest.raises(lutq.LutqError):
         lutq.plan(1, 14336, 4096, 4, path="gemv", tiles=8)
 

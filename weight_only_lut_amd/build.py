@@ -56,11 +56,17 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+# Sources of the matmul device code: a stored kernel profile is current while
+# their digest is unchanged (host-side planning lives in lutq_api.cpp; the
+# profile also records the plan it was taken with).
+KERNEL_SOURCES = ["lutq_device.h", "lutq_internal.h", "lutq_matmul.hip"]
+
+
 def source_digest() -> str:
-    """SHA-256 over the library sources (to tell whether a stored profile is current)."""
+    """SHA-256 over the matmul kernel sources (to tell whether a stored profile is current)."""
     import hashlib
     h = hashlib.sha256()
-    for name in sorted(os.listdir(CSRC)):
+    for name in KERNEL_SOURCES:
         with open(os.path.join(CSRC, name), "rb") as f:
             h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()[:16]

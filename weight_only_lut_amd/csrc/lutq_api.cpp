@@ -108,6 +108,10 @@ int rows_per_launch(int path) {
 
 int kernel_path(int path) { return path == LUTQ_PATH_MFMA ? lutq::kPathMfma : lutq::kPathGemv; }
 
+// K lengths (in 128-code chunks) for the split-K plan.
+constexpr int kSplitMinChunks = 64;  // K >= 8192
+constexpr int kSplitChunks = 32;     // chunks per split, at least
+
 // Checks the caller's options (NULL = all automatic) and copies them to *o.
 int read_options(const lutq_options_t* opts, lutq_options_t* o) {
   std::memset(o, 0, sizeof *o);
@@ -133,8 +137,8 @@ void plan(int M, int N, int K, int cus, lutq_options_t* o) {
     // Batch rows up to which GEMV beats MFMA (measured on MI355X over the
     // Llama projection shapes): on wide matrices MFMA wins from 2 rows; on
     // narrow ones, which run GEMV at one tile per wave, GEMV keeps up to 4
-    // rows, and up to 8 when there are at most half as many tiles as CUs.
-    const int gemv_max = ntiles >= 2 * cus ? 1 : (2 * ntiles <= cus ? 8 : 4);
+    // rows, or 2 when K is long enough for the MFMA path to split it.
+    const int gemv_max = ntiles >= 2 * cus ? 1 : (nchunks >= kSplitMinChunks ? 2 : 4);
     o->path = M <= gemv_max ? LUTQ_PATH_GEMV : LUTQ_PATH_MFMA;
   }
   const int kpath = kernel_path(o->path);
@@ -144,11 +148,21 @@ void plan(int M, int N, int K, int cus, lutq_options_t* o) {
   }
   const int nrb = (ntiles + o->tiles - 1) / o->tiles;
   if (o->ksplit == 0) {
-    // Split K across workgroups only when the matrix has too few row blocks
-    // to give every CU work: the split costs a second pass over fp32
-    // partials and an arrival counter per row block.
+    // A split along K puts two memory round trips (the partial stores, then
+    // the last workgroup's reads) on the critical path: a few microseconds.
+    // MFMA workgroups at more than 8 batch rows (or on a long K) carry
+    // enough compute that splitting pays as soon as the row blocks cover at
+    // most half the CUs. GEMV workgroups are light: split only a long K
+    // (each split keeping at least kSplitChunks chunks) on fewer row blocks
+    // than CUs.
     int k = 1;
-    if (2 * nrb <= cus) k = cus / nrb;
+    if (o->path == LUTQ_PATH_MFMA) {
+      if (2 * nrb <= cus && (M > 8 || nchunks >= kSplitMinChunks)) k = cus / nrb;
+    } else if (nrb < cus && nchunks >= kSplitMinChunks) {
+      k = cus / nrb;
+      if (k > nchunks / kSplitChunks) k = nchunks / kSplitChunks;
+      if (k < 1) k = 1;
+    }
     o->ksplit = k;
   }
   if (o->ksplit > nchunks) o->ksplit = nchunks > 0 ? nchunks : 1;
