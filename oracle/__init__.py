@@ -13,7 +13,10 @@ rescaling of partial sums, which is the same sum in another order):
     y[m, n]     = sum_k x[m, k] * W_hat[n, k]
 
 Every function cites the passage it follows. Parity status of each function
-is in the docstring; all are pinned by tests/test_oracle.py.
+is in the docstring; all are pinned by tests/test_oracle.py, and the
+quantizer (``oracle.quantize``: round-to-nearest onto a table, the weight
+error, the logarithmic table and its base search) by
+tests/test_oracle_quantize.py.
 """
 
 from .lutq_ref import (  # noqa: F401
@@ -25,3 +28,4 @@ from .lutq_ref import (  # noqa: F401
     error_bound,
     check,
 )
+from . import quantize  # noqa: F401
