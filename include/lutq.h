@@ -164,6 +164,55 @@ int lutq_matmul_ex(const uint16_t* x, const lutq_packed_t* packed, const uint16_
  * the one of the first slice, and all slices use it. */
 int lutq_plan(int M, int N, int K, int bits, const lutq_options_t* req, lutq_options_t* out);
 
+/* ---- quantizer ------------------------------------------------------------
+ * Round-to-nearest onto a lookup table: the step that produces the codes and
+ * scales lutq_repack and lutq_matmul consume ("PTQ-damage" abstract:
+ * round-to-nearest at group-128 granularity; FLUTE abstract: arbitrary,
+ * non-uniform tables; LogbQuant abstract: tensor-wise scales and log tables
+ * with an adjustable base).
+ *
+ *   scale (fp64, then rounded once to fp16, nearest even; a zero scale
+ *   becomes 1, one above 65504 is clamped to 65504):
+ *     LUTQ_RULE_ABSMAX: max|w| / max|T|
+ *     LUTQ_RULE_RANGE : max(max(w) / max(T), min(w) / min(T)), for tables
+ *                       with min(T) < 0 < max(T); on the uniform table
+ *                       T[i] = i - z this is asymmetric INT round-to-nearest
+ *   code: the entry nearest to w / s (fp64 quotient of the fp32 weight and
+ *         the fp16 scale, exact comparison), an exact tie to the lower index.
+ * Table entries must be distinct (results are unspecified otherwise).
+ */
+enum { LUTQ_RULE_ABSMAX = 0, LUTQ_RULE_RANGE = 1 };
+
+/*   w      : device, fp32 [N, K] row-major, finite, 8-byte aligned.
+ *   lut    : device, fp16 [2^bits], 2-byte aligned.
+ *   codes  : device, uint8 [N, K] out (one code per byte, the lutq_repack
+ *            input), 2-byte aligned.
+ *   scales : device, fp16 out: [N, K/group] row-major, or [1] (group == 0).
+ * group: 0 or a multiple of 128 that divides K (as lutq_repack).
+ * Errors: LUTQ_EINVAL, LUTQ_EBITS, LUTQ_EGROUP, LUTQ_EALIGN, LUTQ_EUNSUPPORTED,
+ * LUTQ_EHIP. N == 0 or K == 0: nothing to do. Work is enqueued on `stream`;
+ * tensor-wise scales use the library's per-stream scratch buffer. */
+int lutq_quantize(const float* w, const uint16_t* lut, int bits, int N, int K, int group,
+                  int rule, uint8_t* codes, uint16_t* scales, void* stream);
+
+/* The weight error of that quantization, sum over all weights of
+ * (w - s * T[c])^2 in fp64, without writing codes or scales; summed in a
+ * fixed order, so repeated calls agree bit for bit. *err is host memory;
+ * the call waits for the stream. Errors as lutq_quantize. */
+int lutq_quant_error(const float* w, const uint16_t* lut, int bits, int N, int K, int group,
+                     int rule, double* err, void* stream);
+
+/* LogbQuant base search: for each candidate base (host array, each > 1),
+ * the table T[s, k] = (-1)^s * base^-k (code = sign bit on top of the
+ * bits - 1 exponent bits, values rounded to fp16), absmax scales, and its
+ * weight error as lutq_quant_error. Writes the index of the smallest error to
+ * *best (host; the first one on equal errors) and every error to errors
+ * (host, nbases entries, may be NULL). Waits for the stream.
+ * Errors as lutq_quantize, plus LUTQ_EINVAL for nbases < 1 or a base <= 1
+ * or one whose table repeats an fp16 value. */
+int lutq_log_base_search(const float* w, int bits, int N, int K, int group, const double* bases,
+                         int nbases, int* best, double* errors, void* stream);
+
 /* Static string for a status code. */
 const char* lutq_strerror(int status);
 

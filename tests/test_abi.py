@@ -130,6 +130,46 @@ def test_matmul_validates_before_launching(lib):
     assert lib.lutq_unpack(None, P(0x1000), None) == EINVAL
 
 
+def test_quantizer_validates_before_launching(lib):
+    P = ctypes.c_void_p
+    err = ctypes.c_double(0)
+    good = dict(w=P(0x1000), lut=P(0x2000), bits=4, N=8, K=256, group=128, rule=0,
+                codes=P(0x3000), scales=P(0x4000))
+
+    def q(**kw):
+        a = {**good, **kw}
+        return lib.lutq_quantize(a["w"], a["lut"], a["bits"], a["N"], a["K"], a["group"], a["rule"],
+                                 a["codes"], a["scales"], None)
+
+    assert q(bits=5) == EBITS
+    assert q(group=64) == EGROUP
+    assert q(K=200) == EGROUP
+    assert q(rule=2) == EINVAL
+    assert q(N=-1) == EINVAL
+    assert q(N=1 << 25) == EUNSUP
+    assert q(w=P(0)) == EINVAL
+    assert q(codes=P(0)) == EINVAL
+    assert q(w=P(0x1004)) == EALIGN          # fp32 pairs: 8-byte aligned
+    assert q(codes=P(0x3001)) == EALIGN
+    assert q(scales=P(0x4001)) == EALIGN
+    assert q(N=0) == OK and q(K=0) == OK     # nothing to do, no HIP call
+    assert lib.lutq_quant_error(P(0x1000), P(0x2000), 4, 8, 256, 128, 0, None, None) == EINVAL
+    assert lib.lutq_quant_error(P(0x1000), P(0x2000), 4, 0, 256, 128, 0, ctypes.byref(err), None) == OK
+    assert err.value == 0.0
+    best = ctypes.c_int32(-1)
+    bases = (ctypes.c_double * 3)(1.5, 2.0, 1.0)
+    assert lib.lutq_log_base_search(P(0x1000), 4, 8, 256, 128, bases, 3, ctypes.byref(best), None,
+                                    None) == EINVAL          # a base <= 1
+    bases = (ctypes.c_double * 1)(1.0001)                     # the table repeats an fp16 value
+    assert lib.lutq_log_base_search(P(0x1000), 4, 8, 256, 128, bases, 1, ctypes.byref(best), None,
+                                    None) == EINVAL
+    bases = (ctypes.c_double * 2)(1.5, 2.0)
+    assert lib.lutq_log_base_search(P(0x1000), 4, 8, 256, 128, bases, 0, ctypes.byref(best), None,
+                                    None) == EINVAL
+    assert lib.lutq_log_base_search(P(0x1000), 4, 0, 256, 128, bases, 2, ctypes.byref(best), None,
+                                    None) == OK and best.value == 0
+
+
 def test_plan_switches_paths_by_batch():
     # Without a GPU the device is taken to have 256 compute units.
     # wide matrices (>= 512 tiles): GEMV for one row only

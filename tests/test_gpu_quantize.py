@@ -1,0 +1,154 @@
+"""GPU parity for the quantizer (lutq_quantize, lutq_quant_error,
+lutq_log_base_search) against oracle/quantize.py.
+
+Codes and scales are integers decided by fp64 arithmetic on both sides (the
+quotient w / s, the fp64 scale rounded once to fp16), so they must agree bit
+for bit; the weight error is a sum in a different order, compared to 1e-9
+relative. Cases: every table kind and width, both scale rules, grouped and
+tensor-wise scales, ragged row counts, crafted exact ties and fp16 rounding
+ties, all-zero and clamped groups, the full-size matrices of the headline and
+Llama-70B workloads, and quantize -> repack -> matmul end to end.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import quantize as Q
+from synth import draw, tables, workloads
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def lutq():
+    import weight_only_lut_amd as m
+    m.load_library()
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return m
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def gpu_quantize(lutq, w, T, bits, group, rule):
+    c, s = lutq.quantize(dev(w), dev(T), bits, group, rule)
+    torch.cuda.synchronize()
+    return c.cpu().numpy(), s.cpu().numpy()
+
+
+def assert_same(w, T, bits, group, rule, lutq):
+    c, s = gpu_quantize(lutq, w, T, bits, group, rule)
+    c_ref, s_ref = Q.quantize(w, T, group, rule)
+    assert np.array_equal(s.view(np.uint16), s_ref.view(np.uint16)), "scales differ"
+    bad = np.argwhere(c != c_ref)
+    assert bad.size == 0, f"{len(bad)} codes differ, first at {bad[0].tolist()}"
+
+
+TABLE_CASES = [
+    # kind, bits, rule, kwargs
+    ("int", 4, "range", {}), ("int", 3, "range", {}), ("int", 2, "range", {}),
+    ("int", 4, "absmax", {}), ("nf", 4, "absmax", {}), ("nf", 3, "absmax", {}),
+    ("nf", 2, "absmax", {}), ("lloyd_max", 3, "absmax", {}), ("lloyd_max", 4, "absmax", {}),
+    ("log", 4, "absmax", {"base": 2 ** 0.5}), ("log", 3, "absmax", {"base": 1.7}),
+]
+
+
+@pytest.mark.parametrize("kind,bits,rule,kw", TABLE_CASES)
+@pytest.mark.parametrize("group", [128, 256, 0])
+@pytest.mark.parametrize("N,K", [(37, 256), (200, 1024)])
+def test_quantize_matches_oracle(lutq, kind, bits, rule, kw, group, N, K):
+    if group and K % group:
+        pytest.skip("group does not divide K")
+    T = tables.make(kind, bits, **kw)
+    w = draw.weights("student_t", N, K, (71, bits, N, K, group), nu=4.0, scale=0.02)
+    assert_same(w, T, bits, group, rule, lutq)
+
+
+def test_quantize_exact_ties_and_scale_edges(lutq):
+    rng = np.random.default_rng(72)
+    T = tables.make("nf", 4)
+    Ts = np.sort(T.astype(np.float64))
+    mids = (Ts[:-1] + Ts[1:]) / 2
+    N, K = 8, 512
+    w = np.zeros((N, K), np.float32)
+    for n in range(N):
+        for g in range(K // 128):
+            blk = w[n, g * 128:(g + 1) * 128]
+            s = 2.0 ** -(n + 3)                  # exact fp16 scale: absmax = s * 1
+            blk[0] = s
+            blk[1:16] = (mids * s).astype(np.float32)          # every midpoint: exact ties
+            blk[16:31] = np.nextafter(mids * s, np.inf).astype(np.float32)
+            blk[31:] = (rng.normal(0, 0.4, 97) * s).astype(np.float32)
+    w[0, 256:384] = 0.0                                       # all-zero group -> scale 1
+    w[1, 256] = 1e6                                           # clamps to 65504
+    w[2, 384:512] = 0.0
+    w[2, 384] = np.float32(1 + 2 ** -11)                      # fp16 tie in the scale -> even
+    w[3, 384:512] = 0.0
+    w[3, 384] = -np.float32(1 + 3 * 2 ** -11)
+    assert_same(w, T, 4, 128, "absmax", lutq)
+    Ti = tables.make("int", 4)
+    assert_same(w, Ti, 4, 128, "range", lutq)
+    assert_same(w, Ti, 4, 0, "range", lutq)
+
+
+@pytest.mark.parametrize("group", [128, 0])
+def test_quant_error_matches_oracle(lutq, group):
+    T = tables.make("lloyd_max", 3)
+    w = draw.weights("laplace", 96, 1024, (73, group), b=0.015)
+    got = lutq.quant_error(dev(w), dev(T), 3, group, "absmax")
+    c, s = Q.quantize(w, T, group, "absmax")
+    want = Q.sq_error(w, T, c, s, group)
+    assert abs(got - want) <= 1e-9 * want
+    again = lutq.quant_error(dev(w), dev(T), 3, group, "absmax")
+    assert again == got                                       # fixed summation order
+
+
+def test_log_base_search_matches_oracle(lutq):
+    w = draw.weights("laplace", 64, 1024, (74,), b=0.015)
+    bases = [1.2, 1.35, 2 ** 0.5, 1.6, 2.0, 2.5]
+    best, errs = lutq.log_base_search(dev(w), 4, 0, bases)
+    best_ref, errs_ref = Q.log_base_search(w, 4, 0, bases)
+    assert best == best_ref
+    for a, b in zip(errs, errs_ref):
+        assert abs(a - b) <= 1e-9 * b
+
+
+def test_quantize_full_size_headline(lutq):
+    w_ = workloads.WORKLOADS["int4_up_proj"]
+    w = workloads.weights(w_)
+    T = workloads.lut(w_)
+    c, s = gpu_quantize(lutq, w, T, 4, 128, "range")
+    s_ref = Q.scales(w, T, 128, "range")
+    assert np.array_equal(s.view(np.uint16), s_ref.view(np.uint16))
+    rows = np.r_[0:64, 7000:7064, w.shape[0] - 64:w.shape[0]]
+    c_ref = Q.codes(w[rows], T, s_ref[rows], 128)
+    assert np.array_equal(c[rows], c_ref)
+
+
+def test_quantize_full_size_tensor_wise(lutq):
+    w_ = workloads.WORKLOADS["log4_70b"]
+    w = workloads.weights(w_)
+    T = workloads.lut(w_)
+    c, s = gpu_quantize(lutq, w, T, 4, 0, "absmax")
+    s_ref = Q.scales(w, T, 0, "absmax")
+    assert s.view(np.uint16)[0] == s_ref.view(np.uint16)[0]
+    rows = np.r_[0:32, 20000:20032]
+    c_ref = Q.codes(w[rows], T, s_ref, 0)
+    assert np.array_equal(c[rows], c_ref)
+
+
+def test_quantize_repack_matmul_end_to_end(lutq):
+    T = tables.make("nf", 4)
+    w = draw.weights("normal", 300, 1024, (75,), sigma=0.02)
+    x = draw.activations(5, 1024, (76,))
+    cd, sd = lutq.quantize(dev(w), dev(T), 4, 128, "absmax")
+    P = lutq.repack(cd, 4, 128)
+    y = lutq.matmul(dev(x), P, dev(T), sd).cpu().numpy()
+    c_ref, s_ref = Q.quantize(w, T, 128, "absmax")
+    y_ref, B = oracle.reference(x, c_ref, T, s_ref, 128)
+    ok, worst = oracle.check(y, y_ref, B)
+    assert ok, f"max err/bound = {worst:.3g}"

@@ -13,11 +13,16 @@ from ._lib import (  # noqa: F401
     PATH_AUTO,
     PATH_GEMV,
     PATH_MFMA,
+    RULE_ABSMAX,
+    RULE_RANGE,
     library_path,
     load_library,
+    log_base_search,
     matmul,
     packed_bytes,
     plan,
+    quant_error,
+    quantize,
     repack,
     strerror,
     unpack,

@@ -21,7 +21,11 @@ LUTQ_LAYOUT_VERSION = 1
 EXPORTS = (
     "lutq_packed_bytes", "lutq_repack", "lutq_unpack", "lutq_matmul", "lutq_matmul_ex",
     "lutq_plan", "lutq_strerror", "lutq_last_hip_error", "lutq_shutdown",
+    "lutq_quantize", "lutq_quant_error", "lutq_log_base_search",
 )
+
+RULE_ABSMAX, RULE_RANGE = 0, 1
+_RULES = {"absmax": RULE_ABSMAX, "range": RULE_RANGE}
 
 
 class PackedDesc(ctypes.Structure):
@@ -83,6 +87,13 @@ def load_library():
     lib.lutq_last_hip_error.restype = i32
     lib.lutq_shutdown.argtypes = []
     lib.lutq_shutdown.restype = None
+    lib.lutq_quantize.argtypes = [vp, vp, i32, i32, i32, i32, i32, vp, vp, vp]
+    lib.lutq_quantize.restype = i32
+    lib.lutq_quant_error.argtypes = [vp, vp, i32, i32, i32, i32, i32, ctypes.POINTER(ctypes.c_double), vp]
+    lib.lutq_quant_error.restype = i32
+    lib.lutq_log_base_search.argtypes = [vp, i32, i32, i32, i32, ctypes.POINTER(ctypes.c_double), i32,
+                                         ctypes.POINTER(i32), ctypes.POINTER(ctypes.c_double), vp]
+    lib.lutq_log_base_search.restype = i32
     _LIB = lib
     return lib
 
@@ -196,3 +207,49 @@ def matmul(x, p: Packed, lut, scales, *, path: str = "auto", ksplit: int = 0, ti
     if rc:
         raise LutqError(rc, "lutq_matmul")
     return out
+
+
+def quantize(w, lut, bits: int, group: int, rule: str = "absmax"):
+    """lutq_quantize: fp32 weights [N, K] -> (uint8 codes [N, K], fp16 scales
+    [N, K/group] or [1]), round-to-nearest onto the table ``lut``."""
+    import torch
+    _need_cuda(w, "w", torch.float32)
+    _need_cuda(lut, "lut", torch.float16)
+    N, K = w.shape
+    codes = torch.empty((N, K), dtype=torch.uint8, device=w.device)
+    scales = torch.empty((N, K // group) if group else (1,), dtype=torch.float16, device=w.device)
+    rc = _lib().lutq_quantize(_ptr(w), _ptr(lut), bits, N, K, group, _RULES[rule], _ptr(codes),
+                              _ptr(scales), _stream(w.device))
+    if rc:
+        raise LutqError(rc, "lutq_quantize")
+    return codes, scales
+
+
+def quant_error(w, lut, bits: int, group: int, rule: str = "absmax") -> float:
+    """lutq_quant_error: sum (w - s * T[c])^2 (fp64) of that quantization."""
+    import torch
+    _need_cuda(w, "w", torch.float32)
+    _need_cuda(lut, "lut", torch.float16)
+    N, K = w.shape
+    err = ctypes.c_double(0.0)
+    rc = _lib().lutq_quant_error(_ptr(w), _ptr(lut), bits, N, K, group, _RULES[rule],
+                                 ctypes.byref(err), _stream(w.device))
+    if rc:
+        raise LutqError(rc, "lutq_quant_error")
+    return err.value
+
+
+def log_base_search(w, bits: int, group: int, bases):
+    """lutq_log_base_search: (index of the best base, [error of each base])."""
+    import torch
+    _need_cuda(w, "w", torch.float32)
+    N, K = w.shape
+    nb = len(bases)
+    arr = (ctypes.c_double * nb)(*[float(b) for b in bases])
+    errs = (ctypes.c_double * nb)()
+    best = ctypes.c_int32(-1)
+    rc = _lib().lutq_log_base_search(_ptr(w), bits, N, K, group, arr, nb, ctypes.byref(best),
+                                     errs, _stream(w.device))
+    if rc:
+        raise LutqError(rc, "lutq_log_base_search")
+    return best.value, list(errs)

@@ -14,7 +14,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
-SOURCES = ["lutq_api.cpp", "lutq_layout.hip", "lutq_matmul.hip"]
+SOURCES = ["lutq_api.cpp", "lutq_layout.hip", "lutq_matmul.hip", "lutq_quantize.hip"]
 LIB = os.path.join(HERE, "liblutq.so")
 ARCH = "gfx950"
 

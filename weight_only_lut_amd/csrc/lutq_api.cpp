@@ -3,6 +3,7 @@
 // so argument errors are reported without any HIP call.
 #include <hip/hip_runtime.h>
 
+#include <cmath>
 #include <cstring>
 #include <map>
 #include <mutex>
@@ -296,6 +297,147 @@ int lutq_matmul_ex(const uint16_t* x, const lutq_packed_t* packed, const uint16_
 int lutq_matmul(const uint16_t* x, const lutq_packed_t* packed, const uint16_t* lut,
                 const uint16_t* scales, uint16_t* y, int M, int N, int K, void* stream) {
   return lutq_matmul_ex(x, packed, lut, scales, y, M, N, K, nullptr, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+static_assert(LUTQ_RULE_ABSMAX == lutq::kRuleAbsmax && LUTQ_RULE_RANGE == lutq::kRuleRange,
+              "rule values");
+
+// Arguments shared by the quantizer entry points; N, K > 0 after this.
+int check_quant(const float* w, const uint16_t* lut, int bits, int N, int K, int group, int rule) {
+  int rc = check_sizes(N, K);
+  if (rc) return rc;
+  rc = check_bits_group(K, bits, group);
+  if (rc) return rc;
+  if (rule != LUTQ_RULE_ABSMAX && rule != LUTQ_RULE_RANGE) return LUTQ_EINVAL;
+  if (N == 0 || K == 0) return LUTQ_OK;
+  if (!w || !lut) return LUTQ_EINVAL;
+  if (!aligned(w, 8) || !aligned(lut, 2)) return LUTQ_EALIGN;
+  return LUTQ_OK;
+}
+
+// The quantizer's scratch, carved out of the per-stream buffer; `extra` bytes
+// after it (16-byte aligned) for the caller.
+int quant_scratch(void* stream, size_t extra, lutq::QuantScratch* sc, void** extra_out) {
+  float* base = nullptr;
+  uint32_t* counters = nullptr;
+  int rc = get_scratch(stream, lutq::kQuantScratchBytes + 64 + extra, &base, &counters);
+  if (rc) return rc;
+  char* b = reinterpret_cast<char*>(base);
+  sc->err_partial = reinterpret_cast<double*>(b);
+  b += lutq::kQuantMaxBlocks * sizeof(double);
+  sc->err_total = reinterpret_cast<double*>(b);
+  b += 64;
+  sc->extrema = reinterpret_cast<float*>(b);
+  b += 3 * lutq::kQuantMaxBlocks * sizeof(float);
+  sc->tscale = reinterpret_cast<uint16_t*>(b);
+  b += 64;
+  if (extra_out) *extra_out = b;
+  return LUTQ_OK;
+}
+
+// Runs the error pass and copies the total to the host (waits for the stream).
+int quant_error_to_host(const lutq::QuantScratch& sc, const float* w, const uint16_t* lut, int bits,
+                        int N, int K, int group, int rule, double* err, hipStream_t s) {
+  hipError_t e = lutq::launch_quantize(sc, w, lut, bits, N, K, group, rule, nullptr, nullptr,
+                                       true, s);
+  if (e != hipSuccess) return hip_fail(e);
+  e = hipMemcpyAsync(err, sc.err_total, sizeof(double), hipMemcpyDeviceToHost, s);
+  if (e != hipSuccess) return hip_fail(e);
+  e = hipStreamSynchronize(s);
+  return e == hipSuccess ? LUTQ_OK : hip_fail(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+int lutq_quantize(const float* w, const uint16_t* lut, int bits, int N, int K, int group,
+                  int rule, uint8_t* codes, uint16_t* scales, void* stream) {
+  int rc = check_quant(w, lut, bits, N, K, group, rule);
+  if (rc) return rc;
+  if (N == 0 || K == 0) return LUTQ_OK;
+  if (!codes || !scales) return LUTQ_EINVAL;
+  if (!aligned(codes, 2) || !aligned(scales, 2)) return LUTQ_EALIGN;
+  lutq::QuantScratch sc;
+  std::memset(&sc, 0, sizeof sc);
+  if (group == 0) {  // tensor-wise: the extrema and the scale pass through scratch
+    rc = quant_scratch(stream, 0, &sc, nullptr);
+    if (rc) return rc;
+  }
+  hipError_t e = lutq::launch_quantize(sc, w, lut, bits, N, K, group, rule, codes, scales, false,
+                                       (hipStream_t)stream);
+  return e == hipSuccess ? LUTQ_OK : hip_fail(e);
+}
+
+int lutq_quant_error(const float* w, const uint16_t* lut, int bits, int N, int K, int group,
+                     int rule, double* err, void* stream) {
+  if (!err) return LUTQ_EINVAL;
+  int rc = check_quant(w, lut, bits, N, K, group, rule);
+  if (rc) return rc;
+  if (N == 0 || K == 0) {
+    *err = 0.0;
+    return LUTQ_OK;
+  }
+  lutq::QuantScratch sc;
+  rc = quant_scratch(stream, 0, &sc, nullptr);
+  if (rc) return rc;
+  return quant_error_to_host(sc, w, lut, bits, N, K, group, rule, err, (hipStream_t)stream);
+}
+
+int lutq_log_base_search(const float* w, int bits, int N, int K, int group, const double* bases,
+                         int nbases, int* best, double* errors, void* stream) {
+  if (!best || !bases || nbases < 1) return LUTQ_EINVAL;
+  uint16_t dummy = 0;
+  int rc = check_quant(w, &dummy, bits, N, K, group, LUTQ_RULE_ABSMAX);
+  if (rc) return rc;
+  const int L = 1 << bits, half = L / 2;
+  for (int i = 0; i < nbases; ++i) {
+    if (!(bases[i] > 1.0) || !std::isfinite(bases[i])) return LUTQ_EINVAL;
+    // the table must not repeat an fp16 value (it does once base^-k underflows)
+    uint16_t prev = lutq::f64_to_f16_rne(1.0);
+    for (int k = 1; k < half; ++k) {
+      const uint16_t h = lutq::f64_to_f16_rne(std::pow(bases[i], -(double)k));
+      if (h == prev) return LUTQ_EINVAL;
+      prev = h;
+    }
+  }
+  if (N == 0 || K == 0) {
+    *best = 0;
+    if (errors)
+      for (int i = 0; i < nbases; ++i) errors[i] = 0.0;
+    return LUTQ_OK;
+  }
+  lutq::QuantScratch sc;
+  void* tbl = nullptr;
+  rc = quant_scratch(stream, 64, &sc, &tbl);
+  if (rc) return rc;
+  hipStream_t s = (hipStream_t)stream;
+  double best_err = 0.0;
+  for (int i = 0; i < nbases; ++i) {
+    // code = sign bit on top of the exponent bits: (-1)^sign * base^-k
+    uint16_t host_tbl[16];
+    for (int c = 0; c < L; ++c) {
+      const int k = c % half;
+      const double v = std::pow(bases[i], -(double)k);
+      host_tbl[c] = lutq::f64_to_f16_rne(c >= half ? -v : v);
+    }
+    hipError_t e = hipMemcpyAsync(tbl, host_tbl, L * sizeof(uint16_t), hipMemcpyHostToDevice, s);
+    if (e != hipSuccess) return hip_fail(e);
+    double err = 0.0;
+    rc = quant_error_to_host(sc, w, (const uint16_t*)tbl, bits, N, K, group, LUTQ_RULE_ABSMAX,
+                             &err, s);
+    if (rc) return rc;
+    if (errors) errors[i] = err;
+    if (i == 0 || err < best_err) {
+      best_err = err;
+      *best = i;
+    }
+  }
+  return LUTQ_OK;
 }
 
 const char* lutq_strerror(int status) {
