@@ -145,6 +145,73 @@ def cpu_baseline(case, budget_s=15.0):
     }
 
 
+class QuantCase:
+    """The quantizer on one workload matrix: fp32 weights (cold copies) ->
+    codes + scales under `rule`, with `group` (0 = tensor-wise)."""
+
+    def __init__(self, lutq, torch, wname, group, rule, table=None):
+        import numpy as np
+
+        from synth import tables, workloads
+        w = workloads.WORKLOADS[wname]
+        self.w, self.group, self.rule = w, group, rule
+        _, m = w.matrix(None)
+        self.N, self.K = m.N, m.K
+        W = workloads.weights(w)
+        T = workloads.lut(w) if table is None else tables.make(table, w.bits)
+        d = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+        first = d(W)
+        self.ws = [first] + [first.clone() for _ in range(max(1, -(-COLD_SET_BYTES // first.nbytes)) - 1)]
+        self.lut = d(T)
+        self.codes = torch.empty((self.N, self.K), dtype=torch.uint8, device="cuda")
+        self.scales = torch.empty((self.N, self.K // group) if group else (1,), dtype=torch.float16,
+                                  device="cuda")
+        nsc = self.N * (self.K // group) * 2 if group else 2
+        self.bytes = 4 * self.N * self.K + self.N * self.K + nsc + (1 << w.bits) * 2
+        self.host = (W, T)
+        torch.cuda.synchronize()
+
+    def call(self, lutq, i):
+        from weight_only_lut_amd import _lib
+        W = self.ws[i % len(self.ws)]
+        rc = _lib._lib().lutq_quantize(_lib._ptr(W), _lib._ptr(self.lut), self.w.bits, self.N, self.K,
+                                       self.group, _lib._RULES[self.rule], _lib._ptr(self.codes),
+                                       _lib._ptr(self.scales), _lib._stream(W.device))
+        if rc:
+            raise _lib.LutqError(rc, "lutq_quantize")
+
+
+def quantizer_section(lutq, torch, args):
+    """The quantizer (the step before repack) on the headline matrix: grouped
+    INT (range rule) and tensor-wise NormalFloat (absmax), cold weights, with
+    the oracle on a bounded row sample beside it."""
+    import numpy as np
+
+    from oracle import quantize as Q
+    out = {}
+    for label, group, rule, table in (("int4_g128_range", 128, "range", None),
+                                      ("nf4_tensor_absmax", 0, "absmax", "nf")):
+        qc = QuantCase(lutq, torch, "int4_up_proj", group, rule, table)
+        us = time_case(lutq, torch, qc, max(20, args.steps // 10), args.warmup)
+        gbps = qc.bytes / (us * 1e-6) / 1e9
+        W, T = qc.host
+        rows = 256
+        t0 = time.time()
+        s = Q.scales(W, T, group, rule)           # whole-matrix scales: the tensor-wise rule needs them
+        Q.codes(W[:rows], T, s if group == 0 else s[:rows], group)
+        cpu_s = time.time() - t0
+        cpu_bytes = 4 * W.size + rows * qc.K * 1     # scales pass reads W once; codes for `rows`
+        out[label] = {"N": qc.N, "K": qc.K, "group": group, "rule": rule,
+                      "us_per_call": round(us, 3), "effective_GBps": round(gbps, 1),
+                      "hbm_frac": round(gbps / HBM_PEAK_GBS, 4),
+                      "cpu_oracle": {"seconds": round(cpu_s, 3), "GBps": round(cpu_bytes / cpu_s / 1e9, 3),
+                                     "sample": f"scales over the whole matrix, codes for {rows} rows"}}
+        log(f"[bench] quantizer {label}: {us:.1f} us/call, {gbps:.0f} GB/s")
+        del qc
+        torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -152,6 +219,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-batch32", action="store_true")
+    ap.add_argument("--no-quantizer", action="store_true")
     ap.add_argument("--no-warm", action="store_true",
                     help="skip the Infinity-Cache-warm repeats (so a kernel trace holds cold calls only)")
     ap.add_argument("--sweep", action="store_true", help="also time every workload (stderr)")
@@ -229,6 +297,9 @@ def main():
         log(f"[bench] batch32 cold {k_us:.2f} us = {tf:.1f} TFLOP/s; warm {wk_us} us")
         del b32
         torch.cuda.empty_cache()
+
+    if not args.no_quantizer:
+        extra["quantizer"] = quantizer_section(lutq, torch, args)
 
     if args.sweep:
         extra["sweep"] = sweep(lutq, torch, args)

@@ -10,7 +10,7 @@
 #include <utility>
 
 #include "../../include/lutq.h"
-#include "lutq_internal.h"
+#include "lutq_quant.h"
 
 namespace {
 

@@ -51,25 +51,4 @@ hipError_t launch_fill_u16(uint16_t* p, long long n, uint16_t v, hipStream_t s);
 // kMfmaMaxRows (MFMA); `tiles` passes tiles_supported(path, tiles).
 hipError_t launch_matmul(const MatmulParams& p, int bits, int path, int tiles, hipStream_t s);
 
-// Quantizer: device scratch it needs (from the library's per-stream buffer)
-// and the launcher. At most kQuantMaxBlocks workgroups per pass.
-constexpr int kQuantMaxBlocks = 2048;
-enum QuantRule { kRuleAbsmax = 0, kRuleRange = 1 };  // the LUTQ_RULE_* values
-struct QuantScratch {
-  double* err_partial;  // [kQuantMaxBlocks]
-  double* err_total;    // [1]
-  float* extrema;       // [3 * kQuantMaxBlocks]
-  uint16_t* tscale;     // [1]
-};
-constexpr size_t kQuantScratchBytes =
-    kQuantMaxBlocks * sizeof(double) + 64 + 3 * kQuantMaxBlocks * sizeof(float) + 64;
-
-// codes / scales may be null (not written); error: also fill err_total.
-hipError_t launch_quantize(const QuantScratch& sc, const float* w, const uint16_t* lut, int bits,
-                           int N, int K, int group, int rule, uint8_t* codes, uint16_t* scales,
-                           bool error, hipStream_t s);
-
-// fp64 -> fp16 bits, round to nearest even (host and device).
-__host__ __device__ uint16_t f64_to_f16_rne(double d);
-
 }  // namespace lutq

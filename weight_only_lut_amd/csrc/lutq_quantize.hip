@@ -12,7 +12,7 @@
 // quotient w / s compared exactly against the table's midpoints. Tensor-wise
 // scales take three launches: per-workgroup extrema, one reduction to the
 // scale, then the codes.
-#include "lutq_internal.h"
+#include "lutq_quant.h"
 
 namespace lutq {
 
