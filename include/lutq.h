@@ -183,10 +183,10 @@ int lutq_plan(int M, int N, int K, int bits, const lutq_options_t* req, lutq_opt
  */
 enum { LUTQ_RULE_ABSMAX = 0, LUTQ_RULE_RANGE = 1 };
 
-/*   w      : device, fp32 [N, K] row-major, finite, 8-byte aligned.
+/*   w      : device, fp32 [N, K] row-major, finite, 16-byte aligned.
  *   lut    : device, fp16 [2^bits], 2-byte aligned.
  *   codes  : device, uint8 [N, K] out (one code per byte, the lutq_repack
- *            input), 2-byte aligned.
+ *            input), 4-byte aligned.
  *   scales : device, fp16 out: [N, K/group] row-major, or [1] (group == 0).
  * group: 0 or a multiple of 128 that divides K (as lutq_repack).
  * Errors: LUTQ_EINVAL, LUTQ_EBITS, LUTQ_EGROUP, LUTQ_EALIGN, LUTQ_EUNSUPPORTED,

@@ -149,8 +149,8 @@ def test_quantizer_validates_before_launching(lib):
     assert q(N=1 << 25) == EUNSUP
     assert q(w=P(0)) == EINVAL
     assert q(codes=P(0)) == EINVAL
-    assert q(w=P(0x1004)) == EALIGN          # fp32 pairs: 8-byte aligned
-    assert q(codes=P(0x3001)) == EALIGN
+    assert q(w=P(0x1008)) == EALIGN          # weights read 16 bytes at a time
+    assert q(codes=P(0x3002)) == EALIGN      # codes written 4 at a time
     assert q(scales=P(0x4001)) == EALIGN
     assert q(N=0) == OK and q(K=0) == OK     # nothing to do, no HIP call
     assert lib.lutq_quant_error(P(0x1000), P(0x2000), 4, 8, 256, 128, 0, None, None) == EINVAL

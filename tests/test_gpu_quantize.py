@@ -68,31 +68,75 @@ def test_quantize_matches_oracle(lutq, kind, bits, rule, kw, group, N, K):
     assert_same(w, T, bits, group, rule, lutq)
 
 
-def test_quantize_exact_ties_and_scale_edges(lutq):
+@pytest.mark.parametrize("group,K", [(512, 1536), (1024, 2048), (384, 1536), (2048, 4096)])
+@pytest.mark.parametrize("kind,bits,rule", [("nf", 4, "absmax"), ("int", 3, "range"),
+                                            ("log", 2, "absmax")])
+def test_quantize_group_sizes(lutq, group, K, kind, bits, rule):
+    # every way a group is laid over lanes: 32 or 64 lanes held in registers,
+    # or groups that are read twice (not 2^k * 128, or wider than a wave)
+    T = tables.make(kind, bits, **({"base": 1.5} if kind == "log" else {}))
+    w = draw.weights("student_t", 45, K, (79, group, K, bits), nu=4.0, scale=0.02)
+    assert_same(w, T, bits, group, rule, lutq)
+    got = lutq.quant_error(dev(w), dev(T), bits, group, rule)
+    c, s_ = Q.quantize(w, T, group, rule)
+    want = Q.sq_error(w, T, c, s_, group)
+    assert abs(got - want) <= 1e-9 * want
+
+
+TIE_TABLES = [("nf", 4, {}), ("log", 4, {"base": 2 ** 0.5}), ("log", 3, {"base": 1.7}),
+              ("lloyd_max", 3, {})]
+
+
+@pytest.mark.parametrize("kind,bits,kw", TIE_TABLES)
+def test_quantize_exact_ties_and_scale_edges(lutq, kind, bits, kw):
+    # Log tables sort in an order other than their codes' (positive codes
+    # descend), so half of their ties go to the upper entry.
     rng = np.random.default_rng(72)
-    T = tables.make("nf", 4)
+    T = tables.make(kind, bits, **kw)
     Ts = np.sort(T.astype(np.float64))
+    amax = np.abs(Ts).max()
     mids = (Ts[:-1] + Ts[1:]) / 2
     N, K = 8, 512
+    L1 = mids.size
     w = np.zeros((N, K), np.float32)
     for n in range(N):
         for g in range(K // 128):
             blk = w[n, g * 128:(g + 1) * 128]
-            s = 2.0 ** -(n + 3)                  # exact fp16 scale: absmax = s * 1
-            blk[0] = s
-            blk[1:16] = (mids * s).astype(np.float32)          # every midpoint: exact ties
-            blk[16:31] = np.nextafter(mids * s, np.inf).astype(np.float32)
-            blk[31:] = (rng.normal(0, 0.4, 97) * s).astype(np.float32)
+            s = 2.0 ** -(n + 3)                  # exact fp16 scale: absmax = s * amax
+            assert np.all(np.float32(mids * s) == mids * s)
+            blk[0] = s * amax
+            blk[1:1 + L1] = (mids * s).astype(np.float32)               # every midpoint: ties
+            blk[1 + L1:1 + 2 * L1] = np.nextafter(mids * s, np.inf).astype(np.float32)
+            blk[1 + 2 * L1:] = (rng.normal(0, 0.4, 127 - 2 * L1) * s).astype(np.float32)
     w[0, 256:384] = 0.0                                       # all-zero group -> scale 1
     w[1, 256] = 1e6                                           # clamps to 65504
     w[2, 384:512] = 0.0
-    w[2, 384] = np.float32(1 + 2 ** -11)                      # fp16 tie in the scale -> even
+    w[2, 384] = np.float32((1 + 2 ** -11) * amax)              # fp16 tie in the scale -> even
     w[3, 384:512] = 0.0
-    w[3, 384] = -np.float32(1 + 3 * 2 ** -11)
-    assert_same(w, T, 4, 128, "absmax", lutq)
-    Ti = tables.make("int", 4)
-    assert_same(w, Ti, 4, 128, "range", lutq)
-    assert_same(w, Ti, 4, 0, "range", lutq)
+    w[3, 384] = -np.float32((1 + 3 * 2 ** -11) * amax)
+    assert_same(w, T, bits, 128, "absmax", lutq)
+    Ti = tables.make("int", bits)
+    assert_same(w, Ti, bits, 128, "range", lutq)
+    assert_same(w, Ti, bits, 0, "range", lutq)
+
+
+def test_quantize_subnormal_weights_and_scales(lutq):
+    # A table with a midpoint at exactly 0: the sign of fp32 subnormal
+    # weights and of signed zeros decides their codes (+0 and -0 tie there).
+    T = np.array([-1.5, -0.5, 0.5, 1.5], np.float16)
+    sub = np.float32(2.0 ** -149)
+    rng = np.random.default_rng(78)
+    w = np.zeros((4, 256), np.float32)
+    w[0, :128] = sub * rng.integers(-40, 41, 128).astype(np.float32)  # subnormals only: scale 1
+    w[0, :4] = [sub, -sub, 0.0, -0.0]
+    w[1] = rng.normal(0, 1e-6, 256).astype(np.float32)                # fp16-subnormal scales
+    w[2] = rng.normal(0, 1e-7, 256).astype(np.float32)
+    w[2, 5] = np.float32(3e-5)
+    w[3, :128] = rng.normal(0, 1, 128).astype(np.float32)             # subnormals beside normals
+    w[3, 10:20] = sub * np.arange(-5, 5, dtype=np.float32)
+    for bits_t, rule in ((T, "absmax"), (T, "range")):
+        assert_same(w, bits_t, 2, 128, rule, lutq)
+        assert_same(w, bits_t, 2, 0, rule, lutq)
 
 
 @pytest.mark.parametrize("group", [128, 0])

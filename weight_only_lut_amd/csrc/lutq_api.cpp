@@ -315,7 +315,7 @@ int check_quant(const float* w, const uint16_t* lut, int bits, int N, int K, int
   if (rule != LUTQ_RULE_ABSMAX && rule != LUTQ_RULE_RANGE) return LUTQ_EINVAL;
   if (N == 0 || K == 0) return LUTQ_OK;
   if (!w || !lut) return LUTQ_EINVAL;
-  if (!aligned(w, 8) || !aligned(lut, 2)) return LUTQ_EALIGN;
+  if (!aligned(w, 16) || !aligned(lut, 2)) return LUTQ_EALIGN;
   return LUTQ_OK;
 }
 
@@ -361,7 +361,7 @@ int lutq_quantize(const float* w, const uint16_t* lut, int bits, int N, int K, i
   if (rc) return rc;
   if (N == 0 || K == 0) return LUTQ_OK;
   if (!codes || !scales) return LUTQ_EINVAL;
-  if (!aligned(codes, 2) || !aligned(scales, 2)) return LUTQ_EALIGN;
+  if (!aligned(codes, 4) || !aligned(scales, 2)) return LUTQ_EALIGN;
   lutq::QuantScratch sc;
   std::memset(&sc, 0, sizeof sc);
   if (group == 0) {  // tensor-wise: the extrema and the scale pass through scratch

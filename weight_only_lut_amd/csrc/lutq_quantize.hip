@@ -6,12 +6,18 @@
 // abstract: the grid is an arbitrary table, uniform or not. LogbQuant
 // abstract: tensor-wise scales, logarithmic tables with an adjustable base.
 //
-// One wave per group (grouped scales): lanes hold consecutive element pairs,
-// the group's max / min / |max| come from a wave reduction, the scale from
-// fp64 arithmetic rounded once to fp16, and every code from the fp64
-// quotient w / s compared exactly against the table's midpoints. Tensor-wise
-// scales take three launches: per-workgroup extrema, one reduction to the
-// scale, then the codes.
+// Layout: a group of 128 weights spans 8 lanes (16 weights per lane, four
+// 16-byte loads), a wave takes 1024 weights per step and loads the next step
+// while it codes this one. The group's extrema come from a lane reduction
+// (DPP), its scale from fp64 arithmetic rounded once to fp16, and each code
+// from comparisons of the fp32 weight against per-group fp32 thresholds that
+// decide exactly what the fp64 quotient w / s decides against the table's
+// midpoints (derivation at thr32 below): three thresholds in registers pick a
+// quarter of the sorted table, one 16-byte LDS read brings that quarter's
+// three thresholds and four codes. Tensor-wise scales take three launches:
+// per-workgroup extrema, one reduction to the scale, then the codes.
+#include <climits>
+
 #include "lutq_quant.h"
 
 namespace lutq {
@@ -61,94 +67,198 @@ struct QuantParams {
   uint8_t* codes;          // null: do not write codes
   uint16_t* scales;        // null: do not write scales
   double* err_partial;     // per workgroup; null: no error
-  float* extrema;          // tensor-wise: per-workgroup [max, min, |max|]
+  float* extrema;          // tensor-wise: per-workgroup [max, min]
   uint16_t* tscale;        // tensor-wise: the scale (fp16 bits)
-  long long n;             // elements (tensor-wise kernels)
+  long long n;             // weights
   int N, K, group, rule;
-  long long ngroups;       // groups of `group` elements (grouped kernel)
+  long long nrows;         // groups (grouped) or 128-weight pieces (tensor-wise)
 };
 
 constexpr int kQuantThreads = 256;
 constexpr int kQuantWaves = kQuantThreads / kWave;
+constexpr int kLaneElems = 16;                // weights per lane per step: four 16-byte loads
+constexpr int kStep = kWave * kLaneElems;     // weights per wave per step (held groups)
+constexpr int kPiece = 128;                   // a 128-weight piece spans 8 lanes
+constexpr int kMaxAreas = kStep / kPiece;     // groups per wave per step, at most
 
-__device__ inline double h2d(uint16_t h) { return (double)__builtin_bit_cast(_Float16, h); }
+__device__ __forceinline__ double h2d(uint16_t h) { return (double)__builtin_bit_cast(_Float16, h); }
 
-// The table, sorted: midpoints between neighbours, the code of each sorted
-// entry and the lower code of each neighbour pair (for exact ties).
+// The table as one lane needs it. With the L entries sorted ascending,
+// midpoint m lies between sorted entries m and m + 1; lane j (mod 8) of a
+// group owns midpoints j and j + 8 when the group's thresholds are built.
 template <int L>
-struct Grid {
-  double mid[L - 1];
-  uint32_t ord[L];
-  uint32_t tie[L - 1];
+struct Table {
+  double mid_a, mid_b;      // midpoints j and j + 8 (0 where they do not exist)
+  bool up_a, up_b;          // an exact tie there goes to the upper entry (its code is the lower)
+  uint32_t ord_lo, ord_hi;  // code of sorted entry q in bits 4(q mod 8) of ord_lo (q < 8) / ord_hi
   double tmax, tmin, amax;
 };
 
+// Sorts the table in LDS (rank by value, ties by index: entries are
+// distinct) and fills the lane's view; `tval` (LDS, L entries) receives the
+// entries in code order. Contains a workgroup barrier.
 template <int L>
-__device__ void load_grid(const uint16_t* lut, Grid<L>& g) {
+__device__ void load_table(const uint16_t* lut, Table<L>& t, double* tval) {
   __shared__ double sv[L];
   __shared__ uint32_t so[L];
   const int tid = threadIdx.x;
   if (tid < L) {
     const double v = h2d(lut[tid]);
     int rank = 0;
-    for (int j = 0; j < L; ++j) {
-      const double u = h2d(lut[j]);
-      rank += (u < v) || (u == v && j < tid);
+    for (int i = 0; i < L; ++i) {
+      const double u = h2d(lut[i]);
+      rank += (u < v) || (u == v && i < tid);
     }
     sv[rank] = v;
     so[rank] = (uint32_t)tid;
+    tval[tid] = v;
   }
   __syncthreads();
-#pragma unroll
-  for (int j = 0; j < L; ++j) g.ord[j] = so[j];
-#pragma unroll
-  for (int j = 0; j + 1 < L; ++j) {
-    g.mid[j] = (sv[j] + sv[j + 1]) * 0.5;  // exact: fp16 values
-    g.tie[j] = min(so[j], so[j + 1]);
+  const int j = tid & 7;
+  t.mid_a = t.mid_b = 0.0;
+  t.up_a = t.up_b = false;
+  if (j < L - 1) {
+    t.mid_a = (sv[j] + sv[j + 1]) * 0.5;  // exact: fp16 values
+    t.up_a = so[j + 1] < so[j];
   }
-  g.tmin = sv[0];
-  g.tmax = sv[L - 1];
-  g.amax = fmax(-sv[0], sv[L - 1]);
+  if (j + 8 < L - 1) {
+    t.mid_b = (sv[j + 8] + sv[j + 9]) * 0.5;
+    t.up_b = so[j + 9] < so[j + 8];
+  }
+  t.ord_lo = t.ord_hi = 0;
+#pragma unroll
+  for (int q = 0; q < L; ++q) {
+    if (q < 8) t.ord_lo |= so[q] << (4 * q);
+    else t.ord_hi |= so[q] << (4 * (q - 8));
+  }
+  t.tmin = sv[0];
+  t.tmax = sv[L - 1];
+  t.amax = fmax(-sv[0], sv[L - 1]);
 }
 
-// Code of the entry nearest to r; an exact tie to the lower code.
-template <int L>
-__device__ inline uint32_t nearest_code(double r, const Grid<L>& g) {
-  uint32_t c = g.ord[0];
-#pragma unroll
-  for (int j = 0; j + 1 < L; ++j) c = r > g.mid[j] ? g.ord[j + 1] : (r == g.mid[j] ? g.tie[j] : c);
-  return c;
+// fp64 -> fp16 bits, round to nearest even, for 0 <= d <= 65504: round to
+// odd into fp32 (truncate, then set the last bit if anything was dropped),
+// then round to nearest even into fp16. fp32 keeps 13 more significand bits
+// than fp16, so the two roundings give the one correct rounding (Boldo and
+// Melquiond, "Emulation of FMA and correctly rounded sums: proved algorithms
+// using rounding to odd").
+__device__ __forceinline__ uint16_t f16_bits(double d) {
+  float f = (float)d;
+  const double b = (double)f;
+  if (b != d) {
+    uint32_t u = __builtin_bit_cast(uint32_t, f);
+    if (b > d) --u;
+    f = __builtin_bit_cast(float, u | 1u);
+  }
+  return __builtin_bit_cast(uint16_t, (_Float16)f);
 }
 
 // fp16 scale bits from the extrema of a group (or of the tensor).
-template <int L>
-__device__ inline uint16_t scale_bits(float mx, float mn, float am, int rule, const Grid<L>& g) {
-  double s = rule == kRuleAbsmax ? (double)am / g.amax
-                                      : fmax((double)mx / g.tmax, (double)mn / g.tmin);
-  s = fmin(s, 65504.0);
-  uint16_t h = f64_to_f16_rne(s);
-  if ((h & 0x7FFF) == 0) h = 0x3C00;  // zero -> 1
-  return h;
+__device__ __forceinline__ uint16_t scale_bits(float mx, float mn, int rule, double tmax,
+                                               double tmin, double amax) {
+  double s = rule == kRuleAbsmax ? fmax((double)mx, -(double)mn) / amax
+                                 : fmax((double)mx / tmax, (double)mn / tmin);
+  s = fmin(s, 65504.0);  // s >= 0 under both rules
+  const uint16_t h = f16_bits(s);
+  return (h & 0x7FFF) == 0 ? (uint16_t)0x3C00 : h;  // zero -> 1
 }
 
-__device__ inline float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-  return v;
+// Why fp32 thresholds decide exactly what the fp64 quotient decides. Let w be
+// an fp32 weight, s > 0 an fp16 scale and m a midpoint of two fp16 entries
+// (at most 40 significant bits). t = m * s has at most 51 bits, so it is
+// exact in fp64. If w / s != m, then |w / s - m| = |w - t| / s, where w - t
+// is a nonzero multiple of w's last bit or of t's; either way it exceeds half
+// an fp64 ulp of m, so rounding the quotient cannot reach m and
+//   fl(w / s) > m  <=>  w > t,   fl(w / s) == m  <=>  w == t.
+// For every fp32 w:  w > t  <=> w > (largest fp32 <= t),
+//                    w >= t <=> w > (largest fp32 <  t).
+// `up` picks the second form (an exact tie goes to the upper entry).
+__device__ __forceinline__ float prev_f32(float f) {  // next fp32 toward -infinity (f finite)
+  const uint32_t u = __builtin_bit_cast(uint32_t, f);
+  if ((u & 0x7FFFFFFFu) == 0) return __builtin_bit_cast(float, 0x80000001u);
+  return __builtin_bit_cast(float, (int32_t)u > 0 ? u - 1 : u + 1);
 }
-__device__ inline float wave_min(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fminf(v, __shfl_xor(v, o));
-  return v;
+__device__ __forceinline__ float thr32(double t, bool up) {
+  const float f = (float)t;  // |t| < 2^33: finite
+  const double b = (double)f;
+  return (up ? b >= t : b > t) ? prev_f32(f) : f;
 }
-__device__ inline double wave_sum(double v) {
+
+// Integer keys with the order of the floats (finite values): max / min on
+// them fuse with DPP moves into one instruction.
+__device__ __forceinline__ int fkey(float f) {
+  const int u = __builtin_bit_cast(int, f);
+  return u ^ ((u >> 31) & 0x7FFFFFFF);
+}
+__device__ __forceinline__ float funkey(int k) {
+  return __builtin_bit_cast(float, k ^ ((k >> 31) & 0x7FFFFFFF));
+}
+template <int CTRL>
+__device__ __forceinline__ int dpp(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+constexpr int kDppXor1 = 0xB1;         // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;         // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;  // lane i <-> 7 - i in each half row
+constexpr int kDppMirror = 0x140;      // lane i <-> 15 - i in each row
+
+// Max and min over the G consecutive lanes of a group (G = 8 .. 64).
+template <int G, bool MAX>
+__device__ __forceinline__ int group_reduce(int k) {
+  auto op = [](int a, int b) { return MAX ? max(a, b) : min(a, b); };
+  k = op(k, dpp<kDppXor1>(k));
+  k = op(k, dpp<kDppXor2>(k));
+  k = op(k, dpp<kDppHalfMirror>(k));       // quads of a half row
+  if constexpr (G >= 16) k = op(k, dpp<kDppMirror>(k));   // halves of a row
+  if constexpr (G >= 32) k = op(k, __shfl_xor(k, 16));
+  if constexpr (G >= 64) k = op(k, __shfl_xor(k, 32));
+  return k;
+}
+
+// The search structure of one group, in LDS (five 16-byte rows):
+//   row q < 4: thresholds 4q, 4q + 1, 4q + 2 and, in .w, the codes of sorted
+//              positions 4q .. 4q + 3 (one byte each);
+//   row 4    : thresholds 3, 7, 11.
+// A weight's sorted position is 4q + c: q from thresholds 3 / 7 / 11 (held
+// in registers), c from the three thresholds of row q; the code is byte c of
+// row q's .w. Threshold m sits in slot thr_slot(m) of the 20 floats.
+__device__ __forceinline__ int thr_slot(int m) { return (m & 3) == 3 ? 16 + (m >> 2) : m; }
+
+// Codes of sorted positions 4q .. 4q + 3 as four bytes.
+template <int L>
+__device__ __forceinline__ uint32_t row_codes(const Table<L>& t, int q) {
+  const uint32_t nib = (q < 2 ? t.ord_lo : t.ord_hi) >> (16 * (q & 1));
+  return (nib & 0xF) | ((nib >> 4 & 0xF) << 8) | ((nib >> 8 & 0xF) << 16) | ((nib >> 12 & 0xF) << 24);
+}
+
+// Registers a lane keeps per group for the first level of the search.
+struct Level1 { float a, b, c; f32x4 row0; };
+
+template <int L>
+__device__ __forceinline__ uint32_t code_of(float w, const Level1& l1, const f32x4* area) {
+  f32x4 r;
+  if constexpr (L == 16) {
+    const bool b3 = w > l1.b;                       // threshold 7
+    const bool b2 = w > (b3 ? l1.c : l1.a);         // threshold 11 or 3
+    r = area[(b3 ? 2 : 0) + (int)b2];
+  } else if constexpr (L == 8) {
+    r = area[(int)(w > l1.a)];                      // threshold 3
+  } else {
+    r = l1.row0;
+  }
+  const uint32_t c = (uint32_t)(w > r[0]) + (uint32_t)(w > r[1]) + (uint32_t)(w > r[2]);
+  // through a scalar: a bit cast of a vector element reads the vector's first one
+  const float codes = r[3];
+  return __builtin_amdgcn_ubfe(__builtin_bit_cast(uint32_t, codes), c * 8, 8);
+}
+
+// Fixed-order workgroup sum of one double per lane -> err_partial[block].
+__device__ __forceinline__ double wave_sum(double v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
   return v;
 }
-
-// Fixed-order workgroup sum of one double per wave -> err_partial[block].
-__device__ inline void block_error(double e, double* out) {
+__device__ __forceinline__ void block_error(double e, double* out) {
   __shared__ double we[kQuantWaves];
   e = wave_sum(e);
   const int wave = threadIdx.x / kWave;
@@ -162,143 +272,259 @@ __device__ inline void block_error(double e, double* out) {
   }
 }
 
-// Codes (and error) for the pair of weights (w0, w1) under scale s16.
-template <int L, bool ERR>
-__device__ inline uint32_t code_pair(float w0, float w1, uint16_t s16, const Grid<L>& g,
-                                     const uint16_t* lut, double& err) {
-  const double s = h2d(s16);
-  const uint32_t c0 = nearest_code<L>((double)w0 / s, g);
-  const uint32_t c1 = nearest_code<L>((double)w1 / s, g);
-  if constexpr (ERR) {
-    const double d0 = (double)w0 - h2d(lut[c0]) * s;
-    const double d1 = (double)w1 - h2d(lut[c1]) * s;
-    err += d0 * d0 + d1 * d1;
-  }
-  return c0 | (c1 << 8);
+// A raw buffer resource over elements [e0, n) of `base` (`esize` bytes each):
+// offsets past the end read zeros and drop stores.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tail_rsrc(const void* base, long long e0,
+                                                            long long n, int esize) {
+  const long long rem = n - e0;
+  if (rem <= 0) return make_rsrc(base, 0);
+  const long long bytes = rem * esize;
+  return make_rsrc(static_cast<const char*>(base) + e0 * esize,
+                   (uint32_t)(bytes < (1ll << 30) ? bytes : (1ll << 30)));
 }
 
-// Grouped scales: one wave per group, groups dealt round-robin to waves.
-template <int L, bool ERR>
-__global__ __launch_bounds__(kQuantThreads) void quant_group_kernel(const QuantParams p) {
-  Grid<L> g;
-  load_grid<L>(p.lut, g);
-  const int lane = threadIdx.x & 63;
+// Ordering of a wave's own LDS traffic: LDS executes one wave's operations
+// in order, so only the compiler has to be kept from moving them.
+__device__ __forceinline__ void wave_lds_fence() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Round-to-nearest onto the table.
+// Held groups (GL > 0): a group of 16 GL weights spans GL consecutive lanes,
+// 16 weights per lane (float4 i of lane j at 4 j + 4 GL i), and stays in
+// registers between its extrema and its codes; a wave takes 1024 weights per
+// step (64 / GL groups) and loads the next step while coding this one.
+// Tensor-wise: the same with GL = 8 over 128-weight pieces and one scale.
+// GL == 0: groups of any multiple of 128 over 8 lanes, read twice (extrema,
+// then codes), 8 groups per step.
+template <int L, int GL, bool ERR, bool TENSOR>
+__global__ __launch_bounds__(kQuantThreads) void quant_kernel(const QuantParams p) {
+  __shared__ double tval[L];
+  __shared__ f32x4 areas[kQuantWaves][kMaxAreas][5];
+  Table<L> t;
+  load_table<L>(p.lut, t, tval);
+  constexpr int G = GL > 0 ? GL : 8;        // lanes per group
+  constexpr int kGroups = kWave / G;        // groups per step
+  const int lane = threadIdx.x & (kWave - 1);
+  // wave-uniform in a scalar register, so that the buffer resources built
+  // from it are too (a per-lane resource costs a loop over distinct values)
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int r = lane / G;                   // group within the step
+  const int j = lane % G;
+  f32x4* area = areas[wave][TENSOR ? 0 : r];
+  const long long gsize = TENSOR ? kPiece : p.group;          // weights per group
+  const long long per_step = gsize * kGroups;
+  const long long nunits = (p.nrows + kGroups - 1) / kGroups;
   const long long nwaves = (long long)gridDim.x * kQuantWaves;
-  const int gpr = p.K / p.group;
-  const int pieces = p.group / kChunk;  // 128 elements per piece, 2 per lane
-  double err = 0.0;
-  for (long long gi = (long long)blockIdx.x * kQuantWaves + threadIdx.x / kWave; gi < p.ngroups;
-       gi += nwaves) {
-    const long long row = gi / gpr;
-    const long long e0 = row * p.K + (gi - row * gpr) * (long long)p.group;
-    const float2* src = reinterpret_cast<const float2*>(p.w + e0) + lane;
-    float mx = -__builtin_huge_valf(), mn = __builtin_huge_valf(), am = 0.f;
-    for (int i = 0; i < pieces; ++i) {
-      const float2 v = src[i * kWave];
-      mx = fmaxf(mx, fmaxf(v.x, v.y));
-      mn = fminf(mn, fminf(v.x, v.y));
-      am = fmaxf(am, fmaxf(fabsf(v.x), fabsf(v.y)));
+  const long long wave0 = (long long)blockIdx.x * kQuantWaves + wave;
+
+  // the codes column of every search row, once
+  if (lane < kMaxAreas * 4) {
+    f32x4* a = areas[wave][lane >> 2];
+    a[lane & 3][3] = __builtin_bit_cast(float, row_codes<L>(t, lane & 3));
+  }
+
+  Level1 l1;
+  double s = 1.0;
+  // This group's thresholds for scale s16 into its area, then level 1 back.
+  auto build = [&](uint16_t s16) __attribute__((always_inline)) {
+    s = h2d(s16);
+    wave_lds_fence();  // the previous group's reads come first
+    if (j < 8) {
+      if (j < L - 1) reinterpret_cast<float*>(area)[thr_slot(j)] = thr32(t.mid_a * s, t.up_a);
+      if (j + 8 < L - 1)
+        reinterpret_cast<float*>(area)[thr_slot(j + 8)] = thr32(t.mid_b * s, t.up_b);
     }
-    mx = wave_max(mx);
-    mn = wave_min(mn);
-    am = wave_max(am);
-    const uint16_t s16 = scale_bits<L>(mx, mn, am, p.rule, g);
-    if (p.scales && lane == 0) p.scales[gi] = s16;
-    for (int i = 0; i < pieces; ++i) {
-      const float2 v = src[i * kWave];
-      const uint32_t cc = code_pair<L, ERR>(v.x, v.y, s16, g, p.lut, err);
-      if (p.codes)
-        *reinterpret_cast<uint16_t*>(p.codes + e0 + 2 * (i * kWave + lane)) = (uint16_t)cc;
+    wave_lds_fence();
+    if constexpr (L == 4) {
+      l1.row0 = area[0];
+    } else {
+      const f32x4 r4 = area[4];
+      l1.a = r4[0];
+      l1.b = r4[1];
+      l1.c = r4[2];
+    }
+  };
+  if constexpr (TENSOR) build(*p.tscale);
+  else wave_lds_fence();
+  double err = 0.0;
+
+  // Scale of a group from this lane's extrema keys; store it, build the search.
+  auto prepare = [&](int kmx, int kmn, long long gi) __attribute__((always_inline)) {
+    const float mx = funkey(group_reduce<G, true>(kmx));
+    const float mn = funkey(group_reduce<G, false>(kmn));
+    const uint16_t s16 = scale_bits(mx, mn, p.rule, t.tmax, t.tmin, t.amax);
+    if (p.scales && j == 0 && gi < p.nrows) p.scales[gi] = s16;
+    build(s16);
+  };
+  auto extrema = [&](f32x4 v, int& kmx, int& kmn) __attribute__((always_inline)) {
+    kmx = max(kmx, fkey(fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3]))));
+    kmn = min(kmn, fkey(fminf(fminf(v[0], v[1]), fminf(v[2], v[3]))));
+  };
+  // Codes of four weights -> one dword of bytes; error of the active ones.
+  auto code4 = [&](f32x4 v, bool active) __attribute__((always_inline)) {
+    uint32_t packed = 0;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const uint32_t code = code_of<L>(v[c], l1, area);
+      packed |= code << (8 * c);
+      if constexpr (ERR) {
+        const double d = (double)v[c] - tval[code] * s;
+        err += active ? d * d : 0.0;
+      }
+    }
+    return packed;
+  };
+  auto load = [&](__amdgpu_buffer_rsrc_t rs, uint32_t off) __attribute__((always_inline)) {
+    return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, kNontemporal));
+  };
+  auto store = [&](__amdgpu_buffer_rsrc_t rc, uint32_t off, uint32_t v) __attribute__((always_inline)) {
+    __builtin_amdgcn_raw_buffer_store_b32(v, rc, off, 0, 0);
+  };
+
+  if constexpr (GL > 0 || TENSOR) {
+    const uint32_t lane_off = (uint32_t)(r * gsize + 4 * j);  // weights, from the step's start
+    f32x4 bufA[4], bufB[4];
+    auto fetch = [&](f32x4 (&b)[4], long long unit) __attribute__((always_inline)) {
+      const auto rs = tail_rsrc(p.w, unit * per_step, p.n, 4);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) b[i] = load(rs, 4u * (lane_off + 4 * G * i));
+    };
+    auto step = [&](const f32x4 (&b)[4], long long unit) __attribute__((always_inline)) {
+      const long long gi = unit * kGroups + r;
+      if constexpr (!TENSOR) {
+        int kmx = INT_MIN, kmn = INT_MAX;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) extrema(b[i], kmx, kmn);
+        prepare(kmx, kmn, gi);
+      }
+      const bool active = gi < p.nrows;
+      const auto rc = tail_rsrc(p.codes, unit * per_step, p.codes ? p.n : 0, 1);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t packed = code4(b[i], active);
+        if (p.codes) store(rc, lane_off + 4 * G * i, packed);
+      }
+    };
+    long long unit = wave0;
+    if (unit < nunits) {
+      fetch(bufA, unit);
+      for (;;) {
+        fetch(bufB, unit + nwaves);  // past the end: zeros, no memory access
+        step(bufA, unit);
+        unit += nwaves;
+        if (unit >= nunits) break;
+        fetch(bufA, unit + nwaves);
+        step(bufB, unit);
+        unit += nwaves;
+        if (unit >= nunits) break;
+      }
+    }
+  } else {
+    const int pieces = (int)(gsize / kPiece);
+    const uint32_t lane_off = (uint32_t)(r * gsize + 4 * j);
+    for (long long unit = wave0; unit < nunits; unit += nwaves) {
+      const long long gi = unit * kGroups + r;
+      const auto rs = tail_rsrc(p.w, unit * per_step, p.n, 4);
+      int kmx = INT_MIN, kmn = INT_MAX;
+      for (int q = 0; q < pieces; ++q)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) extrema(load(rs, 4u * (lane_off + q * kPiece + 32 * i)), kmx, kmn);
+      prepare(kmx, kmn, gi);
+      const bool active = gi < p.nrows;
+      const auto rc = tail_rsrc(p.codes, unit * per_step, p.codes ? p.n : 0, 1);
+      for (int q = 0; q < pieces; ++q)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t off = lane_off + q * kPiece + 32 * i;
+          const uint32_t packed = code4(load(rs, 4u * off), active);
+          if (p.codes) store(rc, off, packed);
+        }
     }
   }
   if constexpr (ERR) block_error(err, p.err_partial);
 }
 
-// Tensor-wise, pass 1: per-workgroup max, min, |max| over pairs of weights.
+// Tensor-wise, pass 1: per-workgroup max and min.
 __global__ __launch_bounds__(kQuantThreads) void tensor_extrema_kernel(const QuantParams p) {
-  __shared__ float part[3][kQuantWaves];
-  const long long npairs = p.n / 2;
-  float mx = -__builtin_huge_valf(), mn = __builtin_huge_valf(), am = 0.f;
-  const float2* src = reinterpret_cast<const float2*>(p.w);
-  for (long long i = (long long)blockIdx.x * kQuantThreads + threadIdx.x; i < npairs;
-       i += (long long)gridDim.x * kQuantThreads) {
-    const float2 v = src[i];
-    mx = fmaxf(mx, fmaxf(v.x, v.y));
-    mn = fminf(mn, fminf(v.x, v.y));
-    am = fmaxf(am, fmaxf(fabsf(v.x), fabsf(v.y)));
+  __shared__ float part[2][kQuantWaves];
+  const long long nvec = p.n / 4;  // n is a multiple of 128
+  float mx = -__builtin_huge_valf(), mn = __builtin_huge_valf();
+  const f32x4* src = reinterpret_cast<const f32x4*>(p.w);
+  const long long stride = (long long)gridDim.x * kQuantThreads;
+  long long i = (long long)blockIdx.x * kQuantThreads + threadIdx.x;
+  for (; i + 3 * stride < nvec; i += 4 * stride) {  // four loads in flight
+    f32x4 v[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) v[k] = __builtin_nontemporal_load(src + i + k * stride);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      mx = fmaxf(mx, fmaxf(fmaxf(v[k][0], v[k][1]), fmaxf(v[k][2], v[k][3])));
+      mn = fminf(mn, fminf(fminf(v[k][0], v[k][1]), fminf(v[k][2], v[k][3])));
+    }
   }
-  mx = wave_max(mx);
-  mn = wave_min(mn);
-  am = wave_max(am);
+  for (; i < nvec; i += stride) {
+    const f32x4 v = __builtin_nontemporal_load(src + i);
+    mx = fmaxf(mx, fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])));
+    mn = fminf(mn, fminf(fminf(v[0], v[1]), fminf(v[2], v[3])));
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    mx = fmaxf(mx, __shfl_xor(mx, o));
+    mn = fminf(mn, __shfl_xor(mn, o));
+  }
   const int wave = threadIdx.x / kWave;
   if ((threadIdx.x & 63) == 0) {
     part[0][wave] = mx;
     part[1][wave] = mn;
-    part[2][wave] = am;
   }
   __syncthreads();
   if (threadIdx.x == 0) {
-    for (int i = 1; i < kQuantWaves; ++i) {
-      mx = fmaxf(mx, part[0][i]);
-      mn = fminf(mn, part[1][i]);
-      am = fmaxf(am, part[2][i]);
+    for (int k = 1; k < kQuantWaves; ++k) {
+      mx = fmaxf(mx, part[0][k]);
+      mn = fminf(mn, part[1][k]);
     }
-    p.extrema[3 * blockIdx.x + 0] = mx;
-    p.extrema[3 * blockIdx.x + 1] = mn;
-    p.extrema[3 * blockIdx.x + 2] = am;
+    p.extrema[2 * blockIdx.x + 0] = mx;
+    p.extrema[2 * blockIdx.x + 1] = mn;
   }
 }
 
 // Tensor-wise, pass 2 (one workgroup): the scale from all partial extrema.
 template <int L>
 __global__ __launch_bounds__(kQuantThreads) void tensor_scale_kernel(const QuantParams p, int nparts) {
-  Grid<L> g;
-  load_grid<L>(p.lut, g);
-  float mx = -__builtin_huge_valf(), mn = __builtin_huge_valf(), am = 0.f;
+  __shared__ float part[2][kQuantWaves];
+  float mx = -__builtin_huge_valf(), mn = __builtin_huge_valf();
   for (int i = threadIdx.x; i < nparts; i += kQuantThreads) {
-    mx = fmaxf(mx, p.extrema[3 * i + 0]);
-    mn = fminf(mn, p.extrema[3 * i + 1]);
-    am = fmaxf(am, p.extrema[3 * i + 2]);
+    mx = fmaxf(mx, p.extrema[2 * i + 0]);
+    mn = fminf(mn, p.extrema[2 * i + 1]);
   }
-  __shared__ float part[3][kQuantWaves];
-  mx = wave_max(mx);
-  mn = wave_min(mn);
-  am = wave_max(am);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    mx = fmaxf(mx, __shfl_xor(mx, o));
+    mn = fminf(mn, __shfl_xor(mn, o));
+  }
   const int wave = threadIdx.x / kWave;
   if ((threadIdx.x & 63) == 0) {
     part[0][wave] = mx;
     part[1][wave] = mn;
-    part[2][wave] = am;
   }
   __syncthreads();
   if (threadIdx.x == 0) {
-    for (int i = 0; i < kQuantWaves; ++i) {
-      mx = fmaxf(mx, part[0][i]);
-      mn = fminf(mn, part[1][i]);
-      am = fmaxf(am, part[2][i]);
+    for (int k = 0; k < kQuantWaves; ++k) {
+      mx = fmaxf(mx, part[0][k]);
+      mn = fminf(mn, part[1][k]);
     }
-    const uint16_t s16 = scale_bits<L>(mx, mn, am, p.rule, g);
+    double tmin = h2d(p.lut[0]), tmax = tmin;
+    for (int k = 1; k < L; ++k) {
+      tmin = fmin(tmin, h2d(p.lut[k]));
+      tmax = fmax(tmax, h2d(p.lut[k]));
+    }
+    const uint16_t s16 = scale_bits(mx, mn, p.rule, tmax, tmin, fmax(-tmin, tmax));
     *p.tscale = s16;
     if (p.scales) p.scales[0] = s16;
   }
-}
-
-// Tensor-wise, pass 3: codes (and error) under the one scale.
-template <int L, bool ERR>
-__global__ __launch_bounds__(kQuantThreads) void tensor_codes_kernel(const QuantParams p) {
-  Grid<L> g;
-  load_grid<L>(p.lut, g);
-  const uint16_t s16 = *p.tscale;
-  const long long npairs = p.n / 2;
-  const float2* src = reinterpret_cast<const float2*>(p.w);
-  double err = 0.0;
-  for (long long i = (long long)blockIdx.x * kQuantThreads + threadIdx.x; i < npairs;
-       i += (long long)gridDim.x * kQuantThreads) {
-    const float2 v = src[i];
-    const uint32_t cc = code_pair<L, ERR>(v.x, v.y, s16, g, p.lut, err);
-    if (p.codes) *reinterpret_cast<uint16_t*>(p.codes + 2 * i) = (uint16_t)cc;
-  }
-  if constexpr (ERR) block_error(err, p.err_partial);
 }
 
 // Fixed-order sum of the per-workgroup errors (one workgroup).
@@ -316,29 +542,47 @@ __global__ __launch_bounds__(kQuantThreads) void error_sum_kernel(const double* 
   }
 }
 
+template <int L, int GL, bool TENSOR>
+void launch_codes(const QuantParams& p, int nblocks, bool err, hipStream_t s) {
+  if (err)
+    quant_kernel<L, GL, true, TENSOR><<<nblocks, kQuantThreads, 0, s>>>(p);
+  else
+    quant_kernel<L, GL, false, TENSOR><<<nblocks, kQuantThreads, 0, s>>>(p);
+}
+
+// Workgroups for `units` wave steps: one step per wave, at most kQuantMaxBlocks.
+int blocks_for(long long units) {
+  const long long want = (units + kQuantWaves - 1) / kQuantWaves;
+  return (int)(want < kQuantMaxBlocks ? want : kQuantMaxBlocks);
+}
+
 template <int L>
 hipError_t launch_l(const QuantScratch& sc, const QuantParams& p0, bool err, hipStream_t s) {
   QuantParams p = p0;
   p.err_partial = sc.err_partial;
   int nblocks;
   if (p.group != 0) {
-    const long long want = (p.ngroups + kQuantWaves - 1) / kQuantWaves;
-    nblocks = (int)(want < kQuantMaxBlocks ? want : kQuantMaxBlocks);
-    if (err)
-      quant_group_kernel<L, true><<<nblocks, kQuantThreads, 0, s>>>(p);
-    else
-      quant_group_kernel<L, false><<<nblocks, kQuantThreads, 0, s>>>(p);
+    p.nrows = p.n / p.group;
+    const int gl = p.group / kLaneElems;  // lanes per held group
+    const int per_step = gl == 8 || gl == 16 || gl == 32 || gl == 64 ? kWave / gl : 8;
+    nblocks = blocks_for((p.nrows + per_step - 1) / per_step);
+    switch (gl) {
+      case 8: launch_codes<L, 8, false>(p, nblocks, err, s); break;
+      case 16: launch_codes<L, 16, false>(p, nblocks, err, s); break;
+      case 32: launch_codes<L, 32, false>(p, nblocks, err, s); break;
+      case 64: launch_codes<L, 64, false>(p, nblocks, err, s); break;
+      default: launch_codes<L, 0, false>(p, nblocks, err, s); break;
+    }
   } else {
     p.extrema = sc.extrema;
     p.tscale = sc.tscale;
-    const long long want = (p.n / 2 + kQuantThreads - 1) / kQuantThreads;
-    nblocks = (int)(want < kQuantMaxBlocks ? want : kQuantMaxBlocks);
-    tensor_extrema_kernel<<<nblocks, kQuantThreads, 0, s>>>(p);
-    tensor_scale_kernel<L><<<1, kQuantThreads, 0, s>>>(p, nblocks);
-    if (err)
-      tensor_codes_kernel<L, true><<<nblocks, kQuantThreads, 0, s>>>(p);
-    else
-      tensor_codes_kernel<L, false><<<nblocks, kQuantThreads, 0, s>>>(p);
+    p.nrows = p.n / kPiece;
+    const long long want = (p.n / 4 + kQuantThreads - 1) / kQuantThreads;
+    const int nx = (int)(want < kQuantMaxBlocks ? want : kQuantMaxBlocks);
+    tensor_extrema_kernel<<<nx, kQuantThreads, 0, s>>>(p);
+    tensor_scale_kernel<L><<<1, kQuantThreads, 0, s>>>(p, nx);
+    nblocks = blocks_for((p.nrows + kMaxAreas - 1) / kMaxAreas);
+    launch_codes<L, 8, true>(p, nblocks, err, s);
   }
   if (err) error_sum_kernel<<<1, kQuantThreads, 0, s>>>(sc.err_partial, nblocks, sc.err_total);
   return hipGetLastError();
@@ -360,7 +604,6 @@ hipError_t launch_quantize(const QuantScratch& sc, const float* w, const uint16_
   p.K = K;
   p.group = group;
   p.rule = rule;
-  p.ngroups = group ? p.n / group : 0;
   switch (bits) {
     case 2: return launch_l<4>(sc, p, error, s);
     case 3: return launch_l<8>(sc, p, error, s);
