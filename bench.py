@@ -465,6 +465,55 @@ def summarize_profile(kt_dir, fetch_dir, write_dir, command=""):
     with open(os.path.join(ROOT, "profiles", "matmul_kernel_int4_up_proj_log4_70b.md"), "w") as fh:
         fh.write("\n".join(lines) + "\n")
     print(json.dumps(out, indent=1))
+    summarize_quantizer(stats, fetch_dir, write_dir, f_copy, w_copy, f_scale, w_scale, command)
+
+
+# The quantizer's kernels on the 14336 x 4096 matrix of fp32 weights, as the
+# benchmark's quantizer section runs them (name part, what it does, and its
+# algorithmic bytes per launch: weights read, codes and scales written).
+_QN, _QK = 14336, 4096
+QUANT_KERNELS = (
+    ("quant_kernel<16, 8, false, false>", "grouped g128 INT4 (range rule): extrema, scale, codes",
+     4 * _QN * _QK + _QN * _QK + 2 * _QN * (_QK // 128)),
+    ("tensor_extrema_kernel", "tensor-wise NF4, pass 1: per-workgroup extrema", 4 * _QN * _QK),
+    ("tensor_scale_kernel<16>", "tensor-wise NF4, pass 2: the scale (one workgroup)", None),
+    ("quant_kernel<16, 8, false, true>", "tensor-wise NF4, pass 3: codes", 4 * _QN * _QK + _QN * _QK),
+)
+
+
+def summarize_quantizer(stats, fetch_dir, write_dir, f_copy, w_copy, f_scale, w_scale, command):
+    """profiles/quant_kernel_*: the quantizer kernels' durations, HBM traffic
+    per launch and achieved bandwidth against the algorithmic bytes."""
+    from weight_only_lut_amd.build import QUANT_SOURCES, source_digest
+    rec = {"source_digest": source_digest(QUANT_SOURCES), "kernels": {}}
+    lines = ["# lutq quantizer kernels: rocprofv3 summary", "",
+             f"Digest of the quantizer sources: `{rec['source_digest']}`. Matrix: {_QN} x {_QK} "
+             "fp32 weights, cold (rotating copies), as the benchmark's quantizer section runs it.", "",
+             "Command:", "", "```", command or "(not recorded)", "```", "",
+             f"Counter calibration as the matmul summary: copy FETCH_SIZE {f_copy} KiB, "
+             f"WRITE_SIZE {w_copy} KiB for {COPY_BYTES >> 20} MiB.", "",
+             "| kernel | what | calls | avg us | algorithmic MB | achieved GB/s | traffic MB (fetch + write) |",
+             "|---|---|---|---|---|---|---|"]
+    for part, what, algo in QUANT_KERNELS:
+        dur = [r for r in stats if part in r["Name"]]
+        avg = float(dur[0]["AverageNs"]) / 1e3 if dur else None
+        f, _ = _counter_per_dispatch(fetch_dir, "FETCH_SIZE", part)
+        w, _ = _counter_per_dispatch(write_dir, "WRITE_SIZE", part)
+        traffic = (round(f * 1024 * f_scale + w * 1024 * w_scale)
+                   if None not in (f, w, f_scale, w_scale) else None)
+        gbps = algo / (avg * 1e-6) / 1e9 if (algo and avg) else None
+        rec["kernels"][part] = {"what": what, "calls": int(dur[0]["Calls"]) if dur else 0,
+                                "avg_duration_us": avg, "algorithmic_bytes": algo,
+                                "achieved_GBps": gbps, "traffic_bytes_per_launch": traffic}
+        lines.append(f"| `{part}` | {what} | {rec['kernels'][part]['calls']} | "
+                     f"{avg if avg is None else round(avg, 3)} | "
+                     f"{'-' if not algo else round(algo / 1e6, 1)} | "
+                     f"{'-' if gbps is None else round(gbps)} | "
+                     f"{'-' if traffic is None else round(traffic / 1e6, 1)} |")
+    with open(os.path.join(ROOT, "profiles", "quant_kernel_counters.json"), "w") as fh:
+        json.dump(rec, fh, indent=1)
+    with open(os.path.join(ROOT, "profiles", "quant_kernel_int4_up_proj.md"), "w") as fh:
+        fh.write("\n".join(lines) + "\n")
 
 
 def load_traffic(workload, plan):

@@ -103,8 +103,9 @@ size_t lutq_packed_bytes(int N, int K, int bits, int group);
 
 /* Offline restructuring (FLUTE abstract: restructure the quantized weight
  * matrix offline so that unpacking needs few bit operations).
- *   codes : device, uint8 [N, K] row-major, one code per byte; bits above
- *           `bits` are ignored (masked).
+ *   codes : device, uint8 [N, K] row-major, one code per byte, 8-byte
+ *           aligned (read 8 codes at a time); bits above `bits` are ignored
+ *           (masked).
  *   dst   : device, >= lutq_packed_bytes(N, K, bits, group) bytes, 16-byte
  *           aligned; must not overlap `codes`.
  *   out   : host; filled with the descriptor (data = dst) on success.

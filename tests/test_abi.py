@@ -83,6 +83,7 @@ def test_repack_validates_before_launching(lib):
     assert call(codes=P(0)) == EINVAL
     assert call(dst=P(0)) == EINVAL
     assert call(dst=P(0x20008)) == EALIGN
+    assert call(codes=P(0x1004)) == EALIGN          # codes are read 8 at a time
     assert call(nb=100) == ESIZE
     assert call(codes=P(0x20000)) == EINVAL           # overlapping buffers
     assert lib.lutq_repack(P(0x1000), 64, 256, 4, 128, P(0x20000), 1 << 20, None, None) == EINVAL

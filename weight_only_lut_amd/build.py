@@ -62,11 +62,16 @@ def build(verbose: bool = False) -> str:
 KERNEL_SOURCES = ["lutq_device.h", "lutq_internal.h", "lutq_matmul.hip"]
 
 
-def source_digest() -> str:
-    """SHA-256 over the matmul kernel sources (to tell whether a stored profile is current)."""
+# Sources of the quantizer's device code, likewise.
+QUANT_SOURCES = ["lutq_device.h", "lutq_internal.h", "lutq_quant.h", "lutq_quantize.hip"]
+
+
+def source_digest(names=None) -> str:
+    """SHA-256 over kernel sources (to tell whether a stored profile is
+    current): the matmul's by default, or the files named."""
     import hashlib
     h = hashlib.sha256()
-    for name in KERNEL_SOURCES:
+    for name in names or KERNEL_SOURCES:
         with open(os.path.join(CSRC, name), "rb") as f:
             h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()[:16]

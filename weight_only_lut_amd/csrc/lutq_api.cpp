@@ -190,7 +190,7 @@ int lutq_repack(const uint8_t* codes, int N, int K, int bits, int group, void* d
   const size_t need = lutq_packed_bytes(N, K, bits, group);
   if (need) {
     if (!codes || !dst) return LUTQ_EINVAL;
-    if (!aligned(dst, 16)) return LUTQ_EALIGN;
+    if (!aligned(dst, 16) || !aligned(codes, 8)) return LUTQ_EALIGN;
     if (dst_bytes < need) return LUTQ_ESIZE;
     const char* a = (const char*)codes;
     const char* b = (const char*)dst;

@@ -3,9 +3,9 @@
 //
 // FLUTE abstract: the quantized weight matrix is restructured offline so that
 // unpacking in the matmul needs few bit operations. Here one thread produces
-// one lane slot (32 codes of one row), so the write of a 64-lane block is one
-// contiguous store of 256*BITS bytes, and the matmul reads the same block
-// back with one coalesced load per lane. The byte layout is specified in
+// one lane slot (32 codes of one row, read as four 8-byte pieces), so the
+// write of a 64-lane block is one contiguous store of 256*BITS bytes, and the
+// matmul reads the same block back with one coalesced load per lane. The byte layout is specified in
 // include/lutq.h.
 #include "lutq_internal.h"
 
@@ -26,12 +26,19 @@ __global__ __launch_bounds__(256) void repack_kernel(const uint8_t* __restrict__
   const int q = L >> 4;
   const uint32_t mask = (1u << BITS) - 1u;
 
+  // the 8 codes of k-step j are adjacent in the row: one 8-byte load each,
+  // so a wave's loads for one j cover 32 contiguous bytes of each of its 16 rows
+  uint64_t v[4] = {0, 0, 0, 0};
+  if (n < N) {
+    const uint8_t* src = codes + n * K + (long long)c * kChunk + 8 * q;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v[j] = *reinterpret_cast<const uint64_t*>(src + 32 * j);
+  }
   uint32_t cd[4][8];
 #pragma unroll
   for (int j = 0; j < 4; ++j)
 #pragma unroll
-    for (int e = 0; e < 8; ++e)
-      cd[j][e] = (n < N) ? (codes[n * K + (long long)c * kChunk + 32 * j + 8 * q + e] & mask) : 0u;
+    for (int e = 0; e < 8; ++e) cd[j][e] = (uint32_t)(v[j] >> (8 * e)) & mask;
 
   uint32_t out[4] = {0, 0, 0, 0};
   if constexpr (BITS == 4) {
@@ -60,9 +67,15 @@ __global__ __launch_bounds__(256) void repack_kernel(const uint8_t* __restrict__
         }
     }
   }
-  uint32_t* o = reinterpret_cast<uint32_t*>(dst + gid * (4 * BITS));
-#pragma unroll
-  for (int w = 0; w < BITS; ++w) o[w] = out[w];
+  uint8_t* o = dst + gid * (4 * BITS);
+  if constexpr (BITS == 4) {
+    *reinterpret_cast<u32x4*>(o) = u32x4{out[0], out[1], out[2], out[3]};
+  } else if constexpr (BITS == 3) {
+    *reinterpret_cast<u32x2*>(o) = u32x2{out[0], out[1]};  // 12-byte slots: 8-byte aligned
+    *reinterpret_cast<uint32_t*>(o + 8) = out[2];
+  } else {
+    *reinterpret_cast<u32x2*>(o) = u32x2{out[0], out[1]};
+  }
   }
 }
 
