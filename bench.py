@@ -145,6 +145,52 @@ def cpu_baseline(case, budget_s=15.0):
     }
 
 
+class FusedCase:
+    """Matrices of one layer that read the same activations (Llama-3-8B q/k/v,
+    or gate and up), cold, called either as one lutq_matmul per matrix or as
+    one fused lutq_matmul_multi."""
+
+    def __init__(self, lutq, torch, wname, mats, M):
+        self.parts = [Case(lutq, torch, wname, m, M) for m in mats]
+        for part in self.parts[1:]:
+            part.x = self.parts[0].x
+        self.fused = False
+        K = self.parts[0].K
+        self.bytes = sum(p.bytes for p in self.parts) - (len(self.parts) - 1) * M * K * 2
+
+    def call(self, lutq, i):
+        if self.fused:
+            lutq.matmul_multi(self.parts[0].x,
+                              [(p.packed[i % len(p.packed)], p.lut, p.scales) for p in self.parts],
+                              outs=[p.y for p in self.parts])
+        else:
+            for p in self.parts:
+                p.call(lutq, i)
+
+
+def fused_section(lutq, torch, args):
+    """One fused launch against one launch per matrix, for q/k/v and gate/up
+    of the Llama-3-8B layer at batch 1 and 16 (cold weights)."""
+    out = {}
+    steps = max(20, args.steps // 4)
+    for label, mats in (("qkv", ("q", "k", "v")), ("gate_up", ("gate", "up"))):
+        for M in (1, 16):
+            fc = FusedCase(lutq, torch, "nf4_layer", mats, M)
+            fc.fused = False
+            sep = time_case(lutq, torch, fc, steps, args.warmup)
+            fc.fused = True
+            fus = time_case(lutq, torch, fc, steps, args.warmup)
+            out[f"{label}_M{M}"] = {
+                "separate_us": round(sep, 3), "fused_us": round(fus, 3),
+                "speedup": round(sep / fus, 3),
+                "fused_GBps": round(fc.bytes / (fus * 1e-6) / 1e9, 1),
+                "plan": lutq.plan(M, sum(-(-p.N // 16) * 16 for p in fc.parts), fc.parts[0].K, 4)}
+            log(f"[bench] fused {label} M={M}: separate {sep:.2f} us, fused {fus:.2f} us")
+            del fc
+            torch.cuda.empty_cache()
+    return out
+
+
 class QuantCase:
     """The quantizer on one workload matrix: fp32 weights (cold copies) ->
     codes + scales under `rule`, with `group` (0 = tensor-wise)."""
@@ -220,6 +266,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-batch32", action="store_true")
     ap.add_argument("--no-quantizer", action="store_true")
+    ap.add_argument("--no-fused", action="store_true")
     ap.add_argument("--no-warm", action="store_true",
                     help="skip the Infinity-Cache-warm repeats (so a kernel trace holds cold calls only)")
     ap.add_argument("--sweep", action="store_true", help="also time every workload (stderr)")
@@ -300,6 +347,8 @@ def main():
 
     if not args.no_quantizer:
         extra["quantizer"] = quantizer_section(lutq, torch, args)
+    if not args.no_fused:
+        extra["fused"] = fused_section(lutq, torch, args)
 
     if args.sweep:
         extra["sweep"] = sweep(lutq, torch, args)

@@ -165,6 +165,33 @@ int lutq_matmul_ex(const uint16_t* x, const lutq_packed_t* packed, const uint16_
  * the one of the first slice, and all slices use it. */
 int lutq_plan(int M, int N, int K, int bits, const lutq_options_t* req, lutq_options_t* out);
 
+/* ---- fused launch of several matrices ---------------------------------------
+ * The products of one layer that read the same activations (the q, k and v
+ * projections, or gate and up; FLUTE abstract: fused kernels for the linear
+ * layers of an LLM) in one launch per batch slice:
+ *     y_i = x . W_i^T,   i < count <= LUTQ_MAX_FUSED.
+ * Narrow matrices (k, v at batch 1) cannot fill the device alone; sharing a
+ * launch also saves the launches themselves. Every matrix has the same K,
+ * bits and group; each has its own packed codes, table, scales and output,
+ * with the layouts, alignment and numerics of lutq_matmul. Workgroups never
+ * span two matrices, so each y_i is bit-identical to what lutq_matmul_ex
+ * gives for that matrix alone with the same path, shape and K split. The
+ * plan (lutq_plan with N = the sum of the widths rounded up to 16) is made
+ * for the whole launch; `opts` as lutq_matmul_ex (NULL = automatic).
+ *   items : host array of `count` entries (read during the call only).
+ * A matrix with N == 0 is skipped. Errors as lutq_matmul_ex, plus
+ * LUTQ_EINVAL for count outside [1, LUTQ_MAX_FUSED] or a NULL items, and
+ * LUTQ_EMISMATCH for a matrix whose K, bits or group differ. */
+#define LUTQ_MAX_FUSED 4
+typedef struct lutq_matmul_item {
+  const lutq_packed_t* packed; /* host descriptor                           */
+  const uint16_t* lut;         /* device, fp16 [2^bits]                      */
+  const uint16_t* scales;      /* device, fp16 [N, K/group] or [1]           */
+  uint16_t* y;                 /* device, fp16 [M, N] (output)               */
+} lutq_matmul_item_t;
+int lutq_matmul_multi(const uint16_t* x, const lutq_matmul_item_t* items, int count, int M, int K,
+                      const lutq_options_t* opts, void* stream);
+
 /* ---- quantizer ------------------------------------------------------------
  * Round-to-nearest onto a lookup table: the step that produces the codes and
  * scales lutq_repack and lutq_matmul consume ("PTQ-damage" abstract:

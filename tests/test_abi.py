@@ -131,6 +131,52 @@ def test_matmul_validates_before_launching(lib):
     assert lib.lutq_unpack(None, P(0x1000), None) == EINVAL
 
 
+def test_matmul_multi_validates_before_launching(lib):
+    P = ctypes.c_void_p
+    descs = [_desc(), _desc(N=32), _desc(N=16)]
+
+    def items(n=3, **over):
+        arr = (_lib.MatmulItem * max(n, 1))()
+        for i in range(n):
+            d = over.get(f"desc{i}", descs[i % 3])
+            arr[i].packed = ctypes.pointer(d) if d is not None else None
+            arr[i].lut = over.get(f"lut{i}", 0x2000 + 0x100 * i)
+            arr[i].scales = over.get(f"sc{i}", 0x3000 + 0x100 * i)
+            arr[i].y = over.get(f"y{i}", 0x4000 + 0x1000 * i)
+        return arr
+
+    def call(arr=None, count=3, M=1, K=256, x=P(0x1000), opts=None):
+        arr = items(count) if arr is None else arr
+        return lib.lutq_matmul_multi(x, arr, count, M, K, opts, None)
+
+    assert lib.lutq_matmul_multi(P(0x1000), None, 1, 1, 256, None, None) == EINVAL
+    assert call(count=0) == EINVAL
+    assert call(count=_lib.MAX_FUSED + 1, arr=items(_lib.MAX_FUSED + 1)) == EINVAL
+    assert call(K=128) == EMISMATCH                          # K differs from the descriptors
+    assert call(arr=items(desc1=_desc(N=32, bits=3))) == EMISMATCH
+    assert call(arr=items(desc2=_desc(N=16, group=0))) == EMISMATCH
+    bad = _desc(); bad.magic = 0
+    assert call(arr=items(desc1=bad)) == EMISMATCH
+    assert call(arr=items(desc0=None)) == EINVAL
+    assert call(M=-1) == EINVAL
+    assert call(x=P(0)) == EINVAL
+    assert call(x=P(0x1008)) == EALIGN
+    assert call(arr=items(y1=0)) == EINVAL
+    assert call(arr=items(y2=0x4001)) == EALIGN
+    assert call(arr=items(lut0=0x2002)) == EALIGN
+    assert call(arr=items(sc1=0x3001)) == EALIGN
+    assert call(arr=items(lut2=0)) == EINVAL
+    o = _lib.Options(); o.path, o.tiles = 1, 4
+    assert call(opts=ctypes.byref(o)) == EINVAL
+    # nothing to do (no HIP call): M == 0, or every matrix empty
+    assert call(M=0) == OK
+    empty = [_desc(N=0), _desc(N=0)]
+    arr = (_lib.MatmulItem * 2)()
+    for i in range(2):
+        arr[i].packed = ctypes.pointer(empty[i])
+    assert lib.lutq_matmul_multi(P(0x1000), arr, 2, 4, 256, None, None) == OK
+
+
 def test_quantizer_validates_before_launching(lib):
     P = ctypes.c_void_p
     err = ctypes.c_double(0)

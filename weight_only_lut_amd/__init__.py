@@ -18,7 +18,9 @@ from ._lib import (  # noqa: F401
     library_path,
     load_library,
     log_base_search,
+    MAX_FUSED,
     matmul,
+    matmul_multi,
     packed_bytes,
     plan,
     quant_error,

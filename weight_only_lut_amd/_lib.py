@@ -21,8 +21,10 @@ LUTQ_LAYOUT_VERSION = 1
 EXPORTS = (
     "lutq_packed_bytes", "lutq_repack", "lutq_unpack", "lutq_matmul", "lutq_matmul_ex",
     "lutq_plan", "lutq_strerror", "lutq_last_hip_error", "lutq_shutdown",
-    "lutq_quantize", "lutq_quant_error", "lutq_log_base_search",
+    "lutq_quantize", "lutq_quant_error", "lutq_log_base_search", "lutq_matmul_multi",
 )
+
+MAX_FUSED = 4
 
 RULE_ABSMAX, RULE_RANGE = 0, 1
 _RULES = {"absmax": RULE_ABSMAX, "range": RULE_RANGE}
@@ -40,6 +42,11 @@ class PackedDesc(ctypes.Structure):
 class Options(ctypes.Structure):
     _fields_ = [("path", ctypes.c_int32), ("ksplit", ctypes.c_int32),
                 ("tiles", ctypes.c_int32), ("reserved", ctypes.c_int32 * 5)]
+
+
+class MatmulItem(ctypes.Structure):
+    _fields_ = [("packed", ctypes.POINTER(PackedDesc)), ("lut", ctypes.c_void_p),
+                ("scales", ctypes.c_void_p), ("y", ctypes.c_void_p)]
 
 
 class LutqError(RuntimeError):
@@ -80,6 +87,9 @@ def load_library():
                                    ctypes.POINTER(Options), vp]
     lib.lutq_matmul_ex.restype = i32
     lib.lutq_plan.argtypes = [i32, i32, i32, i32, ctypes.POINTER(Options), ctypes.POINTER(Options)]
+    lib.lutq_matmul_multi.argtypes = [vp, ctypes.POINTER(MatmulItem), i32, i32, i32,
+                                      ctypes.POINTER(Options), vp]
+    lib.lutq_matmul_multi.restype = i32
     lib.lutq_plan.restype = i32
     lib.lutq_strerror.argtypes = [i32]
     lib.lutq_strerror.restype = ctypes.c_char_p
@@ -207,6 +217,38 @@ def matmul(x, p: Packed, lut, scales, *, path: str = "auto", ksplit: int = 0, ti
     if rc:
         raise LutqError(rc, "lutq_matmul")
     return out
+
+
+def matmul_multi(x, mats, *, path: str = "auto", ksplit: int = 0, tiles: int = 0, outs=None):
+    """lutq_matmul_multi: one fused launch (per batch slice) for several
+    matrices sharing x: ``mats`` is a list of (Packed, lut, scales); returns
+    the list of fp16 outputs y_i [M, N_i]."""
+    import torch
+    _need_cuda(x, "x", torch.float16)
+    M, K = x.shape
+    if not 1 <= len(mats) <= MAX_FUSED:
+        raise ValueError(f"1 to {MAX_FUSED} matrices per fused launch")
+    items = (MatmulItem * len(mats))()
+    ys = []
+    for i, (p, lut, scales) in enumerate(mats):
+        _need_cuda(lut, "lut", torch.float16)
+        _need_cuda(scales, "scales", torch.float16)
+        if outs is None:
+            y = torch.empty((M, p.N), dtype=torch.float16, device=x.device)
+        else:
+            y = outs[i]
+            _need_cuda(y, "out", torch.float16)
+            if tuple(y.shape) != (M, p.N):
+                raise ValueError("out has the wrong shape")
+        ys.append(y)
+        items[i].packed = ctypes.pointer(p.desc)
+        items[i].lut, items[i].scales, items[i].y = lut.data_ptr(), scales.data_ptr(), y.data_ptr()
+    opts = _options(path, ksplit, tiles)
+    rc = _lib().lutq_matmul_multi(_ptr(x), items, len(mats), M, K, ctypes.byref(opts),
+                                  _stream(x.device))
+    if rc:
+        raise LutqError(rc, "lutq_matmul_multi")
+    return ys
 
 
 def quantize(w, lut, bits: int, group: int, rule: str = "absmax"):

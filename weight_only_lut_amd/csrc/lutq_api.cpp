@@ -169,6 +169,96 @@ void plan(int M, int N, int K, int cus, lutq_options_t* o) {
   if (o->ksplit > nchunks) o->ksplit = nchunks > 0 ? nchunks : 1;
 }
 
+// The product for `count` matrices sharing x and K (descriptors already
+// checked, each matching K; bits and group equal across them). One launch
+// per batch slice covers every matrix with N > 0.
+int run_matmul(const uint16_t* x, const lutq_matmul_item_t* items, int count, int M, int K,
+               const lutq_options_t* opts, void* stream) {
+  lutq_options_t o;
+  int rc = read_options(opts, &o);
+  if (rc) return rc;
+  int live[LUTQ_MAX_FUSED];
+  int nlive = 0, ntiles_all = 0;
+  for (int i = 0; i < count; ++i) {
+    const int N = items[i].packed->N;
+    if (N == 0) continue;
+    live[nlive++] = i;
+    ntiles_all += (N + lutq::kTileRows - 1) / lutq::kTileRows;
+  }
+  if (M == 0 || nlive == 0) return LUTQ_OK;
+  for (int j = 0; j < nlive; ++j) {
+    const lutq_matmul_item_t& it = items[live[j]];
+    if (!it.y) return LUTQ_EINVAL;
+    if (!aligned(it.y, 2)) return LUTQ_EALIGN;
+    if (K == 0) continue;
+    if (!it.lut || !it.scales) return LUTQ_EINVAL;
+    if (!aligned(it.lut, 4) || !aligned(it.scales, 2)) return LUTQ_EALIGN;
+  }
+  hipStream_t s = (hipStream_t)stream;
+  if (K == 0) {  // the empty sum; x, the tables and the scales are not read
+    for (int j = 0; j < nlive; ++j) {
+      const lutq_matmul_item_t& it = items[live[j]];
+      hipError_t e = lutq::launch_fill_u16(it.y, (long long)M * it.packed->N, 0, s);
+      if (e != hipSuccess) return hip_fail(e);
+    }
+    return LUTQ_OK;
+  }
+  if (!x) return LUTQ_EINVAL;
+  if (!aligned(x, 16)) return LUTQ_EALIGN;
+
+  plan(M, ntiles_all * lutq::kTileRows, K, cu_count(), &o);
+  const int path = kernel_path(o.path);
+  const int ksplit = o.ksplit;
+  const int rl = rows_per_launch(o.path);
+
+  lutq::MatmulParams p;
+  std::memset(&p, 0, sizeof p);
+  const lutq_packed_t* d0 = items[live[0]].packed;
+  p.K = K;
+  p.group = d0->group;
+  p.nchunks = K / lutq::kChunk;
+  p.ksplit = ksplit;
+  p.cps = (p.nchunks + ksplit - 1) / ksplit;
+  int nrb = 0;
+  for (int j = 0; j < nlive; ++j) {
+    const lutq_matmul_item_t& it = items[live[j]];
+    lutq::MatmulSegment& g = p.seg[j];
+    g.packed = (const uint8_t*)it.packed->data;
+    g.lut = it.lut;
+    g.scales = it.scales;
+    g.y = it.y;
+    g.N = it.packed->N;
+    g.ntiles = (g.N + lutq::kTileRows - 1) / lutq::kTileRows;
+    g.rb_begin = nrb;
+    nrb += (g.ntiles + o.tiles - 1) / o.tiles;
+  }
+  // the first matrix also in the plain fields (the single-matrix launch)
+  p.packed = p.seg[0].packed;
+  p.lut = p.seg[0].lut;
+  p.scales = p.seg[0].scales;
+  p.N = p.seg[0].N;
+  p.ntiles = p.seg[0].ntiles;
+  p.nseg = nlive;
+  p.nrb = nrb;
+  if (ksplit > 1) {
+    if ((size_t)nrb * sizeof(uint32_t) > kCounterBytes) return LUTQ_EUNSUPPORTED;
+    const size_t rows = (size_t)o.tiles * lutq::kTileRows;
+    const size_t pbytes = (size_t)nrb * (size_t)ksplit * rl * rows * sizeof(float);
+    rc = get_scratch(stream, pbytes, &p.partial, &p.counters);
+    if (rc) return rc;
+  }
+  const int bits = d0->bits;
+  for (int m0 = 0; m0 < M; m0 += rl) {
+    p.M = (M - m0) < rl ? (M - m0) : rl;
+    p.x = x + (size_t)m0 * K;
+    for (int j = 0; j < nlive; ++j) p.seg[j].y = items[live[j]].y + (size_t)m0 * p.seg[j].N;
+    p.y = p.seg[0].y;
+    hipError_t e = lutq::launch_matmul(p, bits, path, o.tiles, s);
+    if (e != hipSuccess) return hip_fail(e);
+  }
+  return LUTQ_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -243,55 +333,22 @@ int lutq_matmul_ex(const uint16_t* x, const lutq_packed_t* packed, const uint16_
   if (rc) return rc;
   if (M < 0 || N < 0 || K < 0) return LUTQ_EINVAL;
   if (N != packed->N || K != packed->K) return LUTQ_EMISMATCH;
-  lutq_options_t o;
-  rc = read_options(opts, &o);
-  if (rc) return rc;
-  if (M == 0 || N == 0) return LUTQ_OK;
-  if (!y) return LUTQ_EINVAL;
-  if (!aligned(y, 2)) return LUTQ_EALIGN;
-  hipStream_t s = (hipStream_t)stream;
-  if (K == 0) {  // the empty sum; x, lut and scales are not read
-    hipError_t e = lutq::launch_fill_u16(y, (long long)M * N, 0, s);
-    return e == hipSuccess ? LUTQ_OK : hip_fail(e);
-  }
-  if (!x || !lut || !scales) return LUTQ_EINVAL;
-  if (!aligned(x, 16)) return LUTQ_EALIGN;
-  if (!aligned(lut, 4) || !aligned(scales, 2)) return LUTQ_EALIGN;
+  const lutq_matmul_item_t item = {packed, lut, scales, y};
+  return run_matmul(x, &item, 1, M, K, opts, stream);
+}
 
-  plan(M, N, K, cu_count(), &o);
-  const int path = kernel_path(o.path);
-  const int ksplit = o.ksplit;
-  const int rl = rows_per_launch(o.path);
-
-  lutq::MatmulParams p;
-  std::memset(&p, 0, sizeof p);
-  p.packed = (const uint8_t*)packed->data;
-  p.lut = lut;
-  p.scales = scales;
-  p.N = N;
-  p.K = K;
-  p.group = packed->group;
-  p.nchunks = K / lutq::kChunk;
-  p.ntiles = (N + lutq::kTileRows - 1) / lutq::kTileRows;
-  p.ksplit = ksplit;
-  p.cps = (p.nchunks + ksplit - 1) / ksplit;
-  if (ksplit > 1) {
-    const size_t nrb = (size_t)(p.ntiles + o.tiles - 1) / o.tiles;
-    if (nrb * sizeof(uint32_t) > kCounterBytes) return LUTQ_EUNSUPPORTED;
-    const size_t rows = (size_t)o.tiles * lutq::kTileRows;
-    const size_t pbytes = nrb * (size_t)ksplit * rl * rows * sizeof(float);
-    rc = get_scratch(stream, pbytes, &p.partial, &p.counters);
+int lutq_matmul_multi(const uint16_t* x, const lutq_matmul_item_t* items, int count, int M, int K,
+                      const lutq_options_t* opts, void* stream) {
+  if (!items || count < 1 || count > LUTQ_MAX_FUSED) return LUTQ_EINVAL;
+  if (M < 0 || K < 0) return LUTQ_EINVAL;
+  for (int i = 0; i < count; ++i) {
+    const int rc = check_desc(items[i].packed);
     if (rc) return rc;
+    const lutq_packed_t* d = items[i].packed;
+    const lutq_packed_t* d0 = items[0].packed;
+    if (d->K != K || d->bits != d0->bits || d->group != d0->group) return LUTQ_EMISMATCH;
   }
-  const int bits = packed->bits;
-  for (int m0 = 0; m0 < M; m0 += rl) {
-    p.M = (M - m0) < rl ? (M - m0) : rl;
-    p.x = x + (size_t)m0 * K;
-    p.y = y + (size_t)m0 * N;
-    hipError_t e = lutq::launch_matmul(p, bits, path, o.tiles, s);
-    if (e != hipSuccess) return hip_fail(e);
-  }
-  return LUTQ_OK;
+  return run_matmul(x, items, count, M, K, opts, stream);
 }
 
 int lutq_matmul(const uint16_t* x, const lutq_packed_t* packed, const uint16_t* lut,
@@ -303,6 +360,7 @@ int lutq_matmul(const uint16_t* x, const lutq_packed_t* packed, const uint16_t* 
 
 namespace {
 
+static_assert(LUTQ_MAX_FUSED == lutq::kMaxSegments, "one kernel segment per fused matrix");
 static_assert(LUTQ_RULE_ABSMAX == lutq::kRuleAbsmax && LUTQ_RULE_RANGE == lutq::kRuleRange,
               "rule values");
 

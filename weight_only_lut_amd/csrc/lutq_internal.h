@@ -10,6 +10,17 @@
 
 namespace lutq {
 
+// One matrix of a fused launch: its own codes, table, scales and output;
+// its row blocks are [rb_begin, rb_begin + ceil(ntiles / tiles)) of the grid.
+struct MatmulSegment {
+  const uint8_t* packed;
+  const uint16_t* lut;
+  const uint16_t* scales;
+  uint16_t* y;            // fp16 [M, N] (this launch's slice of rows)
+  int N, ntiles, rb_begin, pad;
+};
+constexpr int kMaxSegments = 4;
+
 struct MatmulParams {
   const uint16_t* x;      // fp16 [M, K] (this launch's slice of rows)
   const uint8_t* packed;  // wave-block layout
@@ -23,6 +34,11 @@ struct MatmulParams {
   int nchunks, ntiles;
   int ksplit;             // workgroups per row block along K
   int cps;                // chunks per split
+  // Fused launch (nseg > 1): matrices sharing x, K, bits and group; the
+  // fields packed .. y, N and ntiles above are then taken from seg[].
+  int nseg;
+  int nrb;                // row blocks of the whole launch (all segments)
+  MatmulSegment seg[kMaxSegments];
 };
 
 enum Path { kPathGemv = 1, kPathMfma = 2 };

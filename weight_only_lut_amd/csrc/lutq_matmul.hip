@@ -39,7 +39,26 @@ namespace lutq {
 // which split the K range; OCC: waves per SIMD the register budget targets.
 template <int BITS, bool MFMA, int MROWS, bool GROUPED, int PF, int TPW, int WAVES, int OCC>
 __global__ __launch_bounds__(WAVES * kWave) __attribute__((amdgpu_waves_per_eu(OCC)))
-void matmul_kernel(const MatmulParams p) {
+void matmul_kernel(const MatmulParams pk) {
+  // A fused launch covers several matrices: this workgroup's row block picks
+  // its matrix (a wave-uniform scan of at most kMaxSegments entries) and
+  // works on it exactly as a launch of that matrix alone would.
+  MatmulParams p = pk;
+  int rb_base = 0;
+  if (pk.nseg > 1) {
+    const int rbg = blockIdx.x / pk.ksplit;
+    int si = 0;
+#pragma unroll
+    for (int i = 1; i < kMaxSegments; ++i)
+      if (i < pk.nseg && rbg >= pk.seg[i].rb_begin) si = i;
+    p.packed = pk.seg[si].packed;
+    p.lut = pk.seg[si].lut;
+    p.scales = pk.seg[si].scales;
+    p.y = pk.seg[si].y;
+    p.N = pk.seg[si].N;
+    p.ntiles = pk.seg[si].ntiles;
+    rb_base = pk.seg[si].rb_begin;
+  }
   constexpr int kThreads = WAVES * kWave;
   constexpr int kWaves = WAVES;
   constexpr int ROWS = TPW * kTileRows;
@@ -71,8 +90,9 @@ void matmul_kernel(const MatmulParams p) {
   // vector loads of the code stream, so the LDS table is ready early.
   const uint32_t lut_lane = lut_to_lanes<BITS>(p.lut, lane);
 
-  const int rb = blockIdx.x / p.ksplit;
+  const int rb = blockIdx.x / p.ksplit;            // row block of the launch (split-K slots)
   const int ks = blockIdx.x - rb * p.ksplit;
+  const int rbm = rb - rb_base;                     // row block within its matrix
   const int c_begin = ks * p.cps;
   const int c_end = min(p.nchunks, c_begin + p.cps);
   const int span = max(0, c_end - c_begin);
@@ -86,7 +106,7 @@ void matmul_kernel(const MatmulParams p) {
   constexpr int U = !GROUPED || PF % SB == 0 ? PF : (SB % PF == 0 ? SB : PF * SB);
   static_assert(U == PF || U == 2 * PF, "the loop tail below covers one slot round");
   const int nsteps = (nmine + PF - 1) / PF * PF;
-  const int tile0 = rb * TPW;
+  const int tile0 = rbm * TPW;
   const int cpg = GROUPED ? p.group / kChunk : 1;       // chunks per group
   const int gpr = GROUPED ? p.K / p.group : 0;          // groups per row
 
@@ -407,7 +427,7 @@ int pick_tiles(int path, int mrows, int ntiles, int cus) {
 
 template <int BITS, bool MFMA, int MROWS, int TPW, int WAVES, int OCC>
 static hipError_t launch_t(const MatmulParams& p, hipStream_t s) {
-  const int nrb = (p.ntiles + TPW - 1) / TPW;
+  const int nrb = p.nseg > 1 ? p.nrb : (p.ntiles + TPW - 1) / TPW;
   const dim3 grid((unsigned)nrb * (unsigned)p.ksplit);
   // Grouped scales at 32 batch rows x 8 tiles need more than the 256
   // registers of two waves per SIMD; this shape runs on few enough
