@@ -12,6 +12,9 @@ rescaling of partial sums, which is the same sum in another order):
     W_hat[n, k] = T[c[n, k]] * s[n, k // group]      (s[0] when group == 0)
     y[m, n]     = sum_k x[m, k] * W_hat[n, k]
 
+and, with per-group zero points z (page 1, LogbQuant abstract: asymmetric
+linear quantization), W_hat[n, k] = s[n, k // group] * (T[c[n, k]] - z[n, k // group]).
+
 Every function cites the passage it follows. Parity status of each function
 is in the docstring; all are pinned by tests/test_oracle.py, and the
 quantizer (``oracle.quantize``: round-to-nearest onto a table, the weight

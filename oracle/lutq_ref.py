@@ -50,13 +50,31 @@ def unpack_codes(packed: np.ndarray, N: int, K: int, bits: int) -> np.ndarray:
 # -- dequantization (page 2, FLUTE abstract: LUT-quantized weights; scale per
 #    group of 128 along K; page 1: one scale per tensor) ----------------------
 
-def dequant(codes: np.ndarray, lut: np.ndarray, scales: np.ndarray, group: int) -> np.ndarray:
+def dequant(codes: np.ndarray, lut: np.ndarray, scales: np.ndarray, group: int,
+            zeros: np.ndarray | None = None) -> np.ndarray:
     """W_hat = fp32(T[c]) * fp32(s[n, k // group]), one RNE fp32 multiply. [N, K] fp32.
 
+    With per-group zero points ``zeros`` (fp16, shaped like the grouped
+    scales; page 1, LogbQuant abstract: asymmetric linear quantization;
+    page 2, BitMoD abstract: per-group quantization parameters):
+    W_hat = s * (T[c] - z[n, k // group]) in fp64, which is exact for fp16
+    operands. [N, K] fp64.
+
     Pinned: the uniform table reproduces INT RTN dequantization bit-exactly;
-    one-hot products decode single weights.
+    one-hot products decode single weights; zero points against exact
+    rationals, a shift invariance and integer asymmetric RTN.
     """
     N, K = codes.shape
+    if zeros is not None:
+        if group == 0:
+            raise ValueError("zero points need grouped scales")
+        if K % group:
+            raise ValueError("K must be a multiple of group")
+        g = K // group
+        t = lut.astype(np.float64)[codes].reshape(N, g, group)
+        z = zeros.astype(np.float64).reshape(N, g, 1)
+        sc = scales.astype(np.float64).reshape(N, g, 1)
+        return (sc * (t - z)).reshape(N, K)
     t = lut.astype(np.float32)[codes]
     if group == 0:
         return t * np.float32(scales.reshape(-1)[0])
@@ -68,14 +86,15 @@ def dequant(codes: np.ndarray, lut: np.ndarray, scales: np.ndarray, group: int) 
 
 # -- the product (fp64 accumulation) ------------------------------------------
 
-def _rows(codes, lut, scales, group, rows):
+def _rows(codes, lut, scales, group, rows, zeros=None):
     if group == 0:
         return dequant(codes[rows], lut, scales, 0)
-    return dequant(codes[rows], lut, scales[rows], group)
+    return dequant(codes[rows], lut, scales[rows], group,
+                   None if zeros is None else zeros[rows])
 
 
 def reference(x: np.ndarray, codes: np.ndarray, lut: np.ndarray, scales: np.ndarray,
-              group: int):
+              group: int, zeros: np.ndarray | None = None):
     """(y_ref, B): y_ref = fp64(x) @ fp64(W_hat).T and B = |x| @ |W_hat|.T, both [M, N] fp64.
 
     Chunked over N to bound memory. Pinned: exact rational brute force on
@@ -89,16 +108,16 @@ def reference(x: np.ndarray, codes: np.ndarray, lut: np.ndarray, scales: np.ndar
     B = np.empty((M, N), np.float64)
     for n0 in range(0, N, ROW_CHUNK):
         n1 = min(N, n0 + ROW_CHUNK)
-        w = _rows(codes, lut, scales, group, slice(n0, n1)).astype(np.float64)
+        w = _rows(codes, lut, scales, group, slice(n0, n1), zeros).astype(np.float64)
         y[:, n0:n1] = x64 @ w.T
         B[:, n0:n1] = ax @ np.abs(w).T
     return y, B
 
 
-def reference_rows(x, codes, lut, scales, group, rows):
+def reference_rows(x, codes, lut, scales, group, rows, zeros=None):
     """``reference`` restricted to output columns ``rows`` (indices into N)."""
     rows = np.asarray(rows)
-    w = _rows(codes, lut, scales, group, rows).astype(np.float64)
+    w = _rows(codes, lut, scales, group, rows, zeros).astype(np.float64)
     x64 = x.astype(np.float64)
     return x64 @ w.T, np.abs(x64) @ np.abs(w).T
 

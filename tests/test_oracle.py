@@ -185,7 +185,7 @@ def test_check_accepts_inside_and_rejects_outside_the_bound():
 def _mutant_dequant(kind):
     original = lutq_ref.dequant
 
-    def f(codes, lut, scales, group):
+    def f(codes, lut, scales, group, zeros=None):
         N, K = codes.shape
         t = lut.astype(np.float32)[codes]
         if kind == "group_by_row":
@@ -214,3 +214,103 @@ def test_planted_transpose_is_caught():
     ex = _exact(x, c, T, s, 0)
     y, _ = oracle.reference(x, c, T, s, 0)
     assert max(abs(y.T[m, n] - float(ex[m][n])) for m in range(2) for n in range(2)) > 1e-6
+
+
+# -- zero points (W_hat = s * (T[c] - z) per group) ---------------------------
+
+def _zp_case(seed, M=3, N=4, K=256, bits=4, table="nf"):
+    c, T, s, x = workloads.small_case(bits, table, 128, M, N, K, seed=seed)
+    z = np.random.default_rng(seed).uniform(-0.6, 0.6, s.shape).astype(np.float16)
+    return c, T, s, z, x
+
+
+def _exact_zp(x, c, T, s, z, group):
+    M, K = x.shape
+    N = c.shape[0]
+    return [[sum(Fraction(float(x[m, k])) * Fraction(float(s[n, k // group]))
+                 * (Fraction(float(T[c[n, k]])) - Fraction(float(z[n, k // group])))
+                 for k in range(K)) for n in range(N)] for m in range(M)]
+
+
+@pytest.mark.parametrize("bits,table,group,K", [(4, "nf", 128, 256), (3, "lloyd_max", 256, 512),
+                                                (2, "int", 128, 384)])
+def test_zero_points_match_exact_rationals(bits, table, group, K):
+    c, T, s, x = workloads.small_case(bits, table, group, 2, 3, K, seed=31 + bits)
+    z = np.random.default_rng(bits).uniform(-0.6, 0.6, s.shape).astype(np.float16)
+    y, B = oracle.reference(x, c, T, s, group, zeros=z)
+    ex = _exact_zp(x, c, T, s, z, group)
+    for m in range(2):
+        for n in range(3):
+            assert abs(y[m, n] - float(ex[m][n])) <= 1e-12 * B[m, n] + 1e-300
+
+
+def test_zero_points_shift_invariance():
+    # T + d and z + d give the same weights (all values exact in fp16)
+    rng = np.random.default_rng(32)
+    T = (np.arange(16) - 8).astype(np.float16)
+    c = rng.integers(0, 16, (5, 256)).astype(np.uint8)
+    s = (2.0 ** rng.integers(-8, -3, (5, 2))).astype(np.float16)
+    z = (rng.integers(-16, 17, (5, 2)) / 4).astype(np.float16)
+    x = rng.normal(0, 1, (3, 256)).astype(np.float16)
+    d = np.float16(2.5)
+    y1, _ = oracle.reference(x, c, T, s, 128, zeros=z)
+    y2, _ = oracle.reference(x, c, (T + d).astype(np.float16), s, 128, zeros=(z + d).astype(np.float16))
+    assert np.array_equal(y1, y2)
+
+
+def test_zero_points_are_integer_asymmetric_rtn():
+    # uniform table T[i] = i with an integer zero point per group is
+    # asymmetric INT dequantization s * (q - z); integer x and power-of-two
+    # scales make the whole product exact
+    rng = np.random.default_rng(33)
+    for bits in (2, 3, 4):
+        L = 1 << bits
+        T = np.arange(L).astype(np.float16)
+        q = rng.integers(0, L, (6, 384)).astype(np.uint8)
+        z = rng.integers(0, L, (6, 3))
+        e = rng.integers(-6, 0, (6, 3))
+        x = rng.integers(-8, 9, (4, 384))
+        y, _ = oracle.reference(x.astype(np.float16), q, T, (2.0 ** e).astype(np.float16), 128,
+                                zeros=z.astype(np.float16))
+        want = np.zeros((4, 6))
+        for g in range(3):
+            blk = slice(128 * g, 128 * (g + 1))
+            iw = q[:, blk].astype(np.int64) - z[:, g:g + 1]          # [6, 128] integers
+            want += (x[:, blk].astype(np.int64) @ iw.T) * (2.0 ** e[:, g])[None, :]
+        assert np.array_equal(y, want)
+
+
+def test_zero_points_zero_is_the_plain_product():
+    c, T, s, z, x = _zp_case(34)
+    y0, _ = oracle.reference(x, c, T, s, 128)
+    yz, _ = oracle.reference(x, c, T, s, 128, zeros=np.zeros_like(s))
+    assert np.allclose(yz, y0, rtol=1e-6, atol=1e-9)
+    with pytest.raises(ValueError):
+        oracle.dequant(c, T, s[:, :1], 0, zeros=s[:, :1])
+
+
+def _mutant_zp(kind):
+    def f(codes, lut, scales, group, zeros=None):
+        N, K = codes.shape
+        g = K // group
+        t = lut.astype(np.float64)[codes].reshape(N, g, group)
+        sc = scales.astype(np.float64).reshape(N, g, 1)
+        z = zeros.astype(np.float64).reshape(N, g, 1)
+        if kind == "sign":
+            return (sc * (t + z)).reshape(N, K)
+        if kind == "by_row":
+            return (sc * (t - zeros.astype(np.float64).T.reshape(-1)[:N * g].reshape(N, g, 1))).reshape(N, K)
+        if kind == "unscaled":
+            return (sc * t - z).reshape(N, K)
+        raise AssertionError(kind)
+    return f
+
+
+@pytest.mark.parametrize("kind", ["sign", "by_row", "unscaled"])
+def test_planted_zero_point_mistakes_are_caught(monkeypatch, kind):
+    c, T, s, z, x = _zp_case(35, M=2, N=3, K=256)
+    ex = _exact_zp(x, c, T, s, z, 128)
+    monkeypatch.setattr(lutq_ref, "dequant", _mutant_zp(kind))
+    y, _ = oracle.reference(x, c, T, s, 128, zeros=z)
+    err = max(abs(y[m, n] - float(ex[m][n])) for m in range(2) for n in range(3))
+    assert err > 1e-6
