@@ -187,10 +187,29 @@ typedef struct lutq_matmul_item {
   const lutq_packed_t* packed; /* host descriptor                           */
   const uint16_t* lut;         /* device, fp16 [2^bits]                      */
   const uint16_t* scales;      /* device, fp16 [N, K/group] or [1]           */
+  const uint16_t* zeros;       /* device, fp16 [N, K/group] zero points as
+                                  lutq_matmul_zp, or NULL (none)             */
   uint16_t* y;                 /* device, fp16 [M, N] (output)               */
 } lutq_matmul_item_t;
 int lutq_matmul_multi(const uint16_t* x, const lutq_matmul_item_t* items, int count, int M, int K,
                       const lutq_options_t* opts, void* stream);
+
+/* ---- per-group zero points ---------------------------------------------------
+ * Asymmetric quantization with a zero point per group (LogbQuant abstract:
+ * asymmetric linear quantization; BitMoD abstract: quantization parameters
+ * and partial-sum rescaling per group):
+ *     W_hat[n, k] = s[n, g] * (T[c[n, k]] - z[n, g]),   g = k / group,
+ *     y = x . W_hat^T.
+ *   zeros : device, fp16 [N, K/group] row-major (the layout of the scales),
+ *           2-byte aligned; group must be > 0 (LUTQ_EGROUP otherwise).
+ * Computed as s * (sum_k x T[c] - z * sum_k x) per group: the activation sums
+ * come once per group for all output rows, so the zero points cost their
+ * own loads (0.125 bit per weight at group 128) and one multiply-add per
+ * group and output. Other arguments, numerics and errors as lutq_matmul_ex;
+ * NULL zeros with N * K > 0 is LUTQ_EINVAL. */
+int lutq_matmul_zp(const uint16_t* x, const lutq_packed_t* packed, const uint16_t* lut,
+                   const uint16_t* scales, const uint16_t* zeros, uint16_t* y, int M, int N, int K,
+                   const lutq_options_t* opts, void* stream);
 
 /* ---- quantizer ------------------------------------------------------------
  * Round-to-nearest onto a lookup table: the step that produces the codes and

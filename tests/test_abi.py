@@ -177,6 +177,36 @@ def test_matmul_multi_validates_before_launching(lib):
     assert lib.lutq_matmul_multi(P(0x1000), arr, 2, 4, 256, None, None) == OK
 
 
+def test_matmul_zp_validates_before_launching(lib):
+    P = ctypes.c_void_p
+    x, lut, sc, z, y = P(0x1000), P(0x2000), P(0x3000), P(0x5000), P(0x4000)
+
+    def call(desc=None, M=1, N=64, K=256, z=z, opts=None):
+        d = _desc(N=N, K=K) if desc is None else desc
+        return lib.lutq_matmul_zp(x, ctypes.byref(d), lut, sc, z, y, M, N, K, opts, None)
+
+    assert call(desc=_desc(group=0)) == EGROUP          # zero points are per group
+    assert call(z=P(0)) == EINVAL
+    assert call(z=P(0x5001)) == EALIGN
+    assert call(N=65, desc=_desc()) == EMISMATCH
+    assert call(M=0) == OK
+    # the fused launch: zeros on a tensor-wise matrix, misaligned zeros
+    arr = (_lib.MatmulItem * 2)()
+    d0, d1 = _desc(), _desc(N=32, group=0)
+    for i, d in enumerate((d0, d1)):
+        arr[i].packed, arr[i].lut, arr[i].scales, arr[i].y = ctypes.pointer(d), 0x2000, 0x3000, 0x4000
+    arr[1].zeros = 0x5000
+    assert lib.lutq_matmul_multi(x, arr, 2, 1, 256, None, None) == EMISMATCH   # groups differ
+    d1b = _desc(N=32)
+    arr[1].packed = ctypes.pointer(d1b)
+    arr[1].zeros = 0x5001
+    assert lib.lutq_matmul_multi(x, arr, 2, 1, 256, None, None) == EALIGN
+    d2, d3 = _desc(group=0), _desc(N=32, group=0)
+    arr[0].packed, arr[1].packed = ctypes.pointer(d2), ctypes.pointer(d3)
+    arr[1].zeros = 0x5000
+    assert lib.lutq_matmul_multi(x, arr, 2, 1, 256, None, None) == EGROUP
+
+
 def test_quantizer_validates_before_launching(lib):
     P = ctypes.c_void_p
     err = ctypes.c_double(0)

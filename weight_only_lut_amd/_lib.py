@@ -22,6 +22,7 @@ EXPORTS = (
     "lutq_packed_bytes", "lutq_repack", "lutq_unpack", "lutq_matmul", "lutq_matmul_ex",
     "lutq_plan", "lutq_strerror", "lutq_last_hip_error", "lutq_shutdown",
     "lutq_quantize", "lutq_quant_error", "lutq_log_base_search", "lutq_matmul_multi",
+    "lutq_matmul_zp",
 )
 
 MAX_FUSED = 4
@@ -46,7 +47,7 @@ class Options(ctypes.Structure):
 
 class MatmulItem(ctypes.Structure):
     _fields_ = [("packed", ctypes.POINTER(PackedDesc)), ("lut", ctypes.c_void_p),
-                ("scales", ctypes.c_void_p), ("y", ctypes.c_void_p)]
+                ("scales", ctypes.c_void_p), ("zeros", ctypes.c_void_p), ("y", ctypes.c_void_p)]
 
 
 class LutqError(RuntimeError):
@@ -90,6 +91,9 @@ def load_library():
     lib.lutq_matmul_multi.argtypes = [vp, ctypes.POINTER(MatmulItem), i32, i32, i32,
                                       ctypes.POINTER(Options), vp]
     lib.lutq_matmul_multi.restype = i32
+    lib.lutq_matmul_zp.argtypes = [vp, ctypes.POINTER(PackedDesc), vp, vp, vp, vp, i32, i32, i32,
+                                   ctypes.POINTER(Options), vp]
+    lib.lutq_matmul_zp.restype = i32
     lib.lutq_plan.restype = i32
     lib.lutq_strerror.argtypes = [i32]
     lib.lutq_strerror.restype = ctypes.c_char_p
@@ -197,9 +201,10 @@ def unpack(p: Packed):
     return out
 
 
-def matmul(x, p: Packed, lut, scales, *, path: str = "auto", ksplit: int = 0, tiles: int = 0,
-           out=None):
-    """lutq_matmul_ex: y[M, N] = x[M, K] . dequant(p, lut, scales)^T, fp16 out."""
+def matmul(x, p: Packed, lut, scales, *, zeros=None, path: str = "auto", ksplit: int = 0,
+           tiles: int = 0, out=None):
+    """lutq_matmul_ex (lutq_matmul_zp with ``zeros``): y[M, N] = x[M, K] .
+    dequant(p, lut, scales[, zeros])^T, fp16 out."""
     import torch
     _need_cuda(x, "x", torch.float16)
     _need_cuda(lut, "lut", torch.float16)
@@ -212,8 +217,14 @@ def matmul(x, p: Packed, lut, scales, *, path: str = "auto", ksplit: int = 0, ti
         if tuple(out.shape) != (M, p.N):
             raise ValueError("out has the wrong shape")
     opts = _options(path, ksplit, tiles)
-    rc = _lib().lutq_matmul_ex(_ptr(x), ctypes.byref(p.desc), _ptr(lut), _ptr(scales), _ptr(out),
-                               M, p.N, K, ctypes.byref(opts), _stream(x.device))
+    if zeros is None:
+        rc = _lib().lutq_matmul_ex(_ptr(x), ctypes.byref(p.desc), _ptr(lut), _ptr(scales),
+                                   _ptr(out), M, p.N, K, ctypes.byref(opts), _stream(x.device))
+    else:
+        _need_cuda(zeros, "zeros", torch.float16)
+        rc = _lib().lutq_matmul_zp(_ptr(x), ctypes.byref(p.desc), _ptr(lut), _ptr(scales),
+                                   _ptr(zeros), _ptr(out), M, p.N, K, ctypes.byref(opts),
+                                   _stream(x.device))
     if rc:
         raise LutqError(rc, "lutq_matmul")
     return out
@@ -221,8 +232,8 @@ def matmul(x, p: Packed, lut, scales, *, path: str = "auto", ksplit: int = 0, ti
 
 def matmul_multi(x, mats, *, path: str = "auto", ksplit: int = 0, tiles: int = 0, outs=None):
     """lutq_matmul_multi: one fused launch (per batch slice) for several
-    matrices sharing x: ``mats`` is a list of (Packed, lut, scales); returns
-    the list of fp16 outputs y_i [M, N_i]."""
+    matrices sharing x: ``mats`` is a list of (Packed, lut, scales) or
+    (Packed, lut, scales, zeros); returns the list of fp16 outputs y_i [M, N_i]."""
     import torch
     _need_cuda(x, "x", torch.float16)
     M, K = x.shape
@@ -230,9 +241,14 @@ def matmul_multi(x, mats, *, path: str = "auto", ksplit: int = 0, tiles: int = 0
         raise ValueError(f"1 to {MAX_FUSED} matrices per fused launch")
     items = (MatmulItem * len(mats))()
     ys = []
-    for i, (p, lut, scales) in enumerate(mats):
+    for i, mat in enumerate(mats):
+        p, lut, scales = mat[:3]
+        zeros = mat[3] if len(mat) > 3 else None
         _need_cuda(lut, "lut", torch.float16)
         _need_cuda(scales, "scales", torch.float16)
+        if zeros is not None:
+            _need_cuda(zeros, "zeros", torch.float16)
+            items[i].zeros = zeros.data_ptr()
         if outs is None:
             y = torch.empty((M, p.N), dtype=torch.float16, device=x.device)
         else:

@@ -186,10 +186,16 @@ int run_matmul(const uint16_t* x, const lutq_matmul_item_t* items, int count, in
     ntiles_all += (N + lutq::kTileRows - 1) / lutq::kTileRows;
   }
   if (M == 0 || nlive == 0) return LUTQ_OK;
+  bool zp = false;
   for (int j = 0; j < nlive; ++j) {
     const lutq_matmul_item_t& it = items[live[j]];
     if (!it.y) return LUTQ_EINVAL;
     if (!aligned(it.y, 2)) return LUTQ_EALIGN;
+    if (it.zeros) {
+      if (it.packed->group == 0) return LUTQ_EGROUP;  // zero points are per group
+      if (!aligned(it.zeros, 2)) return LUTQ_EALIGN;
+      zp = true;
+    }
     if (K == 0) continue;
     if (!it.lut || !it.scales) return LUTQ_EINVAL;
     if (!aligned(it.lut, 4) || !aligned(it.scales, 2)) return LUTQ_EALIGN;
@@ -226,6 +232,7 @@ int run_matmul(const uint16_t* x, const lutq_matmul_item_t* items, int count, in
     g.packed = (const uint8_t*)it.packed->data;
     g.lut = it.lut;
     g.scales = it.scales;
+    g.zeros = it.zeros;
     g.y = it.y;
     g.N = it.packed->N;
     g.ntiles = (g.N + lutq::kTileRows - 1) / lutq::kTileRows;
@@ -236,6 +243,8 @@ int run_matmul(const uint16_t* x, const lutq_matmul_item_t* items, int count, in
   p.packed = p.seg[0].packed;
   p.lut = p.seg[0].lut;
   p.scales = p.seg[0].scales;
+  p.zeros = p.seg[0].zeros;
+  p.zp = zp;
   p.N = p.seg[0].N;
   p.ntiles = p.seg[0].ntiles;
   p.nseg = nlive;
@@ -333,7 +342,20 @@ int lutq_matmul_ex(const uint16_t* x, const lutq_packed_t* packed, const uint16_
   if (rc) return rc;
   if (M < 0 || N < 0 || K < 0) return LUTQ_EINVAL;
   if (N != packed->N || K != packed->K) return LUTQ_EMISMATCH;
-  const lutq_matmul_item_t item = {packed, lut, scales, y};
+  const lutq_matmul_item_t item = {packed, lut, scales, nullptr, y};
+  return run_matmul(x, &item, 1, M, K, opts, stream);
+}
+
+int lutq_matmul_zp(const uint16_t* x, const lutq_packed_t* packed, const uint16_t* lut,
+                   const uint16_t* scales, const uint16_t* zeros, uint16_t* y, int M, int N, int K,
+                   const lutq_options_t* opts, void* stream) {
+  int rc = check_desc(packed);
+  if (rc) return rc;
+  if (M < 0 || N < 0 || K < 0) return LUTQ_EINVAL;
+  if (N != packed->N || K != packed->K) return LUTQ_EMISMATCH;
+  if (packed->group == 0) return LUTQ_EGROUP;
+  if (!zeros && (size_t)N * K > 0) return LUTQ_EINVAL;
+  const lutq_matmul_item_t item = {packed, lut, scales, zeros, y};
   return run_matmul(x, &item, 1, M, K, opts, stream);
 }
 

@@ -228,6 +228,29 @@ __device__ __forceinline__ uint16_t f32_to_f16_bits(float f) {
   return __builtin_bit_cast(uint16_t, (f16)f);  // round to nearest even
 }
 
+// Sum of the two fp16 values of a packed pair, in fp32 (one dot with 1, 1).
+__device__ __forceinline__ float pair_sum(uint32_t pr) {
+  const f16x2 one = {(f16)1.0f, (f16)1.0f};
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pr), one, 0.f, false);
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over the 16 lanes of a row as a butterfly (partners under xor 1, 2,
+// then the mirrored half and quarter rows): every addition is a + b in one
+// lane and b + a in its partner, so all 16 lanes end with the same bits.
+__device__ __forceinline__ float row_sum16(float v) {
+  v += dpp_f32<0xB1>(v);   // quad_perm [1,0,3,2]
+  v += dpp_f32<0x4E>(v);   // quad_perm [2,3,0,1]
+  v += dpp_f32<0x141>(v);  // row_half_mirror: quads 0 <-> 1 of each half row
+  v += dpp_f32<0x140>(v);  // row_mirror: halves of the row
+  return v;
+}
+
 __device__ __forceinline__ float f16_bits_to_f32(uint16_t h) {
   return (float)__builtin_bit_cast(f16, h);
 }

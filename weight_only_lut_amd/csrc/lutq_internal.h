@@ -16,6 +16,7 @@ struct MatmulSegment {
   const uint8_t* packed;
   const uint16_t* lut;
   const uint16_t* scales;
+  const uint16_t* zeros;  // per-group zero points like the scales, or null (z = 0)
   uint16_t* y;            // fp16 [M, N] (this launch's slice of rows)
   int N, ntiles, rb_begin, pad;
 };
@@ -26,6 +27,7 @@ struct MatmulParams {
   const uint8_t* packed;  // wave-block layout
   const uint16_t* lut;    // fp16 [2^bits]
   const uint16_t* scales; // fp16 [N, K/group] or [1]
+  const uint16_t* zeros;  // fp16 [N, K/group] zero points, or null (grouped only)
   uint16_t* y;            // fp16 [M, N] (this launch's slice of rows)
   float* partial;         // split-K partial sums, or null when ksplit == 1
   uint32_t* counters;     // split-K arrival counters (zero between launches)
@@ -34,6 +36,7 @@ struct MatmulParams {
   int nchunks, ntiles;
   int ksplit;             // workgroups per row block along K
   int cps;                // chunks per split
+  bool zp;                // zero points in this launch (any matrix); grouped only
   // Fused launch (nseg > 1): matrices sharing x, K, bits and group; the
   // fields packed .. y, N and ntiles above are then taken from seg[].
   int nseg;

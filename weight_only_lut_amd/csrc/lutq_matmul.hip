@@ -37,7 +37,7 @@ namespace lutq {
 // pipeline (PF - 1 chunks in flight while one is computed);
 // TPW: 16-row tiles per wave (and per workgroup); WAVES: waves per workgroup,
 // which split the K range; OCC: waves per SIMD the register budget targets.
-template <int BITS, bool MFMA, int MROWS, bool GROUPED, int PF, int TPW, int WAVES, int OCC>
+template <int BITS, bool MFMA, int MROWS, bool GROUPED, bool ZP, int PF, int TPW, int WAVES, int OCC>
 __global__ __launch_bounds__(WAVES * kWave) __attribute__((amdgpu_waves_per_eu(OCC)))
 void matmul_kernel(const MatmulParams pk) {
   // A fused launch covers several matrices: this workgroup's row block picks
@@ -54,6 +54,7 @@ void matmul_kernel(const MatmulParams pk) {
     p.packed = pk.seg[si].packed;
     p.lut = pk.seg[si].lut;
     p.scales = pk.seg[si].scales;
+    p.zeros = pk.seg[si].zeros;
     p.y = pk.seg[si].y;
     p.N = pk.seg[si].N;
     p.ntiles = pk.seg[si].ntiles;
@@ -137,6 +138,12 @@ void matmul_kernel(const MatmulParams pk) {
   uint32_t soff[TPW];
 #pragma unroll
   for (int t = 0; t < TPW; ++t) soff[t] = 2u * (uint32_t)(t * kTileRows + r) * (uint32_t)gpr;
+  // Zero points (same layout and batching as the scales). A matrix without
+  // them gets an empty resource: every load reads z = 0, and s * (acc - 0)
+  // is the plain rescale.
+  const __amdgpu_buffer_rsrc_t zrsrc = make_rsrc(
+      ZP ? p.zeros + (size_t)row0 * gpr : nullptr,
+      ZP && p.zeros ? rows_here * (uint32_t)gpr * 2u : 0u);
 
   // activations of this launch's M rows
   const __amdgpu_buffer_rsrc_t xrsrc =
@@ -158,6 +165,7 @@ void matmul_kernel(const MatmulParams pk) {
 
   SlotRegs<BITS> cbuf[PF][TPW];
   uint32_t scur[TPW], snext[TPW];  // scale batches: in use, in flight
+  uint32_t zcur[ZP ? TPW : 1], znext[ZP ? TPW : 1];  // zero-point batches
   uint32_t xbuf[PF][MFMA ? 1 : MROWS];
   u32x4 abuf[PF][MT][MFMA ? 4 : 1];
 
@@ -196,10 +204,19 @@ void matmul_kernel(const MatmulParams pk) {
 #pragma unroll
     for (int t = 0; t < TPW; ++t)
       snext[t] = __builtin_amdgcn_raw_buffer_load_b16(srsrc, soff[t] + sb, 0, 0);
+    if constexpr (ZP) {
+#pragma unroll
+      for (int t = 0; t < TPW; ++t)
+        znext[t] = __builtin_amdgcn_raw_buffer_load_b16(zrsrc, soff[t] + sb, 0, 0);
+    }
   };
   // the scale of this lane's row at step position u (0 .. SB-1) of the batch
   auto step_scale = [&](int t, int u) __attribute__((always_inline)) {
     const int v = __builtin_amdgcn_ds_bpermute((16 * u + r) * 4, (int)scur[t]);
+    return f16_bits_to_f32((uint16_t)v);
+  };
+  auto step_zero = [&](int t, int u) __attribute__((always_inline)) {
+    const int v = __builtin_amdgcn_ds_bpermute((16 * u + r) * 4, (int)zcur[ZP ? t : 0]);
     return f16_bits_to_f32((uint16_t)v);
   };
 
@@ -240,12 +257,28 @@ void matmul_kernel(const MatmulParams pk) {
             cs[t][m] = dot2_bcast4(cs[t][m], xbuf[s][m], pr[0], pr[1], pr[2], pr[3], j);
         }
       }
+      // Zero points: lane row q multiplied the activations of the 16 lanes of
+      // its row (k = 32j + 8q + e), so its share of the group's activation
+      // sum is the sum over that row (a butterfly: every lane gets the same
+      // value), computed once for all tiles.
+      float xq[ZP ? MROWS : 1];
+      if constexpr (ZP) {
+#pragma unroll
+        for (int m = 0; m < MROWS; ++m) xq[m] = row_sum16(pair_sum(xbuf[s][m]));
+      }
 #pragma unroll
       for (int t = 0; t < TPW; ++t) {
         if constexpr (GROUPED) {
           const float sc = step_scale(t, u);
+          if constexpr (ZP) {
+            const float z = step_zero(t, u);
 #pragma unroll
-          for (int m = 0; m < MROWS; ++m) gacc[t][m] = __builtin_fmaf(sc, cs[t][m], gacc[t][m]);
+            for (int m = 0; m < MROWS; ++m)
+              gacc[t][m] = __builtin_fmaf(sc, __builtin_fmaf(-z, xq[m], cs[t][m]), gacc[t][m]);
+          } else {
+#pragma unroll
+            for (int m = 0; m < MROWS; ++m) gacc[t][m] = __builtin_fmaf(sc, cs[t][m], gacc[t][m]);
+          }
         } else {
 #pragma unroll
           for (int m = 0; m < MROWS; ++m) gacc[t][m] += cs[t][m];
@@ -267,6 +300,21 @@ void matmul_kernel(const MatmulParams pk) {
         }
       };
       lookup(0, bq[0]);
+      // Zero points: the group's activation sums, in the accumulator layout
+      // (a B operand of ones gives C[m][n] = sum_k x[m][k] in every column),
+      // once for all tiles.
+      f32x4 xs[ZP ? MT : 1];
+      if constexpr (ZP) {
+        const f16x8 ones = {1, 1, 1, 1, 1, 1, 1, 1};
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          xs[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            xs[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                __builtin_bit_cast(f16x8, abuf[s][mt][j]), ones, xs[mt], 0, 0, 0);
+        }
+      }
 #pragma unroll
       for (int t = 0; t < TPW; ++t) {
         if (t + 1 < TPW) lookup(t + 1, bq[(t + 1) & 1]);
@@ -290,10 +338,20 @@ void matmul_kernel(const MatmulParams pk) {
         }
         if constexpr (GROUPED) {
           const float sc = step_scale(t, u);
+          if constexpr (ZP) {
+            const float z = step_zero(t, u);
 #pragma unroll
-          for (int mt = 0; mt < MT; ++mt)
+            for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) macc[t][mt][e] = __builtin_fmaf(sc, cg[mt][e], macc[t][mt][e]);
+              for (int e = 0; e < 4; ++e)
+                macc[t][mt][e] = __builtin_fmaf(sc, __builtin_fmaf(-z, xs[mt][e], cg[mt][e]),
+                                                macc[t][mt][e]);
+          } else {
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+              for (int e = 0; e < 4; ++e) macc[t][mt][e] = __builtin_fmaf(sc, cg[mt][e], macc[t][mt][e]);
+          }
         }
       }
     }
@@ -323,6 +381,10 @@ void matmul_kernel(const MatmulParams pk) {
     if constexpr (GROUPED && u % SB == 0) {
 #pragma unroll
       for (int t = 0; t < TPW; ++t) scur[t] = snext[t];
+      if constexpr (ZP) {
+#pragma unroll
+        for (int t = 0; t < TPW; ++t) zcur[t] = znext[t];
+      }
       issue_scales(i + SB);
     }
     issue(std::integral_constant<int, (u + PF - 1) % PF>{}, chunk(i + PF - 1));
@@ -433,10 +495,12 @@ static hipError_t launch_t(const MatmulParams& p, hipStream_t s) {
   // registers of two waves per SIMD; this shape runs on few enough
   // workgroups that one wave per SIMD costs little.
   constexpr int OCC_G = (MFMA && MROWS == 32 && TPW == 8) ? 1 : OCC;
-  if (p.group != 0)
-    matmul_kernel<BITS, MFMA, MROWS, true, kPf, TPW, WAVES, OCC_G><<<grid, WAVES * kWave, 0, s>>>(p);
+  if (p.group != 0 && p.zp)
+    matmul_kernel<BITS, MFMA, MROWS, true, true, kPf, TPW, WAVES, OCC_G><<<grid, WAVES * kWave, 0, s>>>(p);
+  else if (p.group != 0)
+    matmul_kernel<BITS, MFMA, MROWS, true, false, kPf, TPW, WAVES, OCC_G><<<grid, WAVES * kWave, 0, s>>>(p);
   else
-    matmul_kernel<BITS, MFMA, MROWS, false, kPf, TPW, WAVES, OCC><<<grid, WAVES * kWave, 0, s>>>(p);
+    matmul_kernel<BITS, MFMA, MROWS, false, false, kPf, TPW, WAVES, OCC><<<grid, WAVES * kWave, 0, s>>>(p);
   return hipGetLastError();
 }
 
