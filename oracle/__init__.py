@@ -13,7 +13,9 @@ rescaling of partial sums, which is the same sum in another order):
     y[m, n]     = sum_k x[m, k] * W_hat[n, k]
 
 and, with per-group zero points z (page 1, LogbQuant abstract: asymmetric
-linear quantization), W_hat[n, k] = s[n, k // group] * (T[c[n, k]] - z[n, k // group]).
+linear quantization), W_hat[n, k] = s[n, k // group] * (T[c[n, k]] - z[n, k // group]);
+with per-group data types (page 2, BitMoD abstract), T is the table the
+group's type id selects.
 
 Every function cites the passage it follows. Parity status of each function
 is in the docstring; all are pinned by tests/test_oracle.py, and the

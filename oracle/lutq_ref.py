@@ -51,7 +51,7 @@ def unpack_codes(packed: np.ndarray, N: int, K: int, bits: int) -> np.ndarray:
 #    group of 128 along K; page 1: one scale per tensor) ----------------------
 
 def dequant(codes: np.ndarray, lut: np.ndarray, scales: np.ndarray, group: int,
-            zeros: np.ndarray | None = None) -> np.ndarray:
+            zeros: np.ndarray | None = None, types: np.ndarray | None = None) -> np.ndarray:
     """W_hat = fp32(T[c]) * fp32(s[n, k // group]), one RNE fp32 multiply. [N, K] fp32.
 
     With per-group zero points ``zeros`` (fp16, shaped like the grouped
@@ -60,11 +60,30 @@ def dequant(codes: np.ndarray, lut: np.ndarray, scales: np.ndarray, group: int,
     W_hat = s * (T[c] - z[n, k // group]) in fp64, which is exact for fp16
     operands. [N, K] fp64.
 
+    With per-group data types ``types`` (uint8, shaped like the grouped
+    scales; page 2, BitMoD abstract: a data type chosen per group), ``lut``
+    holds one table per type, [n_types, 2^b], and group g of row n reads
+    table types[n, g]: W_hat = s * (T[types[n, g]][c] - z) (z = 0 without
+    zero points), in fp64. [N, K] fp64.
+
     Pinned: the uniform table reproduces INT RTN dequantization bit-exactly;
     one-hot products decode single weights; zero points against exact
-    rationals, a shift invariance and integer asymmetric RTN.
+    rationals, a shift invariance and integer asymmetric RTN; data types
+    against exact rationals and a relabelling invariance.
     """
     N, K = codes.shape
+    if types is not None:
+        if group == 0:
+            raise ValueError("data types need grouped scales")
+        if K % group:
+            raise ValueError("K must be a multiple of group")
+        g = K // group
+        tables = np.asarray(lut).astype(np.float64).reshape(-1, np.asarray(lut).shape[-1])
+        ty = np.repeat(np.asarray(types).astype(np.int64).reshape(N, g), group, axis=1)
+        t = tables[ty, codes].reshape(N, g, group)
+        z = 0.0 if zeros is None else zeros.astype(np.float64).reshape(N, g, 1)
+        sc = scales.astype(np.float64).reshape(N, g, 1)
+        return (sc * (t - z)).reshape(N, K)
     if zeros is not None:
         if group == 0:
             raise ValueError("zero points need grouped scales")
@@ -86,15 +105,16 @@ def dequant(codes: np.ndarray, lut: np.ndarray, scales: np.ndarray, group: int,
 
 # -- the product (fp64 accumulation) ------------------------------------------
 
-def _rows(codes, lut, scales, group, rows, zeros=None):
+def _rows(codes, lut, scales, group, rows, zeros=None, types=None):
     if group == 0:
         return dequant(codes[rows], lut, scales, 0)
     return dequant(codes[rows], lut, scales[rows], group,
-                   None if zeros is None else zeros[rows])
+                   None if zeros is None else zeros[rows],
+                   None if types is None else types[rows])
 
 
 def reference(x: np.ndarray, codes: np.ndarray, lut: np.ndarray, scales: np.ndarray,
-              group: int, zeros: np.ndarray | None = None):
+              group: int, zeros: np.ndarray | None = None, types: np.ndarray | None = None):
     """(y_ref, B): y_ref = fp64(x) @ fp64(W_hat).T and B = |x| @ |W_hat|.T, both [M, N] fp64.
 
     Chunked over N to bound memory. Pinned: exact rational brute force on
@@ -108,16 +128,16 @@ def reference(x: np.ndarray, codes: np.ndarray, lut: np.ndarray, scales: np.ndar
     B = np.empty((M, N), np.float64)
     for n0 in range(0, N, ROW_CHUNK):
         n1 = min(N, n0 + ROW_CHUNK)
-        w = _rows(codes, lut, scales, group, slice(n0, n1), zeros).astype(np.float64)
+        w = _rows(codes, lut, scales, group, slice(n0, n1), zeros, types).astype(np.float64)
         y[:, n0:n1] = x64 @ w.T
         B[:, n0:n1] = ax @ np.abs(w).T
     return y, B
 
 
-def reference_rows(x, codes, lut, scales, group, rows, zeros=None):
+def reference_rows(x, codes, lut, scales, group, rows, zeros=None, types=None):
     """``reference`` restricted to output columns ``rows`` (indices into N)."""
     rows = np.asarray(rows)
-    w = _rows(codes, lut, scales, group, rows, zeros).astype(np.float64)
+    w = _rows(codes, lut, scales, group, rows, zeros, types).astype(np.float64)
     x64 = x.astype(np.float64)
     return x64 @ w.T, np.abs(x64) @ np.abs(w).T
 

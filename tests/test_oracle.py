@@ -185,7 +185,7 @@ def test_check_accepts_inside_and_rejects_outside_the_bound():
 def _mutant_dequant(kind):
     original = lutq_ref.dequant
 
-    def f(codes, lut, scales, group, zeros=None):
+    def f(codes, lut, scales, group, zeros=None, types=None):
         N, K = codes.shape
         t = lut.astype(np.float32)[codes]
         if kind == "group_by_row":
@@ -290,7 +290,7 @@ def test_zero_points_zero_is_the_plain_product():
 
 
 def _mutant_zp(kind):
-    def f(codes, lut, scales, group, zeros=None):
+    def f(codes, lut, scales, group, zeros=None, types=None):
         N, K = codes.shape
         g = K // group
         t = lut.astype(np.float64)[codes].reshape(N, g, group)
@@ -314,3 +314,69 @@ def test_planted_zero_point_mistakes_are_caught(monkeypatch, kind):
     y, _ = oracle.reference(x, c, T, s, 128, zeros=z)
     err = max(abs(y[m, n] - float(ex[m][n])) for m in range(2) for n in range(3))
     assert err > 1e-6
+
+
+# -- per-group data types (a table per type id) --------------------------------
+
+def _typed_case(seed, M=2, N=3, K=256, bits=3, ntypes=3, with_zeros=False):
+    rng = np.random.default_rng(seed)
+    L = 1 << bits
+    luts = np.stack([tables.make(k, bits) for k in ("nf", "int", "lloyd_max", "nf")[:ntypes]])
+    luts[-1] = (luts[-1].astype(np.float32) * 0.5).astype(np.float16)   # distinct tables
+    c = rng.integers(0, L, (N, K)).astype(np.uint8)
+    types = rng.integers(0, ntypes, (N, K // 128)).astype(np.uint8)
+    s = rng.uniform(0.01, 0.05, (N, K // 128)).astype(np.float16)
+    z = rng.uniform(-0.5, 0.5, s.shape).astype(np.float16) if with_zeros else None
+    x = rng.normal(0, 1, (M, K)).astype(np.float16)
+    return c, luts, types, s, z, x
+
+
+def _exact_typed(x, c, luts, types, s, z, group):
+    M, K = x.shape
+    N = c.shape[0]
+    zf = (lambda n, g: Fraction(float(z[n, g]))) if z is not None else (lambda n, g: Fraction(0))
+    return [[sum(Fraction(float(x[m, k])) * Fraction(float(s[n, k // group]))
+                 * (Fraction(float(luts[types[n, k // group], c[n, k]])) - zf(n, k // group))
+                 for k in range(K)) for n in range(N)] for m in range(M)]
+
+
+@pytest.mark.parametrize("with_zeros", [False, True])
+def test_data_types_match_exact_rationals(with_zeros):
+    c, luts, types, s, z, x = _typed_case(41, with_zeros=with_zeros)
+    y, B = oracle.reference(x, c, luts, s, 128, zeros=z, types=types)
+    ex = _exact_typed(x, c, luts, types, s, z, 128)
+    for m in range(2):
+        for n in range(3):
+            assert abs(y[m, n] - float(ex[m][n])) <= 1e-12 * B[m, n] + 1e-300
+
+
+def test_data_types_relabelling_invariance():
+    # the same tables under other ids, the ids mapped along: same weights
+    c, luts, types, s, z, x = _typed_case(42, N=6, K=512, ntypes=4)
+    perm = np.array([2, 0, 3, 1])
+    inv = np.argsort(perm)
+    y1, _ = oracle.reference(x, c, luts, s, 128, types=types)
+    y2, _ = oracle.reference(x, c, luts[perm], s, 128, types=inv[types].astype(np.uint8))
+    assert np.array_equal(y1, y2)
+
+
+def test_data_types_single_type_is_the_plain_product():
+    c, luts, types, s, z, x = _typed_case(43, N=5, K=384)
+    y_typed, _ = oracle.reference(x, c, luts[1:2], s, 128, types=np.zeros_like(types))
+    y_plain, _ = oracle.reference(x, c, luts[1], s, 128)
+    assert np.allclose(y_typed, y_plain, rtol=1e-6, atol=1e-9)
+
+
+def test_planted_type_index_by_row_is_caught(monkeypatch):
+    c, luts, types, s, z, x = _typed_case(44)
+    ex = _exact_typed(x, c, luts, types, s, z, 128)
+
+    def by_row(codes, lut, scales, group, zeros=None, types=None):
+        N, K = codes.shape
+        ty = np.repeat(types.T.reshape(-1)[:N * (K // group)].reshape(N, K // group), group, 1)
+        t = lut.astype(np.float64)[ty, codes]
+        return np.repeat(scales.astype(np.float64), group, 1) * t
+
+    monkeypatch.setattr(lutq_ref, "dequant", by_row)
+    y, _ = oracle.reference(x, c, luts, s, 128, types=types)
+    assert max(abs(y[m, n] - float(ex[m][n])) for m in range(2) for n in range(3)) > 1e-6

@@ -14,7 +14,10 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
-SOURCES = ["lutq_api.cpp", "lutq_layout.hip", "lutq_matmul.hip", "lutq_quantize.hip"]
+# (source, extra flags): the matmul is compiled once per code width
+SOURCES = [("lutq_api.cpp", []), ("lutq_layout.hip", []), ("lutq_quantize.hip", []),
+           ("lutq_matmul.hip", ["-DLUTQ_MATMUL_BITS=2"]), ("lutq_matmul.hip", ["-DLUTQ_MATMUL_BITS=3"]),
+           ("lutq_matmul.hip", ["-DLUTQ_MATMUL_BITS=4"])]
 LIB = os.path.join(HERE, "liblutq.so")
 ARCH = "gfx950"
 
@@ -37,21 +40,43 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build liblutq.so)")
 
 
-def build(verbose: bool = False) -> str:
-    tmp = LIB + f".tmp{os.getpid()}"
-    cmd = [hipcc(), *FLAGS, "-I", os.path.join(ROOT, "include"), "-o", tmp,
-           *[os.path.join(CSRC, s) for s in SOURCES]]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     noise = "packed-fp32-ops"  # host pass does not know the device-only feature
     msgs = [ln for ln in (res.stdout + res.stderr).splitlines() if noise not in ln]
-    if res.returncode != 0:
-        if os.path.exists(tmp):
-            os.remove(tmp)
-        raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
-    if verbose and msgs:
-        print("\n".join(msgs))
+    return res.returncode, msgs
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source to an object (in parallel), then link liblutq.so."""
+    import tempfile
+    from concurrent.futures import ThreadPoolExecutor
+    cc = hipcc()
+    inc = ["-I", os.path.join(ROOT, "include")]
+    with tempfile.TemporaryDirectory(prefix="lutq_build_") as tmpdir:
+        jobs = []
+        for i, (src, extra) in enumerate(SOURCES):
+            obj = os.path.join(tmpdir, f"{i}_{os.path.splitext(src)[0]}.o")
+            cflags = [f for f in FLAGS if f != "-shared"]
+            jobs.append((obj, [cc, *cflags, *extra, *inc, "-c", "-o", obj, os.path.join(CSRC, src)]))
+        workers = max(1, min(len(jobs), os.cpu_count() or 1, 8))
+        with ThreadPoolExecutor(max_workers=workers) as ex:
+            results = list(ex.map(lambda j: _run(j[1], verbose), jobs))
+        errors = [m for rc, m in results if rc != 0]
+        if errors:
+            raise RuntimeError("hipcc failed:\n" + "\n".join(ln for m in errors for ln in m))
+        if verbose:
+            for rc, m in results:
+                if m:
+                    print("\n".join(m))
+        tmp = LIB + f".tmp{os.getpid()}"
+        rc, msgs = _run([cc, *FLAGS, "-o", tmp, *[o for o, _ in jobs]], verbose)
+        if rc != 0:
+            if os.path.exists(tmp):
+                os.remove(tmp)
+            raise RuntimeError("hipcc link failed:\n" + "\n".join(msgs))
     os.replace(tmp, LIB)
     return LIB
 

@@ -68,6 +68,20 @@ hipError_t launch_fill_u16(uint16_t* p, long long n, uint16_t v, hipStream_t s);
 
 // One launch over rows [0, p.M) of x; p.M <= kGemvMaxRows (GEMV) or
 // kMfmaMaxRows (MFMA); `tiles` passes tiles_supported(path, tiles).
-hipError_t launch_matmul(const MatmulParams& p, int bits, int path, int tiles, hipStream_t s);
+// launch_matmul_bits<B> is defined in lutq_matmul.hip, which is compiled
+// once per code width B.
+template <int BITS>
+hipError_t launch_matmul_bits(const MatmulParams& p, int path, int tiles, hipStream_t s);
+extern template hipError_t launch_matmul_bits<2>(const MatmulParams&, int, int, hipStream_t);
+extern template hipError_t launch_matmul_bits<3>(const MatmulParams&, int, int, hipStream_t);
+extern template hipError_t launch_matmul_bits<4>(const MatmulParams&, int, int, hipStream_t);
+inline hipError_t launch_matmul(const MatmulParams& p, int bits, int path, int tiles,
+                                hipStream_t s) {
+  switch (bits) {
+    case 2: return launch_matmul_bits<2>(p, path, tiles, s);
+    case 3: return launch_matmul_bits<3>(p, path, tiles, s);
+    default: return launch_matmul_bits<4>(p, path, tiles, s);
+  }
+}
 
 }  // namespace lutq

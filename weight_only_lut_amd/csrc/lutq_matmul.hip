@@ -472,6 +472,8 @@ void matmul_kernel(const MatmulParams pk) {
 // matrices, which need many workgroups to fill the device).
 constexpr int kPf = 2;
 
+// Host-side shape rules: compiled once (in the width-4 object).
+#if LUTQ_MATMUL_BITS == 4
 bool tiles_supported(int path, int tiles) {
   if (path == kPathMfma) return tiles == 2 || tiles == 4 || tiles == 8;
   return tiles == 1 || tiles == 2;
@@ -486,6 +488,7 @@ int pick_tiles(int path, int mrows, int ntiles, int cus) {
   if (ntiles >= 2 * cus) return 4;
   return 2;
 }
+#endif
 
 template <int BITS, bool MFMA, int MROWS, int TPW, int WAVES, int OCC>
 static hipError_t launch_t(const MatmulParams& p, hipStream_t s) {
@@ -525,7 +528,7 @@ static hipError_t launch_gemv(const MatmulParams& p, int tiles, hipStream_t s) {
 }
 
 template <int BITS>
-static hipError_t launch_bits(const MatmulParams& p, int path, int tiles, hipStream_t s) {
+hipError_t launch_matmul_bits(const MatmulParams& p, int path, int tiles, hipStream_t s) {
   if (path == kPathMfma) {
     if (p.M <= 16) return launch_mfma<BITS, 16>(p, tiles, s);
     return launch_mfma<BITS, 32>(p, tiles, s);
@@ -536,12 +539,11 @@ static hipError_t launch_bits(const MatmulParams& p, int path, int tiles, hipStr
   return launch_gemv<BITS, 8>(p, tiles, s);
 }
 
-hipError_t launch_matmul(const MatmulParams& p, int bits, int path, int tiles, hipStream_t s) {
-  switch (bits) {
-    case 2: return launch_bits<2>(p, path, tiles, s);
-    case 3: return launch_bits<3>(p, path, tiles, s);
-    default: return launch_bits<4>(p, path, tiles, s);
-  }
-}
+// This file is compiled once per code width (the build passes
+// -DLUTQ_MATMUL_BITS=2, 3 and 4), so the widths' kernels compile in parallel.
+#ifndef LUTQ_MATMUL_BITS
+#error "compile with -DLUTQ_MATMUL_BITS=2, 3 or 4"
+#endif
+template hipError_t launch_matmul_bits<LUTQ_MATMUL_BITS>(const MatmulParams&, int, int, hipStream_t);
 
 }  // namespace lutq
