@@ -145,40 +145,51 @@ def cpu_baseline(case, budget_s=15.0):
     }
 
 
-class ZeroPointCase(Case):
-    """A workload matrix with per-group zero points (lutq_matmul_zp)."""
+class VariantCase(Case):
+    """A workload matrix launched plain, with per-group zero points
+    (lutq_matmul_zp) or with four per-group data types (lutq_matmul_typed)."""
 
     def __init__(self, lutq, torch, wname, mat, M):
         import numpy as np
+
+        from synth import tables
         super().__init__(lutq, torch, wname, mat, M)
         c, T, s, x = self.host
         lo, hi = float(T.astype(np.float32).min()), float(T.astype(np.float32).max())
-        z = np.random.default_rng(7).uniform(lo, hi, s.shape).astype(np.float16)
-        self.zeros = torch.from_numpy(z).cuda()
-        self.bytes += z.nbytes
-        self.use_zeros = True
+        rng = np.random.default_rng(7)
+        z = rng.uniform(lo, hi, s.shape).astype(np.float16)
+        luts = np.stack([T] + [tables.make(k, self.w.bits) for k in ("nf", "lloyd_max", "log")])
+        ty = rng.integers(0, 4, s.shape).astype(np.uint8)
+        self.zeros, self.luts, self.types = (torch.from_numpy(a).cuda() for a in (z, luts, ty))
+        self.base_bytes = self.bytes
+        self.extra_bytes = {"plain": 0, "zeros": z.nbytes, "types": ty.nbytes + luts.nbytes}
+        self.mode = "plain"
 
     def call(self, lutq, i):
-        lutq.matmul(self.x, self.packed[i % len(self.packed)], self.lut, self.scales,
-                    zeros=self.zeros if self.use_zeros else None, out=self.y)
+        P = self.packed[i % len(self.packed)]
+        if self.mode == "types":
+            lutq.matmul(self.x, P, self.luts, self.scales, types=self.types, out=self.y)
+        else:
+            lutq.matmul(self.x, P, self.lut, self.scales,
+                        zeros=self.zeros if self.mode == "zeros" else None, out=self.y)
 
 
-def zero_point_section(lutq, torch, args):
-    """Per-group zero points on the headline matrix at batch 1 and 16: time
-    against the same launch without them (cold weights)."""
+def variant_section(lutq, torch, args):
+    """Per-group zero points and per-group data types (four tables) on the
+    headline matrix at batch 1 and 16: time against the plain launch (cold)."""
     out = {}
     steps = max(20, args.steps // 4)
-    for label, wname, M in (("int4_up_proj_M1", "int4_up_proj", 1), ("int4_up_proj_M16", "int4_up_proj", 16)):
-        zc = ZeroPointCase(lutq, torch, wname, None, M)
-        zc.use_zeros = False
-        plain = time_case(lutq, torch, zc, steps, args.warmup)
-        zc.use_zeros = True
-        zp = time_case(lutq, torch, zc, steps, args.warmup)
-        out[label] = {"plain_us": round(plain, 3), "zero_points_us": round(zp, 3),
-                      "zero_points_GBps": round(zc.bytes / (zp * 1e-6) / 1e9, 1),
-                      "overhead": round(zp / plain - 1, 4)}
-        log(f"[bench] zero points {label}: plain {plain:.2f} us, with zero points {zp:.2f} us")
-        del zc
+    for M in (1, 16):
+        vc = VariantCase(lutq, torch, "int4_up_proj", None, M)
+        rec = {}
+        for mode in ("plain", "zeros", "types"):
+            vc.mode = mode
+            us = time_case(lutq, torch, vc, steps, args.warmup)
+            nbytes = vc.base_bytes + vc.extra_bytes[mode]
+            rec[mode] = {"us": round(us, 3), "GBps": round(nbytes / (us * 1e-6) / 1e9, 1)}
+            log(f"[bench] variants M={M} {mode}: {us:.2f} us")
+        out[f"int4_up_proj_M{M}"] = rec
+        del vc
         torch.cuda.empty_cache()
     return out
 
@@ -305,7 +316,8 @@ def main():
     ap.add_argument("--no-batch32", action="store_true")
     ap.add_argument("--no-quantizer", action="store_true")
     ap.add_argument("--no-fused", action="store_true")
-    ap.add_argument("--no-zero-points", action="store_true")
+    ap.add_argument("--no-variants", action="store_true",
+                    help="skip the zero-point and data-type timings")
     ap.add_argument("--no-warm", action="store_true",
                     help="skip the Infinity-Cache-warm repeats (so a kernel trace holds cold calls only)")
     ap.add_argument("--sweep", action="store_true", help="also time every workload (stderr)")
@@ -388,8 +400,8 @@ def main():
         extra["quantizer"] = quantizer_section(lutq, torch, args)
     if not args.no_fused:
         extra["fused"] = fused_section(lutq, torch, args)
-    if not args.no_zero_points:
-        extra["zero_points"] = zero_point_section(lutq, torch, args)
+    if not args.no_variants:
+        extra["variants"] = variant_section(lutq, torch, args)
 
     if args.sweep:
         extra["sweep"] = sweep(lutq, torch, args)

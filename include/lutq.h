@@ -211,6 +211,26 @@ int lutq_matmul_zp(const uint16_t* x, const lutq_packed_t* packed, const uint16_
                    const uint16_t* scales, const uint16_t* zeros, uint16_t* y, int M, int N, int K,
                    const lutq_options_t* opts, void* stream);
 
+/* ---- per-group data types ----------------------------------------------------
+ * A few tables, one chosen per group (BitMoD abstract: the data type is
+ * chosen per group of weights):
+ *     W_hat[n, k] = s[n, g] * (T_{types[n, g]}[c[n, k]] - z[n, g]),  g = k / group,
+ * with z = 0 when `zeros` is NULL (zero points as lutq_matmul_zp).
+ *   luts  : device, fp16 [ntypes][2^bits] (tables one after another),
+ *           4-byte aligned; 1 <= ntypes <= LUTQ_MAX_TYPES.
+ *   types : device, uint8 [N, K/group] row-major type ids. An id is taken
+ *           modulo LUTQ_MAX_TYPES; one (mod 4) at or above ntypes reads table 0.
+ * group must be > 0 (LUTQ_EGROUP otherwise). The tables share the on-chip
+ * duplicated table (16 copies each instead of 64), and the ids are fetched
+ * with the scales (0.0625 bit per weight at group 128). Other arguments,
+ * numerics and errors as lutq_matmul_ex; LUTQ_EINVAL for ntypes outside
+ * [1, LUTQ_MAX_TYPES] or NULL types with N * K > 0. */
+#define LUTQ_MAX_TYPES 4
+int lutq_matmul_typed(const uint16_t* x, const lutq_packed_t* packed, const uint16_t* luts,
+                      int ntypes, const uint8_t* types, const uint16_t* scales,
+                      const uint16_t* zeros, uint16_t* y, int M, int N, int K,
+                      const lutq_options_t* opts, void* stream);
+
 /* ---- quantizer ------------------------------------------------------------
  * Round-to-nearest onto a lookup table: the step that produces the codes and
  * scales lutq_repack and lutq_matmul consume ("PTQ-damage" abstract:

@@ -207,6 +207,22 @@ def test_matmul_zp_validates_before_launching(lib):
     assert lib.lutq_matmul_multi(x, arr, 2, 1, 256, None, None) == EGROUP
 
 
+def test_matmul_typed_validates_before_launching(lib):
+    P = ctypes.c_void_p
+    x, luts, ty, sc, y = P(0x1000), P(0x2000), P(0x6000), P(0x3000), P(0x4000)
+
+    def call(desc=None, nt=2, types=ty, M=1, N=64, K=256, luts=luts):
+        d = _desc(N=N, K=K) if desc is None else desc
+        return lib.lutq_matmul_typed(x, ctypes.byref(d), luts, nt, types, sc, None, y, M, N, K,
+                                     None, None)
+
+    assert call(desc=_desc(group=0)) == EGROUP
+    assert call(nt=0) == EINVAL and call(nt=_lib.MAX_TYPES + 1) == EINVAL
+    assert call(types=P(0)) == EINVAL
+    assert call(luts=P(0x2002)) == EALIGN
+    assert call(M=0) == OK
+
+
 def test_quantizer_validates_before_launching(lib):
     P = ctypes.c_void_p
     err = ctypes.c_double(0)

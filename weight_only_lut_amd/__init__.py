@@ -19,6 +19,7 @@ from ._lib import (  # noqa: F401
     load_library,
     log_base_search,
     MAX_FUSED,
+    MAX_TYPES,
     matmul,
     matmul_multi,
     packed_bytes,

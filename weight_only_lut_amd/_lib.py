@@ -22,8 +22,10 @@ EXPORTS = (
     "lutq_packed_bytes", "lutq_repack", "lutq_unpack", "lutq_matmul", "lutq_matmul_ex",
     "lutq_plan", "lutq_strerror", "lutq_last_hip_error", "lutq_shutdown",
     "lutq_quantize", "lutq_quant_error", "lutq_log_base_search", "lutq_matmul_multi",
-    "lutq_matmul_zp",
+    "lutq_matmul_zp", "lutq_matmul_typed",
 )
+
+MAX_TYPES = 4
 
 MAX_FUSED = 4
 
@@ -94,6 +96,9 @@ def load_library():
     lib.lutq_matmul_zp.argtypes = [vp, ctypes.POINTER(PackedDesc), vp, vp, vp, vp, i32, i32, i32,
                                    ctypes.POINTER(Options), vp]
     lib.lutq_matmul_zp.restype = i32
+    lib.lutq_matmul_typed.argtypes = [vp, ctypes.POINTER(PackedDesc), vp, i32, vp, vp, vp, vp, i32,
+                                      i32, i32, ctypes.POINTER(Options), vp]
+    lib.lutq_matmul_typed.restype = i32
     lib.lutq_plan.restype = i32
     lib.lutq_strerror.argtypes = [i32]
     lib.lutq_strerror.restype = ctypes.c_char_p
@@ -201,10 +206,11 @@ def unpack(p: Packed):
     return out
 
 
-def matmul(x, p: Packed, lut, scales, *, zeros=None, path: str = "auto", ksplit: int = 0,
-           tiles: int = 0, out=None):
-    """lutq_matmul_ex (lutq_matmul_zp with ``zeros``): y[M, N] = x[M, K] .
-    dequant(p, lut, scales[, zeros])^T, fp16 out."""
+def matmul(x, p: Packed, lut, scales, *, zeros=None, types=None, path: str = "auto",
+           ksplit: int = 0, tiles: int = 0, out=None):
+    """lutq_matmul_ex (lutq_matmul_zp with ``zeros``; lutq_matmul_typed with
+    ``types``, uint8 [N, K/group], and ``lut`` fp16 [ntypes, 2^bits]):
+    y[M, N] = x[M, K] . dequant(p, lut, scales[, zeros][, types])^T, fp16 out."""
     import torch
     _need_cuda(x, "x", torch.float16)
     _need_cuda(lut, "lut", torch.float16)
@@ -217,7 +223,15 @@ def matmul(x, p: Packed, lut, scales, *, zeros=None, path: str = "auto", ksplit:
         if tuple(out.shape) != (M, p.N):
             raise ValueError("out has the wrong shape")
     opts = _options(path, ksplit, tiles)
-    if zeros is None:
+    if types is not None:
+        _need_cuda(types, "types", torch.uint8)
+        if zeros is not None:
+            _need_cuda(zeros, "zeros", torch.float16)
+        nt = lut.shape[0] if lut.dim() == 2 else 1
+        rc = _lib().lutq_matmul_typed(_ptr(x), ctypes.byref(p.desc), _ptr(lut), nt, _ptr(types),
+                                      _ptr(scales), _ptr(zeros), _ptr(out), M, p.N, K,
+                                      ctypes.byref(opts), _stream(x.device))
+    elif zeros is None:
         rc = _lib().lutq_matmul_ex(_ptr(x), ctypes.byref(p.desc), _ptr(lut), _ptr(scales),
                                    _ptr(out), M, p.N, K, ctypes.byref(opts), _stream(x.device))
     else:

@@ -173,7 +173,8 @@ void plan(int M, int N, int K, int cus, lutq_options_t* o) {
 // checked, each matching K; bits and group equal across them). One launch
 // per batch slice covers every matrix with N > 0.
 int run_matmul(const uint16_t* x, const lutq_matmul_item_t* items, int count, int M, int K,
-               const lutq_options_t* opts, void* stream) {
+               const lutq_options_t* opts, void* stream, const uint8_t* types = nullptr,
+               int ntypes = 0) {
   lutq_options_t o;
   int rc = read_options(opts, &o);
   if (rc) return rc;
@@ -245,6 +246,8 @@ int run_matmul(const uint16_t* x, const lutq_matmul_item_t* items, int count, in
   p.scales = p.seg[0].scales;
   p.zeros = p.seg[0].zeros;
   p.zp = zp;
+  p.types = types;
+  p.ntypes = ntypes;
   p.N = p.seg[0].N;
   p.ntiles = p.seg[0].ntiles;
   p.nseg = nlive;
@@ -346,6 +349,21 @@ int lutq_matmul_ex(const uint16_t* x, const lutq_packed_t* packed, const uint16_
   return run_matmul(x, &item, 1, M, K, opts, stream);
 }
 
+int lutq_matmul_typed(const uint16_t* x, const lutq_packed_t* packed, const uint16_t* luts,
+                      int ntypes, const uint8_t* types, const uint16_t* scales,
+                      const uint16_t* zeros, uint16_t* y, int M, int N, int K,
+                      const lutq_options_t* opts, void* stream) {
+  int rc = check_desc(packed);
+  if (rc) return rc;
+  if (M < 0 || N < 0 || K < 0) return LUTQ_EINVAL;
+  if (N != packed->N || K != packed->K) return LUTQ_EMISMATCH;
+  if (packed->group == 0) return LUTQ_EGROUP;  // a data type per group
+  if (ntypes < 1 || ntypes > LUTQ_MAX_TYPES) return LUTQ_EINVAL;
+  if ((size_t)N * K > 0 && !types) return LUTQ_EINVAL;
+  const lutq_matmul_item_t item = {packed, luts, scales, zeros, y};
+  return run_matmul(x, &item, 1, M, K, opts, stream, types, ntypes);
+}
+
 int lutq_matmul_zp(const uint16_t* x, const lutq_packed_t* packed, const uint16_t* lut,
                    const uint16_t* scales, const uint16_t* zeros, uint16_t* y, int M, int N, int K,
                    const lutq_options_t* opts, void* stream) {
@@ -383,6 +401,7 @@ int lutq_matmul(const uint16_t* x, const lutq_packed_t* packed, const uint16_t* 
 namespace {
 
 static_assert(LUTQ_MAX_FUSED == lutq::kMaxSegments, "one kernel segment per fused matrix");
+static_assert(LUTQ_MAX_TYPES == lutq::kMaxTypes, "tables the pair table holds");
 static_assert(LUTQ_RULE_ABSMAX == lutq::kRuleAbsmax && LUTQ_RULE_RANGE == lutq::kRuleRange,
               "rule values");
 

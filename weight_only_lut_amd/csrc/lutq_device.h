@@ -153,6 +153,24 @@ __device__ __forceinline__ uint32_t lut_to_lanes(const uint16_t* lut, int lane) 
   return (e & 1) ? (v >> 16) : (v & 0xFFFFu);
 }
 
+// Per-group data types: up to kMaxTypes tables share the LDS pair table,
+// kCopies / kMaxTypes copies each. Entry (idx, type, copy) lives at byte
+// (idx << 8) | (type << 6) | (copy << 2): the same single v_perm builds the
+// address, from a lane byte (type << 6) | ((lane mod 16) << 2).
+constexpr int kMaxTypes = 4;
+constexpr int kTypedCopies = kCopies / kMaxTypes;
+
+// Table (lane >> BITS) entry (lane mod 2^BITS) for lanes 0 .. 4 * 2^BITS - 1
+// (repeating beyond), from `ntypes` tables stored one after another; a table
+// past ntypes repeats table 0. One per-lane load per workgroup.
+template <int BITS>
+__device__ __forceinline__ uint32_t typed_lut_lane(const uint16_t* luts, int ntypes, int lane) {
+  constexpr int L = 1 << BITS;
+  const int e = lane & (kMaxTypes * L - 1);
+  const int t = e >> BITS;
+  return luts[(t < ntypes ? t : 0) * L + (e & (L - 1))];
+}
+
 // Fill the duplicated pair table. `lut_lane` holds T[lane] in lanes
 // 0..2^BITS-1 of every wave; entries are gathered with cross-lane reads.
 // THREADS / 256 threads share an entry: each computes the entry's value once
@@ -161,7 +179,7 @@ __device__ __forceinline__ uint32_t lut_to_lanes(const uint16_t* lut, int lane) 
 // store instruction cover all 64 banks evenly (4 dwords per bank, the
 // minimum for 16-byte stores) instead of piling onto two bank groups. The
 // caller issues a barrier before the first lookup.
-template <int BITS, int THREADS>
+template <int BITS, int THREADS, bool TYPED = false>
 __device__ __forceinline__ void build_pair_table(uint32_t* table, uint32_t lut_lane, int tid) {
   static_assert(THREADS % kPairEntries == 0, "whole threads per entry");
   constexpr int kPerEntry = THREADS / kPairEntries;   // threads per entry
@@ -172,13 +190,33 @@ __device__ __forceinline__ void build_pair_table(uint32_t* table, uint32_t lut_l
   const uint32_t part = (uint32_t)tid % kPerEntry;
   uint32_t c0, c1;
   pair_codes<BITS>(idx, c0, c1);
-  const uint32_t v0 = (uint32_t)__shfl((int)lut_lane, (int)c0) & 0xFFFFu;
-  const uint32_t v1 = (uint32_t)__shfl((int)lut_lane, (int)c1) & 0xFFFFu;
-  const uint32_t v = v0 | (v1 << 16);
-  const u32x4 q = {v, v, v, v};
   u32x4* dst = reinterpret_cast<u32x4*>(table + idx * kCopies + part * kCopiesPer);
+  if constexpr (!TYPED) {
+    const uint32_t v0 = (uint32_t)__shfl((int)lut_lane, (int)c0) & 0xFFFFu;
+    const uint32_t v1 = (uint32_t)__shfl((int)lut_lane, (int)c1) & 0xFFFFu;
+    const uint32_t v = v0 | (v1 << 16);
+    const u32x4 q = {v, v, v, v};
 #pragma unroll
-  for (int k = 0; k < C; ++k) dst[(k + idx) & (C - 1)] = q;
+    for (int k = 0; k < C; ++k) dst[(k + idx) & (C - 1)] = q;
+  } else {
+    // the pair of every type (lut_lane holds table t's entries at lanes t 2^BITS + c)
+    uint32_t v[kMaxTypes];
+#pragma unroll
+    for (int t = 0; t < kMaxTypes; ++t) {
+      const uint32_t v0 = (uint32_t)__shfl((int)lut_lane, (int)((t << BITS) | c0)) & 0xFFFFu;
+      const uint32_t v1 = (uint32_t)__shfl((int)lut_lane, (int)((t << BITS) | c1)) & 0xFFFFu;
+      v[t] = v0 | (v1 << 16);
+    }
+#pragma unroll
+    for (int k = 0; k < C; ++k) {
+      const int slot4 = (k + (int)idx) & (C - 1);                 // 16-byte store in the share
+      const int type = (int)(part * kCopiesPer + 4 * slot4) / kTypedCopies;
+      uint32_t w = v[0];
+#pragma unroll
+      for (int t = 1; t < kMaxTypes; ++t) w = type == t ? v[t] : w;
+      dst[slot4] = u32x4{w, w, w, w};
+    }
+  }
 }
 
 // acc += dot(x from lane 4j+i of this lane's 16-lane row, p_i), i = 0..3, in

@@ -37,6 +37,8 @@ struct MatmulParams {
   int ksplit;             // workgroups per row block along K
   int cps;                // chunks per split
   bool zp;                // zero points in this launch (any matrix); grouped only
+  const uint8_t* types;   // per-group data type ids [N, K/group], or null (one table)
+  int ntypes;             // tables at lut ([ntypes][2^bits]) when types is set
   // Fused launch (nseg > 1): matrices sharing x, K, bits and group; the
   // fields packed .. y, N and ntiles above are then taken from seg[].
   int nseg;

@@ -37,7 +37,8 @@ namespace lutq {
 // pipeline (PF - 1 chunks in flight while one is computed);
 // TPW: 16-row tiles per wave (and per workgroup); WAVES: waves per workgroup,
 // which split the K range; OCC: waves per SIMD the register budget targets.
-template <int BITS, bool MFMA, int MROWS, bool GROUPED, bool ZP, int PF, int TPW, int WAVES, int OCC>
+template <int BITS, bool MFMA, int MROWS, bool GROUPED, bool ZP, bool TYPED, int PF, int TPW, int WAVES,
+          int OCC>
 __global__ __launch_bounds__(WAVES * kWave) __attribute__((amdgpu_waves_per_eu(OCC)))
 void matmul_kernel(const MatmulParams pk) {
   // A fused launch covers several matrices: this workgroup's row block picks
@@ -89,7 +90,8 @@ void matmul_kernel(const MatmulParams pk) {
   // The table values, one per lane (lanes >= 2^BITS repeat the table).
   // Read with wave-uniform (scalar) loads: they do not queue behind the
   // vector loads of the code stream, so the LDS table is ready early.
-  const uint32_t lut_lane = lut_to_lanes<BITS>(p.lut, lane);
+  const uint32_t lut_lane =
+      TYPED ? typed_lut_lane<BITS>(p.lut, p.ntypes, lane) : lut_to_lanes<BITS>(p.lut, lane);
 
   const int rb = blockIdx.x / p.ksplit;            // row block of the launch (split-K slots)
   const int ks = blockIdx.x - rb * p.ksplit;
@@ -144,6 +146,9 @@ void matmul_kernel(const MatmulParams pk) {
   const __amdgpu_buffer_rsrc_t zrsrc = make_rsrc(
       ZP ? p.zeros + (size_t)row0 * gpr : nullptr,
       ZP && p.zeros ? rows_here * (uint32_t)gpr * 2u : 0u);
+  // Data type ids, one byte per group, batched like the scales.
+  const __amdgpu_buffer_rsrc_t trsrc = make_rsrc(
+      TYPED ? p.types + (size_t)row0 * gpr : nullptr, TYPED ? rows_here * (uint32_t)gpr : 0u);
 
   // activations of this launch's M rows
   const __amdgpu_buffer_rsrc_t xrsrc =
@@ -166,6 +171,7 @@ void matmul_kernel(const MatmulParams pk) {
   SlotRegs<BITS> cbuf[PF][TPW];
   uint32_t scur[TPW], snext[TPW];  // scale batches: in use, in flight
   uint32_t zcur[ZP ? TPW : 1], znext[ZP ? TPW : 1];  // zero-point batches
+  uint32_t tcur[TYPED ? TPW : 1], tnext[TYPED ? TPW : 1];  // type-id batches
   uint32_t xbuf[PF][MFMA ? 1 : MROWS];
   u32x4 abuf[PF][MT][MFMA ? 4 : 1];
 
@@ -209,11 +215,27 @@ void matmul_kernel(const MatmulParams pk) {
       for (int t = 0; t < TPW; ++t)
         znext[t] = __builtin_amdgcn_raw_buffer_load_b16(zrsrc, soff[t] + sb, 0, 0);
     }
+    if constexpr (TYPED) {
+      const uint32_t tb = sb == kOutOfRange ? kOutOfRange : sb >> 1;  // one byte per group
+#pragma unroll
+      for (int t = 0; t < TPW; ++t)
+        tnext[t] = __builtin_amdgcn_raw_buffer_load_b8(trsrc, (soff[t] >> 1) + tb, 0, 0);
+    }
   };
   // the scale of this lane's row at step position u (0 .. SB-1) of the batch
   auto step_scale = [&](int t, int u) __attribute__((always_inline)) {
     const int v = __builtin_amdgcn_ds_bpermute((16 * u + r) * 4, (int)scur[t]);
     return f16_bits_to_f32((uint16_t)v);
+  };
+  // the LDS lane byte of tile t at step position u: this lane's copy, and
+  // with data types the type of its row's group
+  auto step_lane_byte = [&](int t, int u) __attribute__((always_inline)) {
+    if constexpr (!TYPED) {
+      return lane_byte;
+    } else {
+      const uint32_t v = (uint32_t)__builtin_amdgcn_ds_bpermute((16 * u + r) * 4, (int)tcur[t]);
+      return ((v & (kMaxTypes - 1)) << 6) | ((uint32_t)r << 2);
+    }
   };
   auto step_zero = [&](int t, int u) __attribute__((always_inline)) {
     const int v = __builtin_amdgcn_ds_bpermute((16 * u + r) * 4, (int)zcur[ZP ? t : 0]);
@@ -241,6 +263,9 @@ void matmul_kernel(const MatmulParams pk) {
       for (int t = 0; t < TPW; ++t)
 #pragma unroll
         for (int m = 0; m < MROWS; ++m) cs[t][m] = 0.f;
+      uint32_t lbt[TPW];
+#pragma unroll
+      for (int t = 0; t < TPW; ++t) lbt[t] = step_lane_byte(t, u);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         uint32_t idx4[TPW];
@@ -250,7 +275,7 @@ void matmul_kernel(const MatmulParams pk) {
         for (int t = 0; t < TPW; ++t) {
           uint32_t pr[4];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) pr[i] = lds_load(table, pair_addr(idx4[t], lane_byte, i));
+          for (int i = 0; i < 4; ++i) pr[i] = lds_load(table, pair_addr(idx4[t], lbt[t], i));
           // pair i of k-step j meets the activations of lane 4j+i of the row
 #pragma unroll
           for (int m = 0; m < MROWS; ++m)
@@ -290,13 +315,14 @@ void matmul_kernel(const MatmulParams pk) {
       // behind them even with a single wave per SIMD.
       u32x4 bq[2][4];
       auto lookup = [&](int t, u32x4(&dst)[4]) __attribute__((always_inline)) {
+        const uint32_t lb = step_lane_byte(t, u);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const uint32_t idx4 = step_indices<BITS>(cbuf[s][t], j);
-          dst[j].x = lds_load(table, pair_addr(idx4, lane_byte, 0));
-          dst[j].y = lds_load(table, pair_addr(idx4, lane_byte, 1));
-          dst[j].z = lds_load(table, pair_addr(idx4, lane_byte, 2));
-          dst[j].w = lds_load(table, pair_addr(idx4, lane_byte, 3));
+          dst[j].x = lds_load(table, pair_addr(idx4, lb, 0));
+          dst[j].y = lds_load(table, pair_addr(idx4, lb, 1));
+          dst[j].z = lds_load(table, pair_addr(idx4, lb, 2));
+          dst[j].w = lds_load(table, pair_addr(idx4, lb, 3));
         }
       };
       lookup(0, bq[0]);
@@ -366,7 +392,7 @@ void matmul_kernel(const MatmulParams pk) {
   if constexpr (GROUPED) issue_scales(0);
   static_for<PF - 1>([&](auto S) { issue(S, chunk(decltype(S)::value)); });
 
-  build_pair_table<BITS, kThreads>(table, lut_lane, tid);
+  build_pair_table<BITS, kThreads, TYPED>(table, lut_lane, tid);
   __syncthreads();
 
   // One step at position u of a U-step group starting at i0. Steps past the
@@ -384,6 +410,10 @@ void matmul_kernel(const MatmulParams pk) {
       if constexpr (ZP) {
 #pragma unroll
         for (int t = 0; t < TPW; ++t) zcur[t] = znext[t];
+      }
+      if constexpr (TYPED) {
+#pragma unroll
+        for (int t = 0; t < TPW; ++t) tcur[t] = tnext[t];
       }
       issue_scales(i + SB);
     }
@@ -498,12 +528,17 @@ static hipError_t launch_t(const MatmulParams& p, hipStream_t s) {
   // registers of two waves per SIMD; this shape runs on few enough
   // workgroups that one wave per SIMD costs little.
   constexpr int OCC_G = (MFMA && MROWS == 32 && TPW == 8) ? 1 : OCC;
-  if (p.group != 0 && p.zp)
-    matmul_kernel<BITS, MFMA, MROWS, true, true, kPf, TPW, WAVES, OCC_G><<<grid, WAVES * kWave, 0, s>>>(p);
-  else if (p.group != 0)
-    matmul_kernel<BITS, MFMA, MROWS, true, false, kPf, TPW, WAVES, OCC_G><<<grid, WAVES * kWave, 0, s>>>(p);
+  const dim3 block(WAVES * kWave);
+  if (p.group == 0)
+    matmul_kernel<BITS, MFMA, MROWS, false, false, false, kPf, TPW, WAVES, OCC><<<grid, block, 0, s>>>(p);
+  else if (p.types && p.zp)
+    matmul_kernel<BITS, MFMA, MROWS, true, true, true, kPf, TPW, WAVES, OCC_G><<<grid, block, 0, s>>>(p);
+  else if (p.types)
+    matmul_kernel<BITS, MFMA, MROWS, true, false, true, kPf, TPW, WAVES, OCC_G><<<grid, block, 0, s>>>(p);
+  else if (p.zp)
+    matmul_kernel<BITS, MFMA, MROWS, true, true, false, kPf, TPW, WAVES, OCC_G><<<grid, block, 0, s>>>(p);
   else
-    matmul_kernel<BITS, MFMA, MROWS, false, false, kPf, TPW, WAVES, OCC><<<grid, WAVES * kWave, 0, s>>>(p);
+    matmul_kernel<BITS, MFMA, MROWS, true, false, false, kPf, TPW, WAVES, OCC_G><<<grid, block, 0, s>>>(p);
   return hipGetLastError();
 }
 
