@@ -15,7 +15,8 @@ rescaling of partial sums, which is the same sum in another order):
 and, with per-group zero points z (page 1, LogbQuant abstract: asymmetric
 linear quantization), W_hat[n, k] = s[n, k // group] * (T[c[n, k]] - z[n, k // group]);
 with per-group data types (page 2, BitMoD abstract), T is the table the
-group's type id selects.
+group's type id selects; binary-coded weights (page 4, AlphaTuning
+abstract) are W_hat[n, k] = sum_i alpha_i[n, g] * (2 bit_i(c[n, k]) - 1).
 
 Every function cites the passage it follows. Parity status of each function
 is in the docstring; all are pinned by tests/test_oracle.py, and the
@@ -30,6 +31,8 @@ from .lutq_ref import (  # noqa: F401
     dequant,
     reference,
     reference_rows,
+    dequant_bcq,
+    reference_bcq,
     error_bound,
     check,
 )

@@ -103,6 +103,54 @@ def dequant(codes: np.ndarray, lut: np.ndarray, scales: np.ndarray, group: int,
     return (t.reshape(N, K // group, group) * s[:, :, None]).reshape(N, K)
 
 
+# -- binary-coding quantization (page 4, AlphaTuning abstract: weights
+#    factorized into binary parameters and separate scaling factors) -------
+
+def dequant_bcq(codes: np.ndarray, alphas: np.ndarray, group: int) -> np.ndarray:
+    """W_hat[n, k] = sum_i alphas[i, n, g] * (2 * bit_i(c[n, k]) - 1), g = k // group, in fp64.
+
+    ``codes`` hold the q binary planes as the bits of a q-bit code (plane i
+    in bit i); ``alphas`` are fp16 [q, N, K / group]. Every weight is a sum of
+    q signed fp16 values, exact in fp64. [N, K] fp64.
+
+    Pinned: exact rationals; q = 1 is a signed binary matrix; power-of-two
+    plane factors (alpha_i = a 2^i) give the uniform table 2c - (2^q - 1)
+    with scale a through ``dequant``; the same weights from the 2^q-entry
+    table of each group.
+    """
+    N, K = codes.shape
+    q = alphas.shape[0]
+    if group <= 0 or K % group:
+        raise ValueError("binary coding needs a group that divides K")
+    g = K // group
+    a = alphas.astype(np.float64).reshape(q, N, g, 1)
+    c = codes.astype(np.int64).reshape(N, g, group)
+    w = np.zeros((N, g, group))
+    for i in range(q):
+        w += a[i] * (2.0 * ((c >> i) & 1) - 1.0)
+    return w.reshape(N, K)
+
+
+def reference_bcq(x: np.ndarray, codes: np.ndarray, alphas: np.ndarray, group: int,
+                  rows=None):
+    """(y_ref, B) as ``reference``, for binary-coded weights (optionally only
+    output columns ``rows``)."""
+    if rows is not None:
+        rows = np.asarray(rows)
+        codes, alphas = codes[rows], alphas[:, rows]
+    x64 = x.astype(np.float64)
+    ax = np.abs(x64)
+    N = codes.shape[0]
+    y = np.empty((x.shape[0], N))
+    B = np.empty((x.shape[0], N))
+    for n0 in range(0, N, ROW_CHUNK):
+        n1 = min(N, n0 + ROW_CHUNK)
+        w = dequant_bcq(codes[n0:n1], alphas[:, n0:n1], group)
+        y[:, n0:n1] = x64 @ w.T
+        B[:, n0:n1] = ax @ np.abs(w).T
+    return y, B
+
+
 # -- the product (fp64 accumulation) ------------------------------------------
 
 def _rows(codes, lut, scales, group, rows, zeros=None, types=None):

@@ -380,3 +380,84 @@ def test_planted_type_index_by_row_is_caught(monkeypatch):
     monkeypatch.setattr(lutq_ref, "dequant", by_row)
     y, _ = oracle.reference(x, c, luts, s, 128, types=types)
     assert max(abs(y[m, n] - float(ex[m][n])) for m in range(2) for n in range(3)) > 1e-6
+
+
+# -- binary-coding quantization ----------------------------------------------
+
+def _bcq_case(seed, q=3, M=2, N=3, K=256, group=128):
+    rng = np.random.default_rng(seed)
+    c = rng.integers(0, 1 << q, (N, K)).astype(np.uint8)
+    a = rng.uniform(0.001, 0.05, (q, N, K // group)).astype(np.float16)
+    x = rng.normal(0, 1, (M, K)).astype(np.float16)
+    return c, a, x
+
+
+def _exact_bcq(x, c, a, group):
+    q = a.shape[0]
+    M, K = x.shape
+    N = c.shape[0]
+    return [[sum(Fraction(float(x[m, k])) * sum(
+        Fraction(float(a[i, n, k // group])) * (1 if (int(c[n, k]) >> i) & 1 else -1)
+        for i in range(q)) for k in range(K)) for n in range(N)] for m in range(M)]
+
+
+@pytest.mark.parametrize("q,group", [(2, 128), (3, 256), (4, 128)])
+def test_bcq_matches_exact_rationals(q, group):
+    c, a, x = _bcq_case(50 + q, q=q, K=512, group=group)
+    y, B = oracle.reference_bcq(x, c, a, group)
+    ex = _exact_bcq(x, c, a, group)
+    for m in range(2):
+        for n in range(3):
+            assert abs(y[m, n] - float(ex[m][n])) <= 1e-12 * B[m, n] + 1e-300
+
+
+def test_bcq_one_plane_is_signed_binary():
+    rng = np.random.default_rng(51)
+    bits = rng.integers(0, 2, (4, 256)).astype(np.uint8)
+    a = rng.uniform(0.01, 0.1, (1, 4, 2)).astype(np.float16)
+    w = oracle.dequant_bcq(bits, a, 128)
+    sign = np.where(bits == 1, 1.0, -1.0)
+    assert np.array_equal(w, sign * np.repeat(a[0].astype(np.float64), 128, axis=1))
+
+
+@pytest.mark.parametrize("q", [2, 3, 4])
+def test_bcq_power_of_two_planes_are_a_uniform_table(q):
+    # alpha_i = a 2^i: W_hat = a (2c - (2^q - 1)), the uniform LUT with scale a
+    rng = np.random.default_rng(52 + q)
+    N, K = 5, 384
+    c = rng.integers(0, 1 << q, (N, K)).astype(np.uint8)
+    base = (2.0 ** rng.integers(-9, -4, (N, K // 128))).astype(np.float16)
+    a = np.stack([(base.astype(np.float64) * 2 ** i).astype(np.float16) for i in range(q)])
+    x = rng.normal(0, 1, (3, K)).astype(np.float16)
+    T = (2 * np.arange(1 << q) - ((1 << q) - 1)).astype(np.float16)
+    y_bcq, _ = oracle.reference_bcq(x, c, a, 128)
+    y_lut, _ = oracle.reference(x, c, T, base, 128)
+    assert np.array_equal(y_bcq, y_lut)
+
+
+def test_bcq_equals_a_table_per_group():
+    # the 2^q-entry table of each (row, group), indexed by the code
+    c, a, x = _bcq_case(53, q=3, N=4, K=384)
+    w = oracle.dequant_bcq(c, a, 128)
+    for n in range(4):
+        for g in range(3):
+            table = [sum(float(a[i, n, g]) * (1 if (code >> i) & 1 else -1) for i in range(3))
+                     for code in range(8)]
+            blk = c[n, 128 * g:128 * (g + 1)]
+            assert np.array_equal(w[n, 128 * g:128 * (g + 1)], np.array(table)[blk])
+
+
+@pytest.mark.parametrize("kind", ["plane_order", "sign", "group_by_row"])
+def test_planted_bcq_mistakes_are_caught(monkeypatch, kind):
+    c, a, x = _bcq_case(54, q=3, K=256)
+    ex = _exact_bcq(x, c, a, 128)
+    real = lutq_ref.dequant_bcq
+    if kind == "plane_order":
+        bad = lambda cc, aa, g: real(cc, aa[::-1], g)
+    elif kind == "sign":
+        bad = lambda cc, aa, g: real((~cc) & 7, aa, g)
+    else:
+        bad = lambda cc, aa, g: real(cc, aa.transpose(0, 2, 1).reshape(aa.shape), g)
+    monkeypatch.setattr(lutq_ref, "dequant_bcq", bad)
+    y, _ = oracle.reference_bcq(x, c, a, 128)
+    assert max(abs(y[m, n] - float(ex[m][n])) for m in range(2) for n in range(3)) > 1e-6
