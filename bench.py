@@ -174,9 +174,44 @@ class VariantCase(Case):
                         zeros=self.zeros if self.mode == "zeros" else None, out=self.y)
 
 
+class BcqCase:
+    """Binary-coded weights (q planes, alphas per plane, row and group 128) of
+    a workload matrix's shape, cold (lutq_matmul_bcq)."""
+
+    def __init__(self, lutq, torch, wname, M, q=3):
+        import numpy as np
+
+        from synth import workloads
+        w = workloads.WORKLOADS[wname]
+        _, m = w.matrix(None)
+        self.N, self.K, self.M = m.N, m.K, M
+        rng = np.random.default_rng(5)
+        c = rng.integers(0, 1 << q, (self.N, self.K)).astype(np.uint8)
+        a = np.stack([rng.uniform(0.01, 0.03, (self.N, self.K // 128)) / 2 ** p
+                      for p in range(q)]).astype(np.float16)
+        d = lambda v: torch.from_numpy(np.ascontiguousarray(v)).cuda()
+        P = lutq.repack(d(c), q, 128)
+        from weight_only_lut_amd._lib import Packed, PackedDesc
+        self.packed = [P]
+        for _ in range(max(2, -(-COLD_SET_BYTES // P.nbytes)) - 1):
+            data = P.data.clone()
+            desc = PackedDesc.from_buffer_copy(P.desc)
+            desc.data = data.data_ptr()
+            self.packed.append(Packed(data, desc))
+        self.alphas = d(a)
+        self.x = d(workloads.activations(w, M))
+        self.y = torch.empty((M, self.N), dtype=torch.float16, device="cuda")
+        self.bytes = (self.N * self.K * q // 8 + a.nbytes + M * self.K * 2 + M * self.N * 2)
+        torch.cuda.synchronize()
+
+    def call(self, lutq, i):
+        lutq.matmul_bcq(self.x, self.packed[i % len(self.packed)], self.alphas, out=self.y)
+
+
 def variant_section(lutq, torch, args):
-    """Per-group zero points and per-group data types (four tables) on the
-    headline matrix at batch 1 and 16: time against the plain launch (cold)."""
+    """Per-group zero points, per-group data types (four tables) and
+    binary-coded weights (q = 3) on the headline matrix's shape at batch 1
+    and 16, against the plain launch (cold)."""
     out = {}
     steps = max(20, args.steps // 4)
     for M in (1, 16):
@@ -190,6 +225,13 @@ def variant_section(lutq, torch, args):
             log(f"[bench] variants M={M} {mode}: {us:.2f} us")
         out[f"int4_up_proj_M{M}"] = rec
         del vc
+        torch.cuda.empty_cache()
+        bc = BcqCase(lutq, torch, "int4_up_proj", M, q=3)
+        us = time_case(lutq, torch, bc, steps, args.warmup)
+        out[f"bcq3_{bc.N}x{bc.K}_M{M}"] = {"us": round(us, 3),
+                                           "GBps": round(bc.bytes / (us * 1e-6) / 1e9, 1)}
+        log(f"[bench] variants M={M} bcq q=3: {us:.2f} us")
+        del bc
         torch.cuda.empty_cache()
     return out
 

@@ -231,6 +231,23 @@ int lutq_matmul_typed(const uint16_t* x, const lutq_packed_t* packed, const uint
                       const uint16_t* zeros, uint16_t* y, int M, int N, int K,
                       const lutq_options_t* opts, void* stream);
 
+/* ---- binary-coded weights ----------------------------------------------------
+ * Binary-coding quantization (AlphaTuning abstract: the weights factorize
+ * into binary parameters and separate scaling factors): q = bits binary
+ * planes, bit p of the q-bit code c[n, k] being plane p, and one fp16
+ * factor per plane, row and group:
+ *     W_hat[n, k] = sum_p alphas[p][n][g] * (2 bit_p(c[n, k]) - 1),  g = k / group,
+ * i.e. a 2^q-entry table per row and group. Computed as
+ * sum_p alpha_p (2 S_p - X) per group, with S_p = sum_k x bit_p(c) from an
+ * on-chip table of the planes' bits and X = sum_k x (as lutq_matmul_zp).
+ *   packed : lutq_repack of the codes with bits = q (2, 3 or 4), group > 0
+ *            (LUTQ_EGROUP otherwise).
+ *   alphas : device, fp16 [q][N][K/group] (plane-major), 2-byte aligned.
+ * The MFMA path runs with 2 tiles per wave (an explicit other `tiles` is
+ * LUTQ_EINVAL). Other arguments, numerics and errors as lutq_matmul_ex. */
+int lutq_matmul_bcq(const uint16_t* x, const lutq_packed_t* packed, const uint16_t* alphas,
+                    uint16_t* y, int M, int N, int K, const lutq_options_t* opts, void* stream);
+
 /* ---- quantizer ------------------------------------------------------------
  * Round-to-nearest onto a lookup table: the step that produces the codes and
  * scales lutq_repack and lutq_matmul consume ("PTQ-damage" abstract:

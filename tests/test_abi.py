@@ -223,6 +223,22 @@ def test_matmul_typed_validates_before_launching(lib):
     assert call(M=0) == OK
 
 
+def test_matmul_bcq_validates_before_launching(lib):
+    P = ctypes.c_void_p
+    x, al, y = P(0x1000), P(0x3000), P(0x4000)
+
+    def call(desc=None, alphas=al, M=1, opts=None):
+        d = _desc(bits=3) if desc is None else desc
+        return lib.lutq_matmul_bcq(x, ctypes.byref(d), alphas, y, M, d.N, d.K, opts, None)
+
+    assert call(desc=_desc(bits=3, group=0)) == EGROUP
+    assert call(alphas=P(0)) == EINVAL
+    assert call(alphas=P(0x3001)) == EALIGN
+    o = _lib.Options(); o.path, o.tiles = 2, 4
+    assert call(opts=ctypes.byref(o)) == EINVAL          # MFMA runs 2 tiles per wave
+    assert call(M=0) == OK
+
+
 def test_quantizer_validates_before_launching(lib):
     P = ctypes.c_void_p
     err = ctypes.c_double(0)

@@ -21,6 +21,7 @@ from ._lib import (  # noqa: F401
     MAX_FUSED,
     MAX_TYPES,
     matmul,
+    matmul_bcq,
     matmul_multi,
     packed_bytes,
     plan,

@@ -22,7 +22,7 @@ EXPORTS = (
     "lutq_packed_bytes", "lutq_repack", "lutq_unpack", "lutq_matmul", "lutq_matmul_ex",
     "lutq_plan", "lutq_strerror", "lutq_last_hip_error", "lutq_shutdown",
     "lutq_quantize", "lutq_quant_error", "lutq_log_base_search", "lutq_matmul_multi",
-    "lutq_matmul_zp", "lutq_matmul_typed",
+    "lutq_matmul_zp", "lutq_matmul_typed", "lutq_matmul_bcq",
 )
 
 MAX_TYPES = 4
@@ -99,6 +99,9 @@ def load_library():
     lib.lutq_matmul_typed.argtypes = [vp, ctypes.POINTER(PackedDesc), vp, i32, vp, vp, vp, vp, i32,
                                       i32, i32, ctypes.POINTER(Options), vp]
     lib.lutq_matmul_typed.restype = i32
+    lib.lutq_matmul_bcq.argtypes = [vp, ctypes.POINTER(PackedDesc), vp, vp, i32, i32, i32,
+                                    ctypes.POINTER(Options), vp]
+    lib.lutq_matmul_bcq.restype = i32
     lib.lutq_plan.restype = i32
     lib.lutq_strerror.argtypes = [i32]
     lib.lutq_strerror.restype = ctypes.c_char_p
@@ -279,6 +282,24 @@ def matmul_multi(x, mats, *, path: str = "auto", ksplit: int = 0, tiles: int = 0
     if rc:
         raise LutqError(rc, "lutq_matmul_multi")
     return ys
+
+
+def matmul_bcq(x, p: Packed, alphas, *, path: str = "auto", ksplit: int = 0, tiles: int = 0,
+               out=None):
+    """lutq_matmul_bcq: binary-coded weights (p packed with bits = q planes,
+    alphas fp16 [q, N, K/group]) -> y[M, N] fp16."""
+    import torch
+    _need_cuda(x, "x", torch.float16)
+    _need_cuda(alphas, "alphas", torch.float16)
+    M, K = x.shape
+    if out is None:
+        out = torch.empty((M, p.N), dtype=torch.float16, device=x.device)
+    opts = _options(path, ksplit, tiles)
+    rc = _lib().lutq_matmul_bcq(_ptr(x), ctypes.byref(p.desc), _ptr(alphas), _ptr(out), M, p.N, K,
+                                ctypes.byref(opts), _stream(x.device))
+    if rc:
+        raise LutqError(rc, "lutq_matmul_bcq")
+    return out
 
 
 def quantize(w, lut, bits: int, group: int, rule: str = "absmax"):

@@ -174,10 +174,12 @@ void plan(int M, int N, int K, int cus, lutq_options_t* o) {
 // per batch slice covers every matrix with N > 0.
 int run_matmul(const uint16_t* x, const lutq_matmul_item_t* items, int count, int M, int K,
                const lutq_options_t* opts, void* stream, const uint8_t* types = nullptr,
-               int ntypes = 0) {
+               int ntypes = 0, bool bcq = false) {
   lutq_options_t o;
   int rc = read_options(opts, &o);
   if (rc) return rc;
+  // binary-coded weights run the GEMV shapes and the 2-tile MFMA shape
+  if (bcq && o.path == LUTQ_PATH_MFMA && o.tiles != 0 && o.tiles != 2) return LUTQ_EINVAL;
   int live[LUTQ_MAX_FUSED];
   int nlive = 0, ntiles_all = 0;
   for (int i = 0; i < count; ++i) {
@@ -198,8 +200,8 @@ int run_matmul(const uint16_t* x, const lutq_matmul_item_t* items, int count, in
       zp = true;
     }
     if (K == 0) continue;
-    if (!it.lut || !it.scales) return LUTQ_EINVAL;
-    if (!aligned(it.lut, 4) || !aligned(it.scales, 2)) return LUTQ_EALIGN;
+    if ((!bcq && !it.lut) || !it.scales) return LUTQ_EINVAL;
+    if ((!bcq && !aligned(it.lut, 4)) || !aligned(it.scales, 2)) return LUTQ_EALIGN;
   }
   hipStream_t s = (hipStream_t)stream;
   if (K == 0) {  // the empty sum; x, the tables and the scales are not read
@@ -214,6 +216,7 @@ int run_matmul(const uint16_t* x, const lutq_matmul_item_t* items, int count, in
   if (!aligned(x, 16)) return LUTQ_EALIGN;
 
   plan(M, ntiles_all * lutq::kTileRows, K, cu_count(), &o);
+  if (bcq && o.path == LUTQ_PATH_MFMA) o.tiles = 2;
   const int path = kernel_path(o.path);
   const int ksplit = o.ksplit;
   const int rl = rows_per_launch(o.path);
@@ -248,6 +251,7 @@ int run_matmul(const uint16_t* x, const lutq_matmul_item_t* items, int count, in
   p.zp = zp;
   p.types = types;
   p.ntypes = ntypes;
+  p.bcq = bcq;
   p.N = p.seg[0].N;
   p.ntiles = p.seg[0].ntiles;
   p.nseg = nlive;
@@ -362,6 +366,17 @@ int lutq_matmul_typed(const uint16_t* x, const lutq_packed_t* packed, const uint
   if ((size_t)N * K > 0 && !types) return LUTQ_EINVAL;
   const lutq_matmul_item_t item = {packed, luts, scales, zeros, y};
   return run_matmul(x, &item, 1, M, K, opts, stream, types, ntypes);
+}
+
+int lutq_matmul_bcq(const uint16_t* x, const lutq_packed_t* packed, const uint16_t* alphas,
+                    uint16_t* y, int M, int N, int K, const lutq_options_t* opts, void* stream) {
+  int rc = check_desc(packed);
+  if (rc) return rc;
+  if (M < 0 || N < 0 || K < 0) return LUTQ_EINVAL;
+  if (N != packed->N || K != packed->K) return LUTQ_EMISMATCH;
+  if (packed->group == 0) return LUTQ_EGROUP;  // an alpha per plane, row and group
+  const lutq_matmul_item_t item = {packed, nullptr, alphas, nullptr, y};
+  return run_matmul(x, &item, 1, M, K, opts, stream, nullptr, 0, true);
 }
 
 int lutq_matmul_zp(const uint16_t* x, const lutq_packed_t* packed, const uint16_t* lut,

@@ -171,6 +171,45 @@ __device__ __forceinline__ uint32_t typed_lut_lane(const uint16_t* luts, int nty
   return luts[(t < ntypes ? t : 0) * L + (e & (L - 1))];
 }
 
+// Binary-coded weights: the entry of pair index idx holds, for each plane p
+// (p < BITS), the fp16 pair (bit_p(c0), bit_p(c1)) of 0.0 / 1.0 as dword p;
+// entries are 8 bytes (2 planes) or 16 (3 or 4), and the 256-byte row of
+// idx holds 256 / that many copies (lane l reads copy l mod copies).
+constexpr int kCopyBytes = 256;
+template <int BITS> constexpr int kBcqEntryBytes = BITS == 2 ? 8 : 16;
+
+template <int BITS>
+__device__ __forceinline__ u32x4 lds_load_bcq(const uint32_t* table, uint32_t byte_addr) {
+  const char* b = reinterpret_cast<const char*>(table) + byte_addr;
+  if constexpr (BITS == 2) {
+    const u32x2 v = *reinterpret_cast<const u32x2*>(b);
+    return u32x4{v.x, v.y, 0u, 0u};
+  } else {
+    return *reinterpret_cast<const u32x4*>(b);
+  }
+}
+
+template <int BITS, int THREADS>
+__device__ __forceinline__ void build_bcq_table(uint32_t* table, int tid) {
+  static_assert(THREADS % kPairEntries == 0, "whole threads per entry");
+  constexpr int kPerEntry = THREADS / kPairEntries;
+  constexpr int kStores = kCopyBytes / 16;                 // 16-byte stores per entry row
+  constexpr int C = kStores / kPerEntry;                    // stores per thread
+  static_assert(C >= 1 && (C & (C - 1)) == 0, "power-of-two stores per thread");
+  const uint32_t idx = (uint32_t)tid / kPerEntry;
+  const uint32_t part = (uint32_t)tid % kPerEntry;
+  uint32_t c0, c1;
+  pair_codes<BITS>(idx, c0, c1);
+  uint32_t d[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int pl = 0; pl < BITS; ++pl)
+    d[pl] = (((c0 >> pl) & 1u) ? 0x3C00u : 0u) | (((c1 >> pl) & 1u) ? 0x3C000000u : 0u);
+  const u32x4 q = BITS == 2 ? u32x4{d[0], d[1], d[0], d[1]} : u32x4{d[0], d[1], d[2], d[3]};
+  u32x4* dst = reinterpret_cast<u32x4*>(table) + idx * kStores + part * C;
+#pragma unroll
+  for (int k = 0; k < C; ++k) dst[(k + idx) & (C - 1)] = q;
+}
+
 // Fill the duplicated pair table. `lut_lane` holds T[lane] in lanes
 // 0..2^BITS-1 of every wave; entries are gathered with cross-lane reads.
 // THREADS / 256 threads share an entry: each computes the entry's value once

@@ -37,8 +37,8 @@ namespace lutq {
 // pipeline (PF - 1 chunks in flight while one is computed);
 // TPW: 16-row tiles per wave (and per workgroup); WAVES: waves per workgroup,
 // which split the K range; OCC: waves per SIMD the register budget targets.
-template <int BITS, bool MFMA, int MROWS, bool GROUPED, bool ZP, bool TYPED, int PF, int TPW, int WAVES,
-          int OCC>
+template <int BITS, bool MFMA, int MROWS, bool GROUPED, bool ZP, bool TYPED, bool BCQ, int PF, int TPW,
+          int WAVES, int OCC>
 __global__ __launch_bounds__(WAVES * kWave) __attribute__((amdgpu_waves_per_eu(OCC)))
 void matmul_kernel(const MatmulParams pk) {
   // A fused launch covers several matrices: this workgroup's row block picks
@@ -63,6 +63,11 @@ void matmul_kernel(const MatmulParams pk) {
   }
   constexpr int kThreads = WAVES * kWave;
   constexpr int kWaves = WAVES;
+  // Binary-coded weights: BITS planes, one alpha stream per plane in place
+  // of the scales, and plane sums (zero points' activation sums included).
+  static_assert(!BCQ || (GROUPED && !ZP && !TYPED), "binary coding has its own parameters");
+  constexpr int QS = BCQ ? BITS : 1;      // scale-like streams (alpha planes)
+  constexpr bool XSUM = ZP || BCQ;        // needs the groups' activation sums
   constexpr int ROWS = TPW * kTileRows;
   constexpr int MT = MFMA ? MROWS / 16 : 1;
   constexpr int SLOT = 4 * BITS;
@@ -85,13 +90,18 @@ void matmul_kernel(const MatmulParams pk) {
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r = lane & 15, q = lane >> 4;
-  const uint32_t lane_byte = (uint32_t)lane << 2;
+  // LDS lane byte: this lane's copy of every table entry (BCQ entries are
+  // 8 or 16 bytes, kBcqEntryBytes<BITS>, with 256 / that many copies)
+  const uint32_t lane_byte =
+      BCQ ? ((uint32_t)lane & (kCopyBytes / kBcqEntryBytes<BITS> - 1)) * kBcqEntryBytes<BITS>
+          : (uint32_t)lane << 2;
 
   // The table values, one per lane (lanes >= 2^BITS repeat the table).
   // Read with wave-uniform (scalar) loads: they do not queue behind the
   // vector loads of the code stream, so the LDS table is ready early.
-  const uint32_t lut_lane =
-      TYPED ? typed_lut_lane<BITS>(p.lut, p.ntypes, lane) : lut_to_lanes<BITS>(p.lut, lane);
+  uint32_t lut_lane = 0;
+  if constexpr (TYPED) lut_lane = typed_lut_lane<BITS>(p.lut, p.ntypes, lane);
+  else if constexpr (!BCQ) lut_lane = lut_to_lanes<BITS>(p.lut, lane);
 
   const int rb = blockIdx.x / p.ksplit;            // row block of the launch (split-K slots)
   const int ks = blockIdx.x - rb * p.ksplit;
@@ -135,8 +145,12 @@ void matmul_kernel(const MatmulParams pk) {
   // per-step load touches 16 cache lines, one per row, for 32 bytes).
   const int row0 = tile0 * kTileRows;
   const uint32_t rows_here = (uint32_t)min(ROWS, p.N - row0);
-  const __amdgpu_buffer_rsrc_t srsrc =
-      make_rsrc(p.scales + (size_t)row0 * gpr, GROUPED ? rows_here * (uint32_t)gpr * 2u : 0u);
+  // (binary coding: plane p's alphas [N][groups] follow plane p - 1's)
+  __amdgpu_buffer_rsrc_t srsrc[QS];
+#pragma unroll
+  for (int pl = 0; pl < QS; ++pl)
+    srsrc[pl] = make_rsrc(p.scales + ((size_t)pl * p.N + row0) * gpr,
+                          GROUPED ? rows_here * (uint32_t)gpr * 2u : 0u);
   uint32_t soff[TPW];
 #pragma unroll
   for (int t = 0; t < TPW; ++t) soff[t] = 2u * (uint32_t)(t * kTileRows + r) * (uint32_t)gpr;
@@ -169,7 +183,7 @@ void matmul_kernel(const MatmulParams pk) {
                                   : kRowOutOfRange;
 
   SlotRegs<BITS> cbuf[PF][TPW];
-  uint32_t scur[TPW], snext[TPW];  // scale batches: in use, in flight
+  uint32_t scur[QS][TPW], snext[QS][TPW];  // scale (alpha) batches: in use, in flight
   uint32_t zcur[ZP ? TPW : 1], znext[ZP ? TPW : 1];  // zero-point batches
   uint32_t tcur[TYPED ? TPW : 1], tnext[TYPED ? TPW : 1];  // type-id batches
   uint32_t xbuf[PF][MFMA ? 1 : MROWS];
@@ -208,8 +222,10 @@ void matmul_kernel(const MatmulParams pk) {
     uint32_t sb = kOutOfRange;
     if (c >= 0) sb = 2u * (cpg == 1 ? (uint32_t)c : (uint32_t)c / (uint32_t)cpg);
 #pragma unroll
-    for (int t = 0; t < TPW; ++t)
-      snext[t] = __builtin_amdgcn_raw_buffer_load_b16(srsrc, soff[t] + sb, 0, 0);
+    for (int pl = 0; pl < QS; ++pl)
+#pragma unroll
+      for (int t = 0; t < TPW; ++t)
+        snext[pl][t] = __builtin_amdgcn_raw_buffer_load_b16(srsrc[pl], soff[t] + sb, 0, 0);
     if constexpr (ZP) {
 #pragma unroll
       for (int t = 0; t < TPW; ++t)
@@ -223,8 +239,8 @@ void matmul_kernel(const MatmulParams pk) {
     }
   };
   // the scale of this lane's row at step position u (0 .. SB-1) of the batch
-  auto step_scale = [&](int t, int u) __attribute__((always_inline)) {
-    const int v = __builtin_amdgcn_ds_bpermute((16 * u + r) * 4, (int)scur[t]);
+  auto step_scale = [&](int t, int u, int pl = 0) __attribute__((always_inline)) {
+    const int v = __builtin_amdgcn_ds_bpermute((16 * u + r) * 4, (int)scur[pl][t]);
     return f16_bits_to_f32((uint16_t)v);
   };
   // the LDS lane byte of tile t at step position u: this lane's copy, and
@@ -258,11 +274,14 @@ void matmul_kernel(const MatmulParams pk) {
     constexpr int u = decltype(B)::value;  // position in the scale batch
     if constexpr (!MFMA) {
       // k-step outer, tile inner: each activation broadcast serves all tiles
-      float cs[TPW][MROWS];
+      // (binary coding: one partial sum per plane)
+      float cs[QS][TPW][MROWS];
 #pragma unroll
-      for (int t = 0; t < TPW; ++t)
+      for (int pl = 0; pl < QS; ++pl)
 #pragma unroll
-        for (int m = 0; m < MROWS; ++m) cs[t][m] = 0.f;
+        for (int t = 0; t < TPW; ++t)
+#pragma unroll
+          for (int m = 0; m < MROWS; ++m) cs[pl][t][m] = 0.f;
       uint32_t lbt[TPW];
 #pragma unroll
       for (int t = 0; t < TPW; ++t) lbt[t] = step_lane_byte(t, u);
@@ -273,40 +292,62 @@ void matmul_kernel(const MatmulParams pk) {
         for (int t = 0; t < TPW; ++t) idx4[t] = step_indices<BITS>(cbuf[s][t], j);
 #pragma unroll
         for (int t = 0; t < TPW; ++t) {
-          uint32_t pr[4];
+          if constexpr (!BCQ) {
+            uint32_t pr[4];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) pr[i] = lds_load(table, pair_addr(idx4[t], lbt[t], i));
-          // pair i of k-step j meets the activations of lane 4j+i of the row
+            for (int i = 0; i < 4; ++i) pr[i] = lds_load(table, pair_addr(idx4[t], lbt[t], i));
+            // pair i of k-step j meets the activations of lane 4j+i of the row
 #pragma unroll
-          for (int m = 0; m < MROWS; ++m)
-            cs[t][m] = dot2_bcast4(cs[t][m], xbuf[s][m], pr[0], pr[1], pr[2], pr[3], j);
+            for (int m = 0; m < MROWS; ++m)
+              cs[0][t][m] = dot2_bcast4(cs[0][t][m], xbuf[s][m], pr[0], pr[1], pr[2], pr[3], j);
+          } else {
+            // one entry per pair holds every plane's (bit, bit) pair
+            u32x4 pw[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) pw[i] = lds_load_bcq<BITS>(table, pair_addr(idx4[t], lbt[t], i));
+#pragma unroll
+            for (int pl = 0; pl < QS; ++pl)
+#pragma unroll
+              for (int m = 0; m < MROWS; ++m)
+                cs[pl][t][m] = dot2_bcast4(cs[pl][t][m], xbuf[s][m], pw[0][pl], pw[1][pl], pw[2][pl],
+                                           pw[3][pl], j);
+          }
         }
       }
       // Zero points: lane row q multiplied the activations of the 16 lanes of
       // its row (k = 32j + 8q + e), so its share of the group's activation
       // sum is the sum over that row (a butterfly: every lane gets the same
       // value), computed once for all tiles.
-      float xq[ZP ? MROWS : 1];
-      if constexpr (ZP) {
+      float xq[XSUM ? MROWS : 1];
+      if constexpr (XSUM) {
 #pragma unroll
         for (int m = 0; m < MROWS; ++m) xq[m] = row_sum16(pair_sum(xbuf[s][m]));
       }
 #pragma unroll
       for (int t = 0; t < TPW; ++t) {
-        if constexpr (GROUPED) {
+        if constexpr (BCQ) {
+          // sum_k x (2 bit_p - 1) = 2 S_p - X per plane, times its alpha
+#pragma unroll
+          for (int pl = 0; pl < QS; ++pl) {
+            const float a = step_scale(t, u, pl);
+#pragma unroll
+            for (int m = 0; m < MROWS; ++m)
+              gacc[t][m] = __builtin_fmaf(a, __builtin_fmaf(2.f, cs[pl][t][m], -xq[m]), gacc[t][m]);
+          }
+        } else if constexpr (GROUPED) {
           const float sc = step_scale(t, u);
           if constexpr (ZP) {
             const float z = step_zero(t, u);
 #pragma unroll
             for (int m = 0; m < MROWS; ++m)
-              gacc[t][m] = __builtin_fmaf(sc, __builtin_fmaf(-z, xq[m], cs[t][m]), gacc[t][m]);
+              gacc[t][m] = __builtin_fmaf(sc, __builtin_fmaf(-z, xq[m], cs[0][t][m]), gacc[t][m]);
           } else {
 #pragma unroll
-            for (int m = 0; m < MROWS; ++m) gacc[t][m] = __builtin_fmaf(sc, cs[t][m], gacc[t][m]);
+            for (int m = 0; m < MROWS; ++m) gacc[t][m] = __builtin_fmaf(sc, cs[0][t][m], gacc[t][m]);
           }
         } else {
 #pragma unroll
-          for (int m = 0; m < MROWS; ++m) gacc[t][m] += cs[t][m];
+          for (int m = 0; m < MROWS; ++m) gacc[t][m] += cs[0][t][m];
         }
       }
     } else {
@@ -325,12 +366,12 @@ void matmul_kernel(const MatmulParams pk) {
           dst[j].w = lds_load(table, pair_addr(idx4, lb, 3));
         }
       };
-      lookup(0, bq[0]);
+      if constexpr (!BCQ) lookup(0, bq[0]);
       // Zero points: the group's activation sums, in the accumulator layout
       // (a B operand of ones gives C[m][n] = sum_k x[m][k] in every column),
       // once for all tiles.
-      f32x4 xs[ZP ? MT : 1];
-      if constexpr (ZP) {
+      f32x4 xs[XSUM ? MT : 1];
+      if constexpr (XSUM) {
         const f16x8 ones = {1, 1, 1, 1, 1, 1, 1, 1};
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
@@ -340,6 +381,43 @@ void matmul_kernel(const MatmulParams pk) {
             xs[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
                 __builtin_bit_cast(f16x8, abuf[s][mt][j]), ones, xs[mt], 0, 0, 0);
         }
+      }
+      if constexpr (BCQ) {
+        // Binary coding: the entry of each pair carries every plane's
+        // (bit, bit) pair; plane p's four pairs of k-step j are its B
+        // operand. No lookahead (the planes' operands take the registers).
+#pragma unroll
+        for (int t = 0; t < TPW; ++t) {
+          const uint32_t lb = step_lane_byte(t, u);
+          f32x4 cg[QS][MT];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const uint32_t idx4 = step_indices<BITS>(cbuf[s][t], j);
+            u32x4 pw[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) pw[i] = lds_load_bcq<BITS>(table, pair_addr(idx4, lb, i));
+#pragma unroll
+            for (int pl = 0; pl < QS; ++pl) {
+              const f16x8 b = __builtin_bit_cast(f16x8, u32x4{pw[0][pl], pw[1][pl], pw[2][pl], pw[3][pl]});
+#pragma unroll
+              for (int mt = 0; mt < MT; ++mt)
+                cg[pl][mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                    __builtin_bit_cast(f16x8, abuf[s][mt][j]), b,
+                    j == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : cg[pl][mt], 0, 0, 0);
+            }
+          }
+#pragma unroll
+          for (int pl = 0; pl < QS; ++pl) {
+            const float a = step_scale(t, u, pl);
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                macc[t][mt][e] = __builtin_fmaf(a, __builtin_fmaf(2.f, cg[pl][mt][e], -xs[mt][e]),
+                                                macc[t][mt][e]);
+          }
+        }
+        return;
       }
 #pragma unroll
       for (int t = 0; t < TPW; ++t) {
@@ -392,7 +470,8 @@ void matmul_kernel(const MatmulParams pk) {
   if constexpr (GROUPED) issue_scales(0);
   static_for<PF - 1>([&](auto S) { issue(S, chunk(decltype(S)::value)); });
 
-  build_pair_table<BITS, kThreads, TYPED>(table, lut_lane, tid);
+  if constexpr (BCQ) build_bcq_table<BITS, kThreads>(table, tid);
+  else build_pair_table<BITS, kThreads, TYPED>(table, lut_lane, tid);
   __syncthreads();
 
   // One step at position u of a U-step group starting at i0. Steps past the
@@ -406,7 +485,9 @@ void matmul_kernel(const MatmulParams pk) {
     const int i = i0 + u;
     if constexpr (GROUPED && u % SB == 0) {
 #pragma unroll
-      for (int t = 0; t < TPW; ++t) scur[t] = snext[t];
+      for (int pl = 0; pl < QS; ++pl)
+#pragma unroll
+        for (int t = 0; t < TPW; ++t) scur[pl][t] = snext[pl][t];
       if constexpr (ZP) {
 #pragma unroll
         for (int t = 0; t < TPW; ++t) zcur[t] = znext[t];
@@ -529,16 +610,28 @@ static hipError_t launch_t(const MatmulParams& p, hipStream_t s) {
   // workgroups that one wave per SIMD costs little.
   constexpr int OCC_G = (MFMA && MROWS == 32 && TPW == 8) ? 1 : OCC;
   const dim3 block(WAVES * kWave);
-  if (p.group == 0)
-    matmul_kernel<BITS, MFMA, MROWS, false, false, false, kPf, TPW, WAVES, OCC><<<grid, block, 0, s>>>(p);
+  if (p.bcq) {
+    // binary-coded weights: GEMV shapes and the 2-tile MFMA shape only
+    if constexpr (!MFMA || TPW == 2)
+      matmul_kernel<BITS, MFMA, MROWS, true, false, false, true, kPf, TPW, WAVES, OCC_G>
+          <<<grid, block, 0, s>>>(p);
+    else
+      return hipErrorInvalidValue;
+  } else if (p.group == 0)
+    matmul_kernel<BITS, MFMA, MROWS, false, false, false, false, kPf, TPW, WAVES, OCC>
+        <<<grid, block, 0, s>>>(p);
   else if (p.types && p.zp)
-    matmul_kernel<BITS, MFMA, MROWS, true, true, true, kPf, TPW, WAVES, OCC_G><<<grid, block, 0, s>>>(p);
+    matmul_kernel<BITS, MFMA, MROWS, true, true, true, false, kPf, TPW, WAVES, OCC_G>
+        <<<grid, block, 0, s>>>(p);
   else if (p.types)
-    matmul_kernel<BITS, MFMA, MROWS, true, false, true, kPf, TPW, WAVES, OCC_G><<<grid, block, 0, s>>>(p);
+    matmul_kernel<BITS, MFMA, MROWS, true, false, true, false, kPf, TPW, WAVES, OCC_G>
+        <<<grid, block, 0, s>>>(p);
   else if (p.zp)
-    matmul_kernel<BITS, MFMA, MROWS, true, true, false, kPf, TPW, WAVES, OCC_G><<<grid, block, 0, s>>>(p);
+    matmul_kernel<BITS, MFMA, MROWS, true, true, false, false, kPf, TPW, WAVES, OCC_G>
+        <<<grid, block, 0, s>>>(p);
   else
-    matmul_kernel<BITS, MFMA, MROWS, true, false, false, kPf, TPW, WAVES, OCC_G><<<grid, block, 0, s>>>(p);
+    matmul_kernel<BITS, MFMA, MROWS, true, false, false, false, kPf, TPW, WAVES, OCC_G>
+        <<<grid, block, 0, s>>>(p);
   return hipGetLastError();
 }
 
