@@ -34,6 +34,7 @@ from .lutq_ref import (  # noqa: F401
     dequant_bcq,
     reference_bcq,
     error_bound,
+    error_bound_bf16,
     check,
 )
 from . import quantize  # noqa: F401

@@ -201,9 +201,22 @@ def error_bound(B: np.ndarray) -> np.ndarray:
     return REL_TOL * B + ABS_TOL
 
 
-def check(y: np.ndarray, y_ref: np.ndarray, B: np.ndarray):
-    """(ok, worst): ok when every |y - y_ref| <= error_bound(B); worst is max(err / bound)."""
+BF16_UNIT_ROUNDOFF = 2.0 ** -8
+
+
+def error_bound_bf16(B: np.ndarray, y_ref: np.ndarray) -> np.ndarray:
+    """Tolerance for bf16 outputs: the fp16-output bound plus the rounding of
+    the fp32 result to bf16 (8 significand bits: at most 2^-8 |y| relative,
+    applied to |y_ref| plus the accumulation bound)."""
+    acc = REL_TOL * B + ABS_TOL
+    return acc + BF16_UNIT_ROUNDOFF * (np.abs(y_ref) + acc)
+
+
+def check(y: np.ndarray, y_ref: np.ndarray, B: np.ndarray, out: str = "fp16"):
+    """(ok, worst): ok when every |y - y_ref| <= the bound (error_bound(B), or
+    error_bound_bf16 for bf16 outputs); worst is max(err / bound)."""
     err = np.abs(y.astype(np.float64) - y_ref)
-    ratio = err / error_bound(B)
+    bound = error_bound(B) if out == "fp16" else error_bound_bf16(B, y_ref)
+    ratio = err / bound
     worst = float(ratio.max()) if ratio.size else 0.0
     return bool(np.all(np.isfinite(y)) and worst <= 1.0), worst

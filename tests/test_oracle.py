@@ -461,3 +461,24 @@ def test_planted_bcq_mistakes_are_caught(monkeypatch, kind):
     monkeypatch.setattr(lutq_ref, "dequant_bcq", bad)
     y, _ = oracle.reference_bcq(x, c, a, 128)
     assert max(abs(y[m, n] - float(ex[m][n])) for m in range(2) for n in range(3)) > 1e-6
+
+
+# -- bf16 outputs ------------------------------------------------------------
+
+def _to_bf16(v):
+    """fp64 -> the nearest bf16 value (ties to even), as fp64; exact via the fp32 bits."""
+    f = np.asarray(v, np.float32).view(np.uint32).astype(np.uint64)
+    r = ((f + 0x7FFF + ((f >> 16) & 1)) >> 16) << 16
+    return r.astype(np.uint32).view(np.float32).astype(np.float64)
+
+
+def test_bf16_bound_covers_output_rounding_only():
+    # the exact product rounded once to bf16 passes; two bf16 steps off fails
+    c, T, s, x = workloads.small_case(4, "nf", 128, 3, 40, 512, seed=60)
+    y, B = oracle.reference(x, c, T, s, 128)
+    yb = _to_bf16(y)
+    assert oracle.check(yb, y, B, out="bf16")[0]
+    big = np.abs(y) > 50 * oracle.error_bound(B)       # where rounding dominates the bound
+    bad = yb.copy()
+    bad[big] = bad[big] * (1 + 2 * 2.0 ** -7)
+    assert not oracle.check(bad, y, B, out="bf16")[0]
