@@ -161,14 +161,18 @@ class VariantCase(Case):
         luts = np.stack([T] + [tables.make(k, self.w.bits) for k in ("nf", "lloyd_max", "log")])
         ty = rng.integers(0, 4, s.shape).astype(np.uint8)
         self.zeros, self.luts, self.types = (torch.from_numpy(a).cuda() for a in (z, luts, ty))
+        self.x_bf16 = self.x.to(torch.bfloat16)
+        self.y_bf16 = torch.empty_like(self.y, dtype=torch.bfloat16)
         self.base_bytes = self.bytes
-        self.extra_bytes = {"plain": 0, "zeros": z.nbytes, "types": ty.nbytes + luts.nbytes}
+        self.extra_bytes = {"plain": 0, "zeros": z.nbytes, "types": ty.nbytes + luts.nbytes, "bf16": 0}
         self.mode = "plain"
 
     def call(self, lutq, i):
         P = self.packed[i % len(self.packed)]
         if self.mode == "types":
             lutq.matmul(self.x, P, self.luts, self.scales, types=self.types, out=self.y)
+        elif self.mode == "bf16":
+            lutq.matmul(self.x_bf16, P, self.lut, self.scales, out=self.y_bf16)
         else:
             lutq.matmul(self.x, P, self.lut, self.scales,
                         zeros=self.zeros if self.mode == "zeros" else None, out=self.y)
@@ -209,15 +213,15 @@ class BcqCase:
 
 
 def variant_section(lutq, torch, args):
-    """Per-group zero points, per-group data types (four tables) and
-    binary-coded weights (q = 3) on the headline matrix's shape at batch 1
-    and 16, against the plain launch (cold)."""
+    """bf16 activations, per-group zero points, per-group data types (four
+    tables) and binary-coded weights (q = 3) on the headline matrix's shape
+    at batch 1 and 16, against the plain launch (cold)."""
     out = {}
     steps = max(20, args.steps // 4)
     for M in (1, 16):
         vc = VariantCase(lutq, torch, "int4_up_proj", None, M)
         rec = {}
-        for mode in ("plain", "zeros", "types"):
+        for mode in ("plain", "bf16", "zeros", "types"):
             vc.mode = mode
             us = time_case(lutq, torch, vc, steps, args.warmup)
             nbytes = vc.base_bytes + vc.extra_bytes[mode]

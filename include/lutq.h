@@ -150,8 +150,22 @@ typedef struct lutq_options {
                      16 * tiles rows); 0 = automatic. Needs an explicit
                      path: GEMV takes 1 or 2, MFMA 2, 4 or 8; anything
                      else gives LUTQ_EINVAL.                                 */
-  int32_t reserved[5]; /* must be zero                                        */
+  int32_t dtype;  /* activations x and output y: LUTQ_DTYPE_F16 (0) or
+                     LUTQ_DTYPE_BF16 (1); bf16 works with plain tables
+                     (lutq_matmul_ex, lutq_matmul_multi without zero
+                     points) and gives LUTQ_EUNSUPPORTED with zero points,
+                     data types or binary coding.                            */
+  int32_t reserved[4]; /* must be zero                                        */
 } lutq_options_t;
+
+/* Activation dtypes (lutq_options_t.dtype). bf16 activations are converted
+ * on chip per (batch row, 128-weight chunk): scaled by a power of two that
+ * puts the chunk's largest magnitude in [2^14, 2^15), every bf16 value
+ * within 2^31 of it is exactly an fp16 value, so the fp16 arithmetic runs
+ * unchanged and the chunk's partial sums are scaled back exactly. Values
+ * smaller than 2^-31 of their chunk's largest lose bits. y is bf16, rounded
+ * to nearest even from the fp32 result. */
+enum { LUTQ_DTYPE_F16 = 0, LUTQ_DTYPE_BF16 = 1 };
 
 /* lutq_matmul with explicit options (host pointer; NULL = automatic). */
 int lutq_matmul_ex(const uint16_t* x, const lutq_packed_t* packed, const uint16_t* lut,

@@ -123,6 +123,18 @@ def test_matmul_validates_before_launching(lib):
     assert call(opts=ctypes.byref(o)) == EINVAL
     o = _lib.Options(); o.reserved[3] = 1
     assert call(opts=ctypes.byref(o)) == EINVAL
+    o = _lib.Options(); o.dtype = 2
+    assert call(opts=ctypes.byref(o)) == EINVAL
+    # bf16 activations run plain tables only
+    o = _lib.Options(); o.dtype = 1
+    z, ty = P(0x5000), P(0x6000)
+    assert lib.lutq_matmul_zp(x, ctypes.byref(d), lut, sc, z, y, 1, 64, 256, ctypes.byref(o),
+                              None) == EUNSUP
+    assert lib.lutq_matmul_typed(x, ctypes.byref(d), lut, 2, ty, sc, None, y, 1, 64, 256,
+                                 ctypes.byref(o), None) == EUNSUP
+    d3 = _desc(bits=3)
+    assert lib.lutq_matmul_bcq(x, ctypes.byref(d3), sc, y, 1, 64, 256, ctypes.byref(o),
+                               None) == EUNSUP
     for path, tiles in [(0, 2), (1, 8), (1, 4), (2, 1), (2, 3), (1, -1)]:
         o = _lib.Options(); o.path, o.tiles = path, tiles
         assert call(opts=ctypes.byref(o)) == EINVAL, (path, tiles)

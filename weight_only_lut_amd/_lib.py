@@ -44,7 +44,8 @@ class PackedDesc(ctypes.Structure):
 
 class Options(ctypes.Structure):
     _fields_ = [("path", ctypes.c_int32), ("ksplit", ctypes.c_int32),
-                ("tiles", ctypes.c_int32), ("reserved", ctypes.c_int32 * 5)]
+                ("tiles", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("reserved", ctypes.c_int32 * 4)]
 
 
 class MatmulItem(ctypes.Structure):
@@ -132,12 +133,24 @@ def packed_bytes(N: int, K: int, bits: int, group: int) -> int:
     return int(_lib().lutq_packed_bytes(N, K, bits, group))
 
 
-def _options(path: str, ksplit: int, tiles: int) -> Options:
+DTYPE_F16, DTYPE_BF16 = 0, 1
+
+
+def _options(path: str, ksplit: int, tiles: int, dtype: int = DTYPE_F16) -> Options:
     o = Options()
     o.path = _PATHS[path]
     o.ksplit = ksplit
     o.tiles = tiles
+    o.dtype = dtype
     return o
+
+
+def _act_dtype(x):
+    """(torch dtype, lutq dtype) of fp16 or bf16 activations."""
+    import torch
+    if isinstance(x, torch.Tensor) and x.dtype == torch.bfloat16:
+        return torch.bfloat16, DTYPE_BF16
+    return torch.float16, DTYPE_F16
 
 
 def plan(M: int, N: int, K: int, bits: int, *, path: str = "auto", ksplit: int = 0,
@@ -215,17 +228,18 @@ def matmul(x, p: Packed, lut, scales, *, zeros=None, types=None, path: str = "au
     ``types``, uint8 [N, K/group], and ``lut`` fp16 [ntypes, 2^bits]):
     y[M, N] = x[M, K] . dequant(p, lut, scales[, zeros][, types])^T, fp16 out."""
     import torch
-    _need_cuda(x, "x", torch.float16)
+    tdt, ldt = _act_dtype(x)
+    _need_cuda(x, "x", tdt)
     _need_cuda(lut, "lut", torch.float16)
     _need_cuda(scales, "scales", torch.float16)
     M, K = x.shape
     if out is None:
-        out = torch.empty((M, p.N), dtype=torch.float16, device=x.device)
+        out = torch.empty((M, p.N), dtype=tdt, device=x.device)
     else:
-        _need_cuda(out, "out", torch.float16)
+        _need_cuda(out, "out", tdt)
         if tuple(out.shape) != (M, p.N):
             raise ValueError("out has the wrong shape")
-    opts = _options(path, ksplit, tiles)
+    opts = _options(path, ksplit, tiles, ldt)
     if types is not None:
         _need_cuda(types, "types", torch.uint8)
         if zeros is not None:
@@ -252,7 +266,8 @@ def matmul_multi(x, mats, *, path: str = "auto", ksplit: int = 0, tiles: int = 0
     matrices sharing x: ``mats`` is a list of (Packed, lut, scales) or
     (Packed, lut, scales, zeros); returns the list of fp16 outputs y_i [M, N_i]."""
     import torch
-    _need_cuda(x, "x", torch.float16)
+    tdt, ldt = _act_dtype(x)
+    _need_cuda(x, "x", tdt)
     M, K = x.shape
     if not 1 <= len(mats) <= MAX_FUSED:
         raise ValueError(f"1 to {MAX_FUSED} matrices per fused launch")
@@ -267,16 +282,16 @@ def matmul_multi(x, mats, *, path: str = "auto", ksplit: int = 0, tiles: int = 0
             _need_cuda(zeros, "zeros", torch.float16)
             items[i].zeros = zeros.data_ptr()
         if outs is None:
-            y = torch.empty((M, p.N), dtype=torch.float16, device=x.device)
+            y = torch.empty((M, p.N), dtype=tdt, device=x.device)
         else:
             y = outs[i]
-            _need_cuda(y, "out", torch.float16)
+            _need_cuda(y, "out", tdt)
             if tuple(y.shape) != (M, p.N):
                 raise ValueError("out has the wrong shape")
         ys.append(y)
         items[i].packed = ctypes.pointer(p.desc)
         items[i].lut, items[i].scales, items[i].y = lut.data_ptr(), scales.data_ptr(), y.data_ptr()
-    opts = _options(path, ksplit, tiles)
+    opts = _options(path, ksplit, tiles, ldt)
     rc = _lib().lutq_matmul_multi(_ptr(x), items, len(mats), M, K, ctypes.byref(opts),
                                   _stream(x.device))
     if rc:

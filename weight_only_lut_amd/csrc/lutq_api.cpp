@@ -117,8 +117,9 @@ constexpr int kSplitChunks = 32;     // chunks per split, at least
 int read_options(const lutq_options_t* opts, lutq_options_t* o) {
   std::memset(o, 0, sizeof *o);
   if (!opts) return LUTQ_OK;
-  for (int i = 0; i < 5; ++i)
+  for (int i = 0; i < 4; ++i)
     if (opts->reserved[i]) return LUTQ_EINVAL;
+  if (opts->dtype != LUTQ_DTYPE_F16 && opts->dtype != LUTQ_DTYPE_BF16) return LUTQ_EINVAL;
   if (opts->path < LUTQ_PATH_AUTO || opts->path > LUTQ_PATH_MFMA || opts->ksplit < 0 ||
       opts->tiles < 0)
     return LUTQ_EINVAL;
@@ -180,6 +181,8 @@ int run_matmul(const uint16_t* x, const lutq_matmul_item_t* items, int count, in
   if (rc) return rc;
   // binary-coded weights run the GEMV shapes and the 2-tile MFMA shape
   if (bcq && o.path == LUTQ_PATH_MFMA && o.tiles != 0 && o.tiles != 2) return LUTQ_EINVAL;
+  const bool bf16 = o.dtype == LUTQ_DTYPE_BF16;
+  if (bf16 && (bcq || types)) return LUTQ_EUNSUPPORTED;
   int live[LUTQ_MAX_FUSED];
   int nlive = 0, ntiles_all = 0;
   for (int i = 0; i < count; ++i) {
@@ -195,6 +198,7 @@ int run_matmul(const uint16_t* x, const lutq_matmul_item_t* items, int count, in
     if (!it.y) return LUTQ_EINVAL;
     if (!aligned(it.y, 2)) return LUTQ_EALIGN;
     if (it.zeros) {
+      if (bf16) return LUTQ_EUNSUPPORTED;
       if (it.packed->group == 0) return LUTQ_EGROUP;  // zero points are per group
       if (!aligned(it.zeros, 2)) return LUTQ_EALIGN;
       zp = true;
@@ -252,6 +256,7 @@ int run_matmul(const uint16_t* x, const lutq_matmul_item_t* items, int count, in
   p.types = types;
   p.ntypes = ntypes;
   p.bcq = bcq;
+  p.bf16 = bf16;
   p.N = p.seg[0].N;
   p.ntiles = p.seg[0].ntiles;
   p.nseg = nlive;

@@ -317,6 +317,23 @@ __device__ __forceinline__ float dpp_f32(float v) {
       float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
 }
 
+// Maximum over the 64 lanes of the wave.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  auto dm = [](uint32_t a, auto ctrl) {
+    constexpr int C = decltype(ctrl)::value;
+    const uint32_t b = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)a, C, 0xF, 0xF, false);
+    return a > b ? a : b;
+  };
+  v = dm(v, std::integral_constant<int, 0xB1>{});   // quad_perm [1,0,3,2]
+  v = dm(v, std::integral_constant<int, 0x4E>{});   // quad_perm [2,3,0,1]
+  v = dm(v, std::integral_constant<int, 0x141>{});  // row_half_mirror
+  v = dm(v, std::integral_constant<int, 0x140>{});  // row_mirror
+  const uint32_t a = (uint32_t)__shfl_xor((int)v, 16);
+  v = v > a ? v : a;
+  const uint32_t b = (uint32_t)__shfl_xor((int)v, 32);
+  return v > b ? v : b;
+}
+
 // Sum over the 16 lanes of a row as a butterfly (partners under xor 1, 2,
 // then the mirrored half and quarter rows): every addition is a + b in one
 // lane and b + a in its partner, so all 16 lanes end with the same bits.
@@ -326,6 +343,31 @@ __device__ __forceinline__ float row_sum16(float v) {
   v += dpp_f32<0x141>(v);  // row_half_mirror: quads 0 <-> 1 of each half row
   v += dpp_f32<0x140>(v);  // row_mirror: halves of the row
   return v;
+}
+
+// fp32 -> bf16 bits, round to nearest even (NaN stays a quiet NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x40u);
+  return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+
+// bf16 activations are converted per (batch row, 128-weight chunk): scaled
+// by a power of two that puts the chunk's largest magnitude in [2^14, 2^15),
+// every value within 2^31 of it is an exact fp16 value, so the fp16 dot and
+// MFMA arithmetic runs unchanged and the chunk's partial sums are scaled
+// back by the inverse power of two (exact). `amax` holds the largest bf16
+// magnitude (bits & 0x7FFF) of the chunk; the shift is 141 - exponent field.
+__device__ __forceinline__ int bf16_chunk_shift(uint32_t amax) { return 141 - (int)(amax >> 7); }
+__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t v, int shift) {
+  const float lo = __builtin_ldexpf(__builtin_bit_cast(float, v << 16), shift);
+  const float hi = __builtin_ldexpf(__builtin_bit_cast(float, v & 0xFFFF0000u), shift);
+  // exact values: the rounding mode of the pack does not matter
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));
+}
+__device__ __forceinline__ uint32_t bf16x2_absmax(uint32_t v) {
+  const uint32_t a = v & 0x7FFFu, b = (v >> 16) & 0x7FFFu;
+  return a > b ? a : b;
 }
 
 __device__ __forceinline__ float f16_bits_to_f32(uint16_t h) {

@@ -38,6 +38,7 @@ struct MatmulParams {
   int cps;                // chunks per split
   bool zp;                // zero points in this launch (any matrix); grouped only
   bool bcq;               // binary-coded weights: scales = alphas [BITS][N][K/group], no table
+  bool bf16;              // x and y are bf16 (plain tables only)
   const uint8_t* types;   // per-group data type ids [N, K/group], or null (one table)
   int ntypes;             // tables at lut ([ntypes][2^bits]) when types is set
   // Fused launch (nseg > 1): matrices sharing x, K, bits and group; the

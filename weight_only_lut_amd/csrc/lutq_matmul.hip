@@ -37,8 +37,8 @@ namespace lutq {
 // pipeline (PF - 1 chunks in flight while one is computed);
 // TPW: 16-row tiles per wave (and per workgroup); WAVES: waves per workgroup,
 // which split the K range; OCC: waves per SIMD the register budget targets.
-template <int BITS, bool MFMA, int MROWS, bool GROUPED, bool ZP, bool TYPED, bool BCQ, int PF, int TPW,
-          int WAVES, int OCC>
+template <int BITS, bool MFMA, int MROWS, bool GROUPED, bool ZP, bool TYPED, bool BCQ, bool BF16, int PF,
+          int TPW, int WAVES, int OCC>
 __global__ __launch_bounds__(WAVES * kWave) __attribute__((amdgpu_waves_per_eu(OCC)))
 void matmul_kernel(const MatmulParams pk) {
   // A fused launch covers several matrices: this workgroup's row block picks
@@ -66,6 +66,7 @@ void matmul_kernel(const MatmulParams pk) {
   // Binary-coded weights: BITS planes, one alpha stream per plane in place
   // of the scales, and plane sums (zero points' activation sums included).
   static_assert(!BCQ || (GROUPED && !ZP && !TYPED), "binary coding has its own parameters");
+  static_assert(!BF16 || (!ZP && !TYPED && !BCQ), "bf16 activations: plain tables only");
   constexpr int QS = BCQ ? BITS : 1;      // scale-like streams (alpha planes)
   constexpr bool XSUM = ZP || BCQ;        // needs the groups' activation sums
   constexpr int ROWS = TPW * kTileRows;
@@ -273,6 +274,17 @@ void matmul_kernel(const MatmulParams pk) {
     constexpr int s = decltype(S)::value;
     constexpr int u = decltype(B)::value;  // position in the scale batch
     if constexpr (!MFMA) {
+      // bf16 activations: this chunk of each batch row (one pair per lane)
+      // to fp16 under the chunk's power-of-two shift; fm undoes it
+      float fm[BF16 ? MROWS : 1];
+      if constexpr (BF16) {
+#pragma unroll
+        for (int m = 0; m < MROWS; ++m) {
+          const int sh = bf16_chunk_shift(wave_max_u32(bf16x2_absmax(xbuf[s][m])));
+          xbuf[s][m] = bf16x2_to_f16x2(xbuf[s][m], sh);
+          fm[m] = __builtin_ldexpf(1.f, -sh);
+        }
+      }
       // k-step outer, tile inner: each activation broadcast serves all tiles
       // (binary coding: one partial sum per plane)
       float cs[QS][TPW][MROWS];
@@ -343,8 +355,12 @@ void matmul_kernel(const MatmulParams pk) {
               gacc[t][m] = __builtin_fmaf(sc, __builtin_fmaf(-z, xq[m], cs[0][t][m]), gacc[t][m]);
           } else {
 #pragma unroll
-            for (int m = 0; m < MROWS; ++m) gacc[t][m] = __builtin_fmaf(sc, cs[0][t][m], gacc[t][m]);
+            for (int m = 0; m < MROWS; ++m)
+              gacc[t][m] = __builtin_fmaf(BF16 ? sc * fm[BF16 ? m : 0] : sc, cs[0][t][m], gacc[t][m]);
           }
+        } else if constexpr (BF16) {
+#pragma unroll
+          for (int m = 0; m < MROWS; ++m) gacc[t][m] = __builtin_fmaf(fm[m], cs[0][t][m], gacc[t][m]);
         } else {
 #pragma unroll
           for (int m = 0; m < MROWS; ++m) gacc[t][m] += cs[0][t][m];
@@ -366,6 +382,32 @@ void matmul_kernel(const MatmulParams pk) {
           dst[j].w = lds_load(table, pair_addr(idx4, lb, 3));
         }
       };
+      // bf16 activations: each batch row's chunk (32 values per lane, its
+      // four quarters in lanes r, r + 16, r + 32, r + 48) to fp16 under the
+      // chunk's shift; fe[mt][e] undoes it for accumulator row 4q + e
+      f32x4 fe[BF16 ? MT : 1];
+      if constexpr (BF16) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          uint32_t a = 0;
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int w = 0; w < 4; ++w) a = max(a, bf16x2_absmax(abuf[s][mt][j][w]));
+          a = max(a, (uint32_t)__shfl_xor((int)a, 16));
+          a = max(a, (uint32_t)__shfl_xor((int)a, 32));
+          const int sh = bf16_chunk_shift(a);
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int w = 0; w < 4; ++w) abuf[s][mt][j][w] = bf16x2_to_f16x2(abuf[s][mt][j][w], sh);
+          const float f = __builtin_ldexpf(1.f, -sh);   // of batch row mt 16 + r
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            fe[mt][e] = __builtin_bit_cast(
+                float, __builtin_amdgcn_ds_bpermute((4 * q + e) * 4, __builtin_bit_cast(int, f)));
+        }
+      }
       if constexpr (!BCQ) lookup(0, bq[0]);
       // Zero points: the group's activation sums, in the accumulator layout
       // (a B operand of ones gives C[m][n] = sum_k x[m][k] in every column),
@@ -431,8 +473,8 @@ void matmul_kernel(const MatmulParams pk) {
 #pragma unroll
           for (int mt = 0; mt < MT; ++mt) {
             const f16x8 a = __builtin_bit_cast(f16x8, abuf[s][mt][j]);
-            if constexpr (GROUPED) {
-              // the group's partial sum starts from zero and is rescaled below
+            if constexpr (GROUPED || BF16) {
+              // the chunk's partial sum starts from zero and is rescaled below
               cg[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
                   a, b, j == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : cg[mt], 0, 0, 0);
             } else {
@@ -440,7 +482,14 @@ void matmul_kernel(const MatmulParams pk) {
             }
           }
         }
-        if constexpr (GROUPED) {
+        if constexpr (BF16) {
+          const float sc = GROUPED ? step_scale(t, u) : 1.f;
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              macc[t][mt][e] = __builtin_fmaf(sc * fe[mt][e], cg[mt][e], macc[t][mt][e]);
+        } else if constexpr (GROUPED) {
           const float sc = step_scale(t, u);
           if constexpr (ZP) {
             const float z = step_zero(t, u);
@@ -541,7 +590,7 @@ void matmul_kernel(const MatmulParams pk) {
     v *= tscale;
     const int n = tile0 * kTileRows + row;
     if (p.ksplit == 1) {
-      if (n < p.N) p.y[(size_t)m * p.N + n] = f32_to_f16_bits(v);
+      if (n < p.N) p.y[(size_t)m * p.N + n] = BF16 ? f32_to_bf16_bits(v) : f32_to_f16_bits(v);
     } else {
       float* dst = p.partial + (((size_t)rb * p.ksplit + ks) * MROWS + m) * ROWS + row;
       __hip_atomic_store(dst, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -572,7 +621,7 @@ void matmul_kernel(const MatmulParams pk) {
     for (int k2 = 0; k2 < p.ksplit; ++k2)
       v += __hip_atomic_load(p.partial + (((size_t)rb * p.ksplit + k2) * MROWS + m) * ROWS + row,
                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (n < p.N) p.y[(size_t)m * p.N + n] = f32_to_f16_bits(v);
+    if (n < p.N) p.y[(size_t)m * p.N + n] = BF16 ? f32_to_bf16_bits(v) : f32_to_f16_bits(v);
   }
   if (tid == 0) __hip_atomic_store(p.counters + rb, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -615,28 +664,33 @@ static hipError_t launch_t(const MatmulParams& p, hipStream_t s) {
   // 8.3 us on 4096 x 14336), else 2 (wider shapes lose occupancy with 4).
   constexpr int PFK = (!MFMA && MROWS == 1 && TPW == 1) ? 4 : kPf;
   const dim3 block(WAVES * kWave);
+  // flags: GROUPED, ZP, TYPED, BCQ, BF16
+#define LUTQ_LAUNCH(G, Z, T, Q, H, OCCV)                                                   \
+  matmul_kernel<BITS, MFMA, MROWS, G, Z, T, Q, H, PFK, TPW, WAVES, OCCV><<<grid, block, 0, s>>>(p)
   if (p.bcq) {
     // binary-coded weights: GEMV shapes and the 2-tile MFMA shape only
     if constexpr (!MFMA || TPW == 2)
-      matmul_kernel<BITS, MFMA, MROWS, true, false, false, true, PFK, TPW, WAVES, OCC_G>
-          <<<grid, block, 0, s>>>(p);
+      LUTQ_LAUNCH(true, false, false, true, false, OCC_G);
     else
       return hipErrorInvalidValue;
-  } else if (p.group == 0)
-    matmul_kernel<BITS, MFMA, MROWS, false, false, false, false, PFK, TPW, WAVES, OCC>
-        <<<grid, block, 0, s>>>(p);
-  else if (p.types && p.zp)
-    matmul_kernel<BITS, MFMA, MROWS, true, true, true, false, PFK, TPW, WAVES, OCC_G>
-        <<<grid, block, 0, s>>>(p);
-  else if (p.types)
-    matmul_kernel<BITS, MFMA, MROWS, true, false, true, false, PFK, TPW, WAVES, OCC_G>
-        <<<grid, block, 0, s>>>(p);
-  else if (p.zp)
-    matmul_kernel<BITS, MFMA, MROWS, true, true, false, false, PFK, TPW, WAVES, OCC_G>
-        <<<grid, block, 0, s>>>(p);
-  else
-    matmul_kernel<BITS, MFMA, MROWS, true, false, false, false, PFK, TPW, WAVES, OCC_G>
-        <<<grid, block, 0, s>>>(p);
+  } else if (p.bf16) {
+    // bf16 activations, plain tables
+    if (p.group == 0)
+      LUTQ_LAUNCH(false, false, false, false, true, OCC);
+    else
+      LUTQ_LAUNCH(true, false, false, false, true, OCC_G);
+  } else if (p.group == 0) {
+    LUTQ_LAUNCH(false, false, false, false, false, OCC);
+  } else if (p.types && p.zp) {
+    LUTQ_LAUNCH(true, true, true, false, false, OCC_G);
+  } else if (p.types) {
+    LUTQ_LAUNCH(true, false, true, false, false, OCC_G);
+  } else if (p.zp) {
+    LUTQ_LAUNCH(true, true, false, false, false, OCC_G);
+  } else {
+    LUTQ_LAUNCH(true, false, false, false, false, OCC_G);
+  }
+#undef LUTQ_LAUNCH
   return hipGetLastError();
 }
 
