@@ -534,8 +534,10 @@ def copy_calibration(torch):
     torch.cuda.synchronize()
 
 
-HEADLINE_KERNEL = "matmul_kernel<4, false, 1, true"   # 4-bit, GEMV, batch 1, grouped scales
-BATCH32_KERNEL = "matmul_kernel<4, true, 32, false"   # 4-bit, MFMA, batch 32, tensor scale
+# template arguments: bits, MFMA, batch rows, grouped, zero points, data types,
+# binary coding, bf16, prefetch depth, tiles per wave, waves, occupancy
+HEADLINE_KERNEL = "matmul_kernel<4, false, 1, true, false, false, false, false, 2, 2, 8, 4>"
+BATCH32_KERNEL = "matmul_kernel<4, true, 32, false, false, false, false, false, 2, 8, 4, 2>"
 
 
 def _read_csv(path):
