@@ -311,6 +311,21 @@ int lutq_quant_error(const float* w, const uint16_t* lut, int bits, int N, int K
 int lutq_log_base_search(const float* w, int bits, int N, int K, int group, const double* bases,
                          int nbases, int* best, double* errors, void* stream);
 
+/* The quantizer entry points for 16-bit weights as models ship them: `w` is
+ * fp32 (LUTQ_WEIGHT_F32, 16-byte aligned), fp16 (LUTQ_WEIGHT_F16) or bf16
+ * (LUTQ_WEIGHT_BF16), both 8-byte aligned. 16-bit weights are widened to
+ * fp32 exactly, so the results are those of lutq_quantize on the same
+ * values. Otherwise as lutq_quantize, lutq_quant_error and
+ * lutq_log_base_search; LUTQ_EINVAL for another wdtype. */
+enum { LUTQ_WEIGHT_F32 = 0, LUTQ_WEIGHT_F16 = 1, LUTQ_WEIGHT_BF16 = 2 };
+int lutq_quantize_ex(const void* w, int wdtype, const uint16_t* lut, int bits, int N, int K,
+                     int group, int rule, uint8_t* codes, uint16_t* scales, void* stream);
+int lutq_quant_error_ex(const void* w, int wdtype, const uint16_t* lut, int bits, int N, int K,
+                        int group, int rule, double* err, void* stream);
+int lutq_log_base_search_ex(const void* w, int wdtype, int bits, int N, int K, int group,
+                            const double* bases, int nbases, int* best, double* errors,
+                            void* stream);
+
 /* Static string for a status code. */
 const char* lutq_strerror(int status);
 

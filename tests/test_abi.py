@@ -274,6 +274,11 @@ def test_quantizer_validates_before_launching(lib):
     assert q(codes=P(0x3002)) == EALIGN      # codes written 4 at a time
     assert q(scales=P(0x4001)) == EALIGN
     assert q(N=0) == OK and q(K=0) == OK     # nothing to do, no HIP call
+    # 16-bit weights: another dtype is rejected, and they need 8-byte alignment
+    qx = lambda w, wdt: lib.lutq_quantize_ex(w, wdt, P(0x2000), 4, 8, 256, 128, 0, P(0x3000),
+                                             P(0x4000), None)
+    assert qx(P(0x1000), 3) == EINVAL
+    assert qx(P(0x1004), 1) == EALIGN and qx(P(0x1004), 2) == EALIGN
     assert lib.lutq_quant_error(P(0x1000), P(0x2000), 4, 8, 256, 128, 0, None, None) == EINVAL
     assert lib.lutq_quant_error(P(0x1000), P(0x2000), 4, 0, 256, 128, 0, ctypes.byref(err), None) == OK
     assert err.value == 0.0

@@ -196,3 +196,38 @@ def test_quantize_repack_matmul_end_to_end(lutq):
     y_ref, B = oracle.reference(x, c_ref, T, s_ref, 128)
     ok, worst = oracle.check(y, y_ref, B)
     assert ok, f"max err/bound = {worst:.3g}"
+
+
+def _to_16bit(w, dtype):
+    """fp32 weights -> torch fp16 / bf16 tensor on the GPU, and the exact fp32 values."""
+    t = torch.from_numpy(np.ascontiguousarray(w)).to(dtype)
+    return t.cuda(), t.float().numpy()
+
+
+@pytest.mark.parametrize("dtype", ["float16", "bfloat16"])
+@pytest.mark.parametrize("kind,bits,rule,group", [("nf", 4, "absmax", 128), ("int", 3, "range", 0),
+                                                   ("log", 4, "absmax", 256), ("int", 2, "range", 512)])
+def test_quantize_16bit_weights(lutq, dtype, kind, bits, rule, group):
+    # weights as models ship them: widened to fp32 exactly on the GPU
+    T = tables.make(kind, bits, **({"base": 2 ** 0.5} if kind == "log" else {}))
+    w = draw.weights("student_t", 77, 1024, (76, bits, group), nu=4.0, scale=0.02)
+    wd, wv = _to_16bit(w, getattr(torch, dtype))
+    c, s = lutq.quantize(wd, dev(T), bits, group, rule)
+    torch.cuda.synchronize()
+    c_ref, s_ref = Q.quantize(wv, T, group, rule)
+    assert np.array_equal(s.cpu().numpy().view(np.uint16), s_ref.view(np.uint16))
+    assert np.array_equal(c.cpu().numpy(), c_ref)
+    got = lutq.quant_error(wd, dev(T), bits, group, rule)
+    want = Q.sq_error(wv, T, c_ref, s_ref, group)
+    assert abs(got - want) <= 1e-9 * want
+
+
+def test_log_base_search_fp16_weights(lutq):
+    w = draw.weights("laplace", 64, 1024, (78,), b=0.015)
+    wd, wv = _to_16bit(w, torch.float16)
+    bases = [1.3, 2 ** 0.5, 1.7, 2.2]
+    best, errs = lutq.log_base_search(wd, 4, 128, bases)
+    best_ref, errs_ref = Q.log_base_search(wv, 4, 128, bases)
+    assert best == best_ref
+    for a, b in zip(errs, errs_ref):
+        assert abs(a - b) <= 1e-9 * b

@@ -23,6 +23,7 @@ EXPORTS = (
     "lutq_plan", "lutq_strerror", "lutq_last_hip_error", "lutq_shutdown",
     "lutq_quantize", "lutq_quant_error", "lutq_log_base_search", "lutq_matmul_multi",
     "lutq_matmul_zp", "lutq_matmul_typed", "lutq_matmul_bcq",
+    "lutq_quantize_ex", "lutq_quant_error_ex", "lutq_log_base_search_ex",
 )
 
 MAX_TYPES = 4
@@ -103,6 +104,16 @@ def load_library():
     lib.lutq_matmul_bcq.argtypes = [vp, ctypes.POINTER(PackedDesc), vp, vp, i32, i32, i32,
                                     ctypes.POINTER(Options), vp]
     lib.lutq_matmul_bcq.restype = i32
+    lib.lutq_quantize_ex.argtypes = [vp, i32, vp, i32, i32, i32, i32, i32, vp, vp, vp]
+    lib.lutq_quantize_ex.restype = i32
+    lib.lutq_quant_error_ex.argtypes = [vp, i32, vp, i32, i32, i32, i32, i32,
+                                        ctypes.POINTER(ctypes.c_double), vp]
+    lib.lutq_quant_error_ex.restype = i32
+    lib.lutq_log_base_search_ex.argtypes = [vp, i32, i32, i32, i32, i32,
+                                            ctypes.POINTER(ctypes.c_double), i32,
+                                            ctypes.POINTER(ctypes.c_int32),
+                                            ctypes.POINTER(ctypes.c_double), vp]
+    lib.lutq_log_base_search_ex.restype = i32
     lib.lutq_plan.restype = i32
     lib.lutq_strerror.argtypes = [i32]
     lib.lutq_strerror.restype = ctypes.c_char_p
@@ -317,16 +328,29 @@ def matmul_bcq(x, p: Packed, alphas, *, path: str = "auto", ksplit: int = 0, til
     return out
 
 
+WEIGHT_F32, WEIGHT_F16, WEIGHT_BF16 = 0, 1, 2
+
+
+def _weight_dtype(w) -> int:
+    """The LUTQ_WEIGHT_* value of a weight tensor (fp32, fp16 or bf16 on the GPU)."""
+    import torch
+    codes = {torch.float32: WEIGHT_F32, torch.float16: WEIGHT_F16, torch.bfloat16: WEIGHT_BF16}
+    if not isinstance(w, torch.Tensor) or w.dtype not in codes:
+        raise TypeError("w must be a float32, float16 or bfloat16 tensor")
+    _need_cuda(w, "w", w.dtype)
+    return codes[w.dtype]
+
+
 def quantize(w, lut, bits: int, group: int, rule: str = "absmax"):
-    """lutq_quantize: fp32 weights [N, K] -> (uint8 codes [N, K], fp16 scales
+    """lutq_quantize_ex: fp32, fp16 or bf16 weights [N, K] -> (uint8 codes [N, K], fp16 scales
     [N, K/group] or [1]), round-to-nearest onto the table ``lut``."""
     import torch
-    _need_cuda(w, "w", torch.float32)
+    wdt = _weight_dtype(w)
     _need_cuda(lut, "lut", torch.float16)
     N, K = w.shape
     codes = torch.empty((N, K), dtype=torch.uint8, device=w.device)
     scales = torch.empty((N, K // group) if group else (1,), dtype=torch.float16, device=w.device)
-    rc = _lib().lutq_quantize(_ptr(w), _ptr(lut), bits, N, K, group, _RULES[rule], _ptr(codes),
+    rc = _lib().lutq_quantize_ex(_ptr(w), wdt, _ptr(lut), bits, N, K, group, _RULES[rule], _ptr(codes),
                               _ptr(scales), _stream(w.device))
     if rc:
         raise LutqError(rc, "lutq_quantize")
@@ -336,11 +360,11 @@ def quantize(w, lut, bits: int, group: int, rule: str = "absmax"):
 def quant_error(w, lut, bits: int, group: int, rule: str = "absmax") -> float:
     """lutq_quant_error: sum (w - s * T[c])^2 (fp64) of that quantization."""
     import torch
-    _need_cuda(w, "w", torch.float32)
+    wdt = _weight_dtype(w)
     _need_cuda(lut, "lut", torch.float16)
     N, K = w.shape
     err = ctypes.c_double(0.0)
-    rc = _lib().lutq_quant_error(_ptr(w), _ptr(lut), bits, N, K, group, _RULES[rule],
+    rc = _lib().lutq_quant_error_ex(_ptr(w), wdt, _ptr(lut), bits, N, K, group, _RULES[rule],
                                  ctypes.byref(err), _stream(w.device))
     if rc:
         raise LutqError(rc, "lutq_quant_error")
@@ -350,13 +374,13 @@ def quant_error(w, lut, bits: int, group: int, rule: str = "absmax") -> float:
 def log_base_search(w, bits: int, group: int, bases):
     """lutq_log_base_search: (index of the best base, [error of each base])."""
     import torch
-    _need_cuda(w, "w", torch.float32)
+    wdt = _weight_dtype(w)
     N, K = w.shape
     nb = len(bases)
     arr = (ctypes.c_double * nb)(*[float(b) for b in bases])
     errs = (ctypes.c_double * nb)()
     best = ctypes.c_int32(-1)
-    rc = _lib().lutq_log_base_search(_ptr(w), bits, N, K, group, arr, nb, ctypes.byref(best),
+    rc = _lib().lutq_log_base_search_ex(_ptr(w), wdt, bits, N, K, group, arr, nb, ctypes.byref(best),
                                      errs, _stream(w.device))
     if rc:
         raise LutqError(rc, "lutq_log_base_search")

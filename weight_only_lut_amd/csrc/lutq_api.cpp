@@ -426,15 +426,19 @@ static_assert(LUTQ_RULE_ABSMAX == lutq::kRuleAbsmax && LUTQ_RULE_RANGE == lutq::
               "rule values");
 
 // Arguments shared by the quantizer entry points; N, K > 0 after this.
-int check_quant(const float* w, const uint16_t* lut, int bits, int N, int K, int group, int rule) {
+int check_quant(const void* w, int wdtype, const uint16_t* lut, int bits, int N, int K, int group,
+                int rule) {
   int rc = check_sizes(N, K);
   if (rc) return rc;
   rc = check_bits_group(K, bits, group);
   if (rc) return rc;
   if (rule != LUTQ_RULE_ABSMAX && rule != LUTQ_RULE_RANGE) return LUTQ_EINVAL;
+  if (wdtype != LUTQ_WEIGHT_F32 && wdtype != LUTQ_WEIGHT_F16 && wdtype != LUTQ_WEIGHT_BF16)
+    return LUTQ_EINVAL;
   if (N == 0 || K == 0) return LUTQ_OK;
   if (!w || !lut) return LUTQ_EINVAL;
-  if (!aligned(w, 16) || !aligned(lut, 2)) return LUTQ_EALIGN;
+  // four weights per load: 16 bytes of fp32, 8 of fp16 / bf16
+  if (!aligned(w, wdtype == LUTQ_WEIGHT_F32 ? 16 : 8) || !aligned(lut, 2)) return LUTQ_EALIGN;
   return LUTQ_OK;
 }
 
@@ -459,10 +463,11 @@ int quant_scratch(void* stream, size_t extra, lutq::QuantScratch* sc, void** ext
 }
 
 // Runs the error pass and copies the total to the host (waits for the stream).
-int quant_error_to_host(const lutq::QuantScratch& sc, const float* w, const uint16_t* lut, int bits,
-                        int N, int K, int group, int rule, double* err, hipStream_t s) {
-  hipError_t e = lutq::launch_quantize(sc, w, lut, bits, N, K, group, rule, nullptr, nullptr,
-                                       true, s);
+int quant_error_to_host(const lutq::QuantScratch& sc, const void* w, int wdtype,
+                        const uint16_t* lut, int bits, int N, int K, int group, int rule,
+                        double* err, hipStream_t s) {
+  hipError_t e = lutq::launch_quantize(sc, w, wdtype, lut, bits, N, K, group, rule, nullptr,
+                                       nullptr, true, s);
   if (e != hipSuccess) return hip_fail(e);
   e = hipMemcpyAsync(err, sc.err_total, sizeof(double), hipMemcpyDeviceToHost, s);
   if (e != hipSuccess) return hip_fail(e);
@@ -470,13 +475,16 @@ int quant_error_to_host(const lutq::QuantScratch& sc, const float* w, const uint
   return e == hipSuccess ? LUTQ_OK : hip_fail(e);
 }
 
+static_assert(LUTQ_WEIGHT_F32 == 0 && LUTQ_WEIGHT_F16 == 1 && LUTQ_WEIGHT_BF16 == 2,
+              "the quantizer kernels' weight type values");
+
 }  // namespace
 
 extern "C" {
 
-int lutq_quantize(const float* w, const uint16_t* lut, int bits, int N, int K, int group,
-                  int rule, uint8_t* codes, uint16_t* scales, void* stream) {
-  int rc = check_quant(w, lut, bits, N, K, group, rule);
+int lutq_quantize_ex(const void* w, int wdtype, const uint16_t* lut, int bits, int N, int K,
+                     int group, int rule, uint8_t* codes, uint16_t* scales, void* stream) {
+  int rc = check_quant(w, wdtype, lut, bits, N, K, group, rule);
   if (rc) return rc;
   if (N == 0 || K == 0) return LUTQ_OK;
   if (!codes || !scales) return LUTQ_EINVAL;
@@ -487,15 +495,20 @@ int lutq_quantize(const float* w, const uint16_t* lut, int bits, int N, int K, i
     rc = quant_scratch(stream, 0, &sc, nullptr);
     if (rc) return rc;
   }
-  hipError_t e = lutq::launch_quantize(sc, w, lut, bits, N, K, group, rule, codes, scales, false,
-                                       (hipStream_t)stream);
+  hipError_t e = lutq::launch_quantize(sc, w, wdtype, lut, bits, N, K, group, rule, codes, scales,
+                                       false, (hipStream_t)stream);
   return e == hipSuccess ? LUTQ_OK : hip_fail(e);
 }
 
-int lutq_quant_error(const float* w, const uint16_t* lut, int bits, int N, int K, int group,
-                     int rule, double* err, void* stream) {
+int lutq_quantize(const float* w, const uint16_t* lut, int bits, int N, int K, int group,
+                  int rule, uint8_t* codes, uint16_t* scales, void* stream) {
+  return lutq_quantize_ex(w, LUTQ_WEIGHT_F32, lut, bits, N, K, group, rule, codes, scales, stream);
+}
+
+int lutq_quant_error_ex(const void* w, int wdtype, const uint16_t* lut, int bits, int N, int K,
+                        int group, int rule, double* err, void* stream) {
   if (!err) return LUTQ_EINVAL;
-  int rc = check_quant(w, lut, bits, N, K, group, rule);
+  int rc = check_quant(w, wdtype, lut, bits, N, K, group, rule);
   if (rc) return rc;
   if (N == 0 || K == 0) {
     *err = 0.0;
@@ -504,14 +517,21 @@ int lutq_quant_error(const float* w, const uint16_t* lut, int bits, int N, int K
   lutq::QuantScratch sc;
   rc = quant_scratch(stream, 0, &sc, nullptr);
   if (rc) return rc;
-  return quant_error_to_host(sc, w, lut, bits, N, K, group, rule, err, (hipStream_t)stream);
+  return quant_error_to_host(sc, w, wdtype, lut, bits, N, K, group, rule, err,
+                             (hipStream_t)stream);
 }
 
-int lutq_log_base_search(const float* w, int bits, int N, int K, int group, const double* bases,
-                         int nbases, int* best, double* errors, void* stream) {
+int lutq_quant_error(const float* w, const uint16_t* lut, int bits, int N, int K, int group,
+                     int rule, double* err, void* stream) {
+  return lutq_quant_error_ex(w, LUTQ_WEIGHT_F32, lut, bits, N, K, group, rule, err, stream);
+}
+
+int lutq_log_base_search_ex(const void* w, int wdtype, int bits, int N, int K, int group,
+                            const double* bases, int nbases, int* best, double* errors,
+                            void* stream) {
   if (!best || !bases || nbases < 1) return LUTQ_EINVAL;
   uint16_t dummy = 0;
-  int rc = check_quant(w, &dummy, bits, N, K, group, LUTQ_RULE_ABSMAX);
+  int rc = check_quant(w, wdtype, &dummy, bits, N, K, group, LUTQ_RULE_ABSMAX);
   if (rc) return rc;
   const int L = 1 << bits, half = L / 2;
   for (int i = 0; i < nbases; ++i) {
@@ -547,8 +567,8 @@ int lutq_log_base_search(const float* w, int bits, int N, int K, int group, cons
     hipError_t e = hipMemcpyAsync(tbl, host_tbl, L * sizeof(uint16_t), hipMemcpyHostToDevice, s);
     if (e != hipSuccess) return hip_fail(e);
     double err = 0.0;
-    rc = quant_error_to_host(sc, w, (const uint16_t*)tbl, bits, N, K, group, LUTQ_RULE_ABSMAX,
-                             &err, s);
+    rc = quant_error_to_host(sc, w, wdtype, (const uint16_t*)tbl, bits, N, K, group,
+                             LUTQ_RULE_ABSMAX, &err, s);
     if (rc) return rc;
     if (errors) errors[i] = err;
     if (i == 0 || err < best_err) {
@@ -557,6 +577,12 @@ int lutq_log_base_search(const float* w, int bits, int N, int K, int group, cons
     }
   }
   return LUTQ_OK;
+}
+
+int lutq_log_base_search(const float* w, int bits, int N, int K, int group, const double* bases,
+                         int nbases, int* best, double* errors, void* stream) {
+  return lutq_log_base_search_ex(w, LUTQ_WEIGHT_F32, bits, N, K, group, bases, nbases, best,
+                                 errors, stream);
 }
 
 const char* lutq_strerror(int status) {

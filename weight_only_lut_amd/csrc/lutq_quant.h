@@ -21,9 +21,10 @@ constexpr size_t kQuantScratchBytes =
     kQuantMaxBlocks * sizeof(double) + 64 + 3 * kQuantMaxBlocks * sizeof(float) + 64;
 
 // codes / scales may be null (not written); error: also fill err_total.
-hipError_t launch_quantize(const QuantScratch& sc, const float* w, const uint16_t* lut, int bits,
-                           int N, int K, int group, int rule, uint8_t* codes, uint16_t* scales,
-                           bool error, hipStream_t s);
+// wdtype: the LUTQ_WEIGHT_* value of the weights at w.
+hipError_t launch_quantize(const QuantScratch& sc, const void* w, int wdtype, const uint16_t* lut,
+                           int bits, int N, int K, int group, int rule, uint8_t* codes,
+                           uint16_t* scales, bool error, hipStream_t s);
 
 // fp64 -> fp16 bits, round to nearest even (host and device).
 __host__ __device__ uint16_t f64_to_f16_rne(double d);

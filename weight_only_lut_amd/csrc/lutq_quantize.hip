@@ -62,7 +62,7 @@ __host__ __device__ uint16_t f64_to_f16_rne(double d) {
 namespace {
 
 struct QuantParams {
-  const float* w;
+  const void* w;           // weights, fp32 or (kWeightF16 / kWeightBf16) 16-bit
   const uint16_t* lut;
   uint8_t* codes;          // null: do not write codes
   uint16_t* scales;        // null: do not write scales
@@ -82,6 +82,49 @@ constexpr int kPiece = 128;                   // a 128-weight piece spans 8 lane
 constexpr int kMaxAreas = kStep / kPiece;     // groups per wave per step, at most
 
 __device__ __forceinline__ double h2d(uint16_t h) { return (double)__builtin_bit_cast(_Float16, h); }
+
+// Weights: fp32, or fp16 / bf16 widened to fp32 (exactly) on load.
+constexpr int kWeightF32 = 0, kWeightF16 = 1, kWeightBf16 = 2;
+
+template <int WT>
+__device__ __forceinline__ f32x4 widen4(u32x2 v) {
+  f32x4 r;
+  if constexpr (WT == kWeightF16) {
+    r[0] = (float)__builtin_bit_cast(_Float16, (uint16_t)(v.x & 0xFFFFu));
+    r[1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(v.x >> 16));
+    r[2] = (float)__builtin_bit_cast(_Float16, (uint16_t)(v.y & 0xFFFFu));
+    r[3] = (float)__builtin_bit_cast(_Float16, (uint16_t)(v.y >> 16));
+  } else {
+    r[0] = __builtin_bit_cast(float, v.x << 16);
+    r[1] = __builtin_bit_cast(float, v.x & 0xFFFF0000u);
+    r[2] = __builtin_bit_cast(float, v.y << 16);
+    r[3] = __builtin_bit_cast(float, v.y & 0xFFFF0000u);
+  }
+  return r;
+}
+
+// Four weights at element offset e of a buffer resource.
+template <int WT>
+__device__ __forceinline__ f32x4 load_weights4(__amdgpu_buffer_rsrc_t rs, uint32_t e) {
+  if constexpr (WT == kWeightF32) {
+    return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, 4u * e, 0, kNontemporal));
+  } else {
+    return widen4<WT>(
+        __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, 2u * e, 0, kNontemporal)));
+  }
+}
+
+// Four weights (vector i) of a plain pointer.
+template <int WT>
+struct Weights4 {
+  const void* base;
+  __device__ __forceinline__ f32x4 at(long long i) const {
+    if constexpr (WT == kWeightF32)
+      return __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(base) + i);
+    else
+      return widen4<WT>(__builtin_nontemporal_load(reinterpret_cast<const u32x2*>(base) + i));
+  }
+};
 
 // The table as one lane needs it. With the L entries sorted ascending,
 // midpoint m lies between sorted entries m and m + 1; lane j (mod 8) of a
@@ -299,8 +342,9 @@ __device__ __forceinline__ void wave_lds_fence() {
 // Tensor-wise: the same with GL = 8 over 128-weight pieces and one scale.
 // GL == 0: groups of any multiple of 128 over 8 lanes, read twice (extrema,
 // then codes), 8 groups per step.
-template <int L, int GL, bool ERR, bool TENSOR>
+template <int L, int GL, bool ERR, bool TENSOR, int WT>
 __global__ __launch_bounds__(kQuantThreads) void quant_kernel(const QuantParams p) {
+  constexpr int ES = WT == kWeightF32 ? 4 : 2;  // bytes per weight
   __shared__ double tval[L];
   __shared__ f32x4 areas[kQuantWaves][kMaxAreas][5];
   Table<L> t;
@@ -377,8 +421,9 @@ __global__ __launch_bounds__(kQuantThreads) void quant_kernel(const QuantParams 
     }
     return packed;
   };
-  auto load = [&](__amdgpu_buffer_rsrc_t rs, uint32_t off) __attribute__((always_inline)) {
-    return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, kNontemporal));
+  // four weights at element offset `e` of the resource, as fp32 (exact)
+  auto load = [&](__amdgpu_buffer_rsrc_t rs, uint32_t e) __attribute__((always_inline)) {
+    return load_weights4<WT>(rs, e);
   };
   auto store = [&](__amdgpu_buffer_rsrc_t rc, uint32_t off, uint32_t v) __attribute__((always_inline)) {
     __builtin_amdgcn_raw_buffer_store_b32(v, rc, off, 0, 0);
@@ -388,9 +433,9 @@ __global__ __launch_bounds__(kQuantThreads) void quant_kernel(const QuantParams 
     const uint32_t lane_off = (uint32_t)(r * gsize + 4 * j);  // weights, from the step's start
     f32x4 bufA[4], bufB[4];
     auto fetch = [&](f32x4 (&b)[4], long long unit) __attribute__((always_inline)) {
-      const auto rs = tail_rsrc(p.w, unit * per_step, p.n, 4);
+      const auto rs = tail_rsrc(p.w, unit * per_step, p.n, ES);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) b[i] = load(rs, 4u * (lane_off + 4 * G * i));
+      for (int i = 0; i < 4; ++i) b[i] = load(rs, lane_off + 4 * G * i);
     };
     auto step = [&](const f32x4 (&b)[4], long long unit) __attribute__((always_inline)) {
       const long long gi = unit * kGroups + r;
@@ -427,11 +472,11 @@ __global__ __launch_bounds__(kQuantThreads) void quant_kernel(const QuantParams 
     const uint32_t lane_off = (uint32_t)(r * gsize + 4 * j);
     for (long long unit = wave0; unit < nunits; unit += nwaves) {
       const long long gi = unit * kGroups + r;
-      const auto rs = tail_rsrc(p.w, unit * per_step, p.n, 4);
+      const auto rs = tail_rsrc(p.w, unit * per_step, p.n, ES);
       int kmx = INT_MIN, kmn = INT_MAX;
       for (int q = 0; q < pieces; ++q)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) extrema(load(rs, 4u * (lane_off + q * kPiece + 32 * i)), kmx, kmn);
+        for (int i = 0; i < 4; ++i) extrema(load(rs, lane_off + q * kPiece + 32 * i), kmx, kmn);
       prepare(kmx, kmn, gi);
       const bool active = gi < p.nrows;
       const auto rc = tail_rsrc(p.codes, unit * per_step, p.codes ? p.n : 0, 1);
@@ -439,7 +484,7 @@ __global__ __launch_bounds__(kQuantThreads) void quant_kernel(const QuantParams 
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const uint32_t off = lane_off + q * kPiece + 32 * i;
-          const uint32_t packed = code4(load(rs, 4u * off), active);
+          const uint32_t packed = code4(load(rs, off), active);
           if (p.codes) store(rc, off, packed);
         }
     }
@@ -448,17 +493,18 @@ __global__ __launch_bounds__(kQuantThreads) void quant_kernel(const QuantParams 
 }
 
 // Tensor-wise, pass 1: per-workgroup max and min.
+template <int WT>
 __global__ __launch_bounds__(kQuantThreads) void tensor_extrema_kernel(const QuantParams p) {
   __shared__ float part[2][kQuantWaves];
   const long long nvec = p.n / 4;  // n is a multiple of 128
   float mx = -__builtin_huge_valf(), mn = __builtin_huge_valf();
-  const f32x4* src = reinterpret_cast<const f32x4*>(p.w);
+  const Weights4<WT> src{p.w};
   const long long stride = (long long)gridDim.x * kQuantThreads;
   long long i = (long long)blockIdx.x * kQuantThreads + threadIdx.x;
   for (; i + 3 * stride < nvec; i += 4 * stride) {  // four loads in flight
     f32x4 v[4];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) v[k] = __builtin_nontemporal_load(src + i + k * stride);
+    for (int k = 0; k < 4; ++k) v[k] = src.at(i + k * stride);
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       mx = fmaxf(mx, fmaxf(fmaxf(v[k][0], v[k][1]), fmaxf(v[k][2], v[k][3])));
@@ -466,7 +512,7 @@ __global__ __launch_bounds__(kQuantThreads) void tensor_extrema_kernel(const Qua
     }
   }
   for (; i < nvec; i += stride) {
-    const f32x4 v = __builtin_nontemporal_load(src + i);
+    const f32x4 v = src.at(i);
     mx = fmaxf(mx, fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])));
     mn = fminf(mn, fminf(fminf(v[0], v[1]), fminf(v[2], v[3])));
   }
@@ -542,12 +588,12 @@ __global__ __launch_bounds__(kQuantThreads) void error_sum_kernel(const double* 
   }
 }
 
-template <int L, int GL, bool TENSOR>
+template <int L, int GL, bool TENSOR, int WT>
 void launch_codes(const QuantParams& p, int nblocks, bool err, hipStream_t s) {
   if (err)
-    quant_kernel<L, GL, true, TENSOR><<<nblocks, kQuantThreads, 0, s>>>(p);
+    quant_kernel<L, GL, true, TENSOR, WT><<<nblocks, kQuantThreads, 0, s>>>(p);
   else
-    quant_kernel<L, GL, false, TENSOR><<<nblocks, kQuantThreads, 0, s>>>(p);
+    quant_kernel<L, GL, false, TENSOR, WT><<<nblocks, kQuantThreads, 0, s>>>(p);
 }
 
 // Workgroups for `units` wave steps: one step per wave, at most kQuantMaxBlocks.
@@ -556,7 +602,7 @@ int blocks_for(long long units) {
   return (int)(want < kQuantMaxBlocks ? want : kQuantMaxBlocks);
 }
 
-template <int L>
+template <int L, int WT>
 hipError_t launch_l(const QuantScratch& sc, const QuantParams& p0, bool err, hipStream_t s) {
   QuantParams p = p0;
   p.err_partial = sc.err_partial;
@@ -567,11 +613,11 @@ hipError_t launch_l(const QuantScratch& sc, const QuantParams& p0, bool err, hip
     const int per_step = gl == 8 || gl == 16 || gl == 32 || gl == 64 ? kWave / gl : 8;
     nblocks = blocks_for((p.nrows + per_step - 1) / per_step);
     switch (gl) {
-      case 8: launch_codes<L, 8, false>(p, nblocks, err, s); break;
-      case 16: launch_codes<L, 16, false>(p, nblocks, err, s); break;
-      case 32: launch_codes<L, 32, false>(p, nblocks, err, s); break;
-      case 64: launch_codes<L, 64, false>(p, nblocks, err, s); break;
-      default: launch_codes<L, 0, false>(p, nblocks, err, s); break;
+      case 8: launch_codes<L, 8, false, WT>(p, nblocks, err, s); break;
+      case 16: launch_codes<L, 16, false, WT>(p, nblocks, err, s); break;
+      case 32: launch_codes<L, 32, false, WT>(p, nblocks, err, s); break;
+      case 64: launch_codes<L, 64, false, WT>(p, nblocks, err, s); break;
+      default: launch_codes<L, 0, false, WT>(p, nblocks, err, s); break;
     }
   } else {
     p.extrema = sc.extrema;
@@ -579,20 +625,30 @@ hipError_t launch_l(const QuantScratch& sc, const QuantParams& p0, bool err, hip
     p.nrows = p.n / kPiece;
     const long long want = (p.n / 4 + kQuantThreads - 1) / kQuantThreads;
     const int nx = (int)(want < kQuantMaxBlocks ? want : kQuantMaxBlocks);
-    tensor_extrema_kernel<<<nx, kQuantThreads, 0, s>>>(p);
+    tensor_extrema_kernel<WT><<<nx, kQuantThreads, 0, s>>>(p);
     tensor_scale_kernel<L><<<1, kQuantThreads, 0, s>>>(p, nx);
     nblocks = blocks_for((p.nrows + kMaxAreas - 1) / kMaxAreas);
-    launch_codes<L, 8, true>(p, nblocks, err, s);
+    launch_codes<L, 8, true, WT>(p, nblocks, err, s);
   }
   if (err) error_sum_kernel<<<1, kQuantThreads, 0, s>>>(sc.err_partial, nblocks, sc.err_total);
   return hipGetLastError();
 }
 
+template <int WT>
+hipError_t launch_w(const QuantScratch& sc, const QuantParams& p, int bits, bool error,
+                    hipStream_t s) {
+  switch (bits) {
+    case 2: return launch_l<4, WT>(sc, p, error, s);
+    case 3: return launch_l<8, WT>(sc, p, error, s);
+    default: return launch_l<16, WT>(sc, p, error, s);
+  }
+}
+
 }  // namespace
 
-hipError_t launch_quantize(const QuantScratch& sc, const float* w, const uint16_t* lut, int bits,
-                           int N, int K, int group, int rule, uint8_t* codes, uint16_t* scales,
-                           bool error, hipStream_t s) {
+hipError_t launch_quantize(const QuantScratch& sc, const void* w, int wdtype, const uint16_t* lut,
+                           int bits, int N, int K, int group, int rule, uint8_t* codes,
+                           uint16_t* scales, bool error, hipStream_t s) {
   QuantParams p;
   __builtin_memset(&p, 0, sizeof p);
   p.w = w;
@@ -604,10 +660,10 @@ hipError_t launch_quantize(const QuantScratch& sc, const float* w, const uint16_
   p.K = K;
   p.group = group;
   p.rule = rule;
-  switch (bits) {
-    case 2: return launch_l<4>(sc, p, error, s);
-    case 3: return launch_l<8>(sc, p, error, s);
-    default: return launch_l<16>(sc, p, error, s);
+  switch (wdtype) {
+    case kWeightF16: return launch_w<kWeightF16>(sc, p, bits, error, s);
+    case kWeightBf16: return launch_w<kWeightBf16>(sc, p, bits, error, s);
+    default: return launch_w<kWeightF32>(sc, p, bits, error, s);
   }
 }
 
