@@ -25,7 +25,11 @@ tensor-wise granularity and logarithmic tables whose base is adjustable):
   table search;
 - the logarithmic table ``T[sign, k] = (-1)^sign * base^(-k)`` (sign = the top
   code bit, k = the remaining bits) and the base search: the candidate base
-  with the smallest weight error.
+  with the smallest weight error;
+- table tuning on the weight error (page 2, FLUTE abstract: NormalFloat
+  tables; page 3, TurboQuant/EDEN note: the Lloyd-Max algorithm): with the
+  scales fixed from the initial table, alternate round-to-nearest codes and
+  the least-squares entry T[i] = sum w s / sum s^2 over the weights coded i.
 
 Parity status: every function here is pinned by tests/test_oracle_quantize.py
 (closed forms, brute force with exact rationals, invariants).
@@ -152,3 +156,38 @@ def log_base_search(w: np.ndarray, bits: int, group: int, bases) -> tuple[int, l
         c, s16 = quantize(w, T, group, "absmax")
         errs.append(sq_error(w, T, c, s16, group))
     return int(np.argmin(errs)), errs
+
+
+def tune_table(w: np.ndarray, lut: np.ndarray, group: int, rule: str, iters: int):
+    """Lloyd iterations on the weight error with fixed scales.
+
+    The scales come from ``lut`` under ``rule`` and stay fixed. Each
+    iteration codes the weights by round-to-nearest and replaces every used
+    entry by the fp16 (nearest even) value of sum(w * s) / sum(s^2) over the
+    weights holding that code, both sums in fp64 (exact products); an unused
+    entry keeps its value. An update that would repeat an fp16 value stops
+    the iterations. Returns (table, scales, errors): errors[k] is the weight
+    error of the k-th table (errors[0] that of ``lut``), one more than the
+    updates made.
+    """
+    s16 = scales(w, lut, group, rule)
+    T = np.asarray(lut, np.float16).copy()
+    N, K = w.shape
+    w64 = np.asarray(w, np.float32).astype(np.float64)
+    sfull = (np.full((N, K), s16.astype(np.float64)[0]) if group == 0
+             else np.repeat(s16.astype(np.float64), group, axis=1))
+    errors = []
+    for k in range(iters + 1):
+        c = codes(w, T, s16, group)
+        errors.append(sq_error(w, T, c, s16, group))
+        if k == iters:
+            break
+        num = np.bincount(c.ravel(), weights=(w64 * sfull).ravel(), minlength=T.size)
+        den = np.bincount(c.ravel(), weights=(sfull * sfull).ravel(), minlength=T.size)
+        T_new = T.copy()
+        used = den > 0
+        T_new[used] = (num[used] / den[used]).astype(np.float16)
+        if np.unique(T_new.astype(np.float64)).size != T_new.size:
+            break
+        T = T_new
+    return T, s16, errors

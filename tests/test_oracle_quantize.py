@@ -9,7 +9,10 @@
   the ``absmax`` rule landing the largest weight on the outermost entry;
 - the weight error against a hand sum with exact rationals;
 - the log table's values, and the base search recovering the base that
-  generated the weights (error exactly 0) among other candidates.
+  generated the weights (error exactly 0) among other candidates;
+- table tuning: one step against exact rational centroids, a table that is
+  already the centroids of its own weights stays put, unused codes keep
+  their entries, and the error of each table matches its own evaluation.
 """
 
 from fractions import Fraction
@@ -139,3 +142,46 @@ def test_log_base_search_recovers_the_generating_base():
     best, errs = Q.log_base_search(w, 4, 128, bases)
     assert best == 1 and errs[1] == 0.0
     assert all(e > 0 for i, e in enumerate(errs) if i != 1)
+
+
+def test_tune_one_step_is_the_exact_centroid():
+    rng = np.random.default_rng(11)
+    T0 = TABLES["nf4"]
+    w = rng.normal(0, 0.3, (6, 256)).astype(np.float32)
+    T1, s16, errs = Q.tune_table(w, T0, 128, "absmax", 1)
+    c = Q.codes(w, T0, s16, 128)
+    for i in range(16):
+        num = den = Fraction(0)
+        for n in range(6):
+            for k in range(256):
+                if c[n, k] == i:
+                    sv = Fraction(float(s16[n, k // 128]))
+                    num += Fraction(float(w[n, k])) * sv
+                    den += sv * sv
+        want = np.float16(float(num / den)) if den else T0[i]
+        assert T1[i] == want, i
+    assert len(errs) == 2
+
+
+def test_tune_keeps_a_table_that_is_its_own_centroids():
+    # every code's weights sit exactly on s * T[i], and each group holds +-s
+    rng = np.random.default_rng(12)
+    T0 = TABLES["nf4"]
+    c = rng.integers(0, 16, (4, 256))
+    c[:, 0] = 15
+    c[:, 128] = 15
+    s = (2.0 ** -rng.integers(3, 8, (4, 2))).astype(np.float32)
+    w = (T0[c].astype(np.float32) * np.repeat(s, 128, axis=1)).astype(np.float32)
+    T, _, errs = Q.tune_table(w, T0, 128, "absmax", 3)
+    assert np.array_equal(T.view(np.uint16), T0.view(np.uint16))
+    assert errs == [0.0] * 4
+
+
+def test_tune_unused_codes_keep_their_entries_and_errors_are_consistent():
+    rng = np.random.default_rng(13)
+    T0 = TABLES["int2"]                       # -2 -1 0 1
+    w = np.abs(rng.normal(0, 1, (3, 256))).astype(np.float32)    # never near -2 or -1
+    T, s16, errs = Q.tune_table(w, T0, 0, "range", 4)
+    assert T[0] == T0[0] and T[1] == T0[1]
+    assert errs[-1] == Q.sq_error(w, T, Q.codes(w, T, s16, 0), s16, 0)
+    assert errs[-1] <= errs[0]
