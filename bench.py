@@ -348,6 +348,18 @@ def quantizer_section(lutq, torch, args):
                       "cpu_oracle": {"seconds": round(cpu_s, 3), "GBps": round(cpu_bytes / cpu_s / 1e9, 3),
                                      "sample": f"scales over the whole matrix, codes for {rows} rows"}}
         log(f"[bench] quantizer {label}: {us:.1f} us/call, {gbps:.0f} GB/s")
+        if group:
+            # NormalFloat table tuning on the same weights: 5 Lloyd updates
+            from synth import tables
+            T0 = torch.from_numpy(tables.make("nf", qc.w.bits)).cuda()
+            torch.cuda.synchronize()
+            t0 = time.time()
+            _, _, errs = lutq.tune_table(qc.ws[0], T0, qc.w.bits, group, "absmax", iters=5)
+            dt = time.time() - t0
+            out[label]["nf_tune"] = {"updates": len(errs) - 1, "seconds": round(dt, 4),
+                                     "us_per_pass": round(dt * 1e6 / (len(errs) + 1), 1),
+                                     "error_first_last": [errs[0], errs[-1]]}
+            log(f"[bench] NF table tuning: {len(errs) - 1} updates in {dt * 1e3:.2f} ms")
         del qc
         torch.cuda.empty_cache()
     return out

@@ -326,6 +326,27 @@ int lutq_log_base_search_ex(const void* w, int wdtype, int bits, int N, int K, i
                             const double* bases, int nbases, int* best, double* errors,
                             void* stream);
 
+/* Table tuning on the weight error (FLUTE abstract: NormalFloat tables;
+ * TurboQuant/EDEN note: the Lloyd-Max algorithm), no data needed: the scales
+ * come from the initial table under `rule` and stay fixed; each iteration
+ * codes the weights by round-to-nearest and replaces every used entry by the
+ * fp16 (nearest even) value of sum(w s) / sum(s^2) over the weights holding
+ * that code (fp64 sums in a fixed order); an unused entry keeps its value.
+ * An update that would repeat an fp16 value stops the iterations.
+ *   w, wdtype, bits, N, K, group, rule : as lutq_quantize_ex.
+ *   lut     : device, fp16 [2^bits]: the initial table in, the tuned one out.
+ *   iters   : at most this many updates (>= 0).
+ *   scales  : device, fp16, the fixed scales out (layout of lutq_quantize),
+ *             2-byte aligned, or NULL.
+ *   errors  : host, iters + 1 entries, or NULL: errors[k] is the weight
+ *             error of the k-th table, for k = 0 .. *updates.
+ *   updates : host, the number of updates made.
+ * Waits for the stream. Errors as lutq_quantize_ex, plus LUTQ_EINVAL for a
+ * NULL updates or iters < 0. */
+int lutq_tune_table(const void* w, int wdtype, uint16_t* lut, int bits, int N, int K, int group,
+                    int rule, int iters, uint16_t* scales, double* errors, int* updates,
+                    void* stream);
+
 /* Static string for a status code. */
 const char* lutq_strerror(int status);
 

@@ -279,6 +279,17 @@ def test_quantizer_validates_before_launching(lib):
                                              P(0x4000), None)
     assert qx(P(0x1000), 3) == EINVAL
     assert qx(P(0x1004), 1) == EALIGN and qx(P(0x1004), 2) == EALIGN
+    # table tuning
+    upd = ctypes.c_int32(-1)
+    tt = lambda **k: lib.lutq_tune_table(k.get("w", P(0x1000)), 0, P(0x2000), 4, k.get("N", 8), 256,
+                                         128, 0, k.get("iters", 3), None, None, k.get("upd", ctypes.byref(upd)),
+                                         None)
+    assert tt(upd=None) == EINVAL and tt(iters=-1) == EINVAL
+    assert tt(w=P(0x1004)) == EALIGN
+    errs = (ctypes.c_double * 4)(1, 1, 1, 1)
+    assert lib.lutq_tune_table(P(0x1000), 0, P(0x2000), 4, 0, 256, 128, 0, 3, None, errs,
+                               ctypes.byref(upd), None) == OK
+    assert upd.value == 0 and list(errs) == [0.0] * 4
     assert lib.lutq_quant_error(P(0x1000), P(0x2000), 4, 8, 256, 128, 0, None, None) == EINVAL
     assert lib.lutq_quant_error(P(0x1000), P(0x2000), 4, 0, 256, 128, 0, ctypes.byref(err), None) == OK
     assert err.value == 0.0

@@ -231,3 +231,24 @@ def test_log_base_search_fp16_weights(lutq):
     assert best == best_ref
     for a, b in zip(errs, errs_ref):
         assert abs(a - b) <= 1e-9 * b
+
+
+@pytest.mark.parametrize("kind,bits,rule,group,dtype", [
+    ("nf", 4, "absmax", 128, "float32"), ("nf", 3, "absmax", 0, "float32"),
+    ("int", 4, "range", 256, "float16"), ("lloyd_max", 3, "absmax", 128, "bfloat16"),
+    ("nf", 2, "absmax", 384, "float32")])
+def test_tune_table_matches_oracle(lutq, kind, bits, rule, group, dtype):
+    # The sums are fp64 in a different order on each side, so a tuned entry
+    # could differ only if its centroid fell within ~1e-16 of an fp16
+    # rounding boundary; the tables and scales are compared bit for bit.
+    T0 = tables.make(kind, bits)
+    w = draw.weights("student_t", 90, 1536, (80, bits, group), nu=4.0, scale=0.02)
+    wd, wv = _to_16bit(w, getattr(torch, dtype)) if dtype != "float32" else (dev(w), w)
+    T, s, errs = lutq.tune_table(wd, dev(T0), bits, group, rule, iters=6)
+    T_ref, s_ref, errs_ref = Q.tune_table(wv, T0, group, rule, 6)
+    assert np.array_equal(T.cpu().numpy().view(np.uint16), T_ref.view(np.uint16))
+    assert np.array_equal(s.cpu().numpy().view(np.uint16), s_ref.view(np.uint16))
+    assert len(errs) == len(errs_ref)
+    for a, b in zip(errs, errs_ref):
+        assert abs(a - b) <= 1e-9 * b
+    assert errs[-1] <= errs[0]

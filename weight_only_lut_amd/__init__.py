@@ -29,5 +29,6 @@ from ._lib import (  # noqa: F401
     quantize,
     repack,
     strerror,
+    tune_table,
     unpack,
 )

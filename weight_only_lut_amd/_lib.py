@@ -23,7 +23,7 @@ EXPORTS = (
     "lutq_plan", "lutq_strerror", "lutq_last_hip_error", "lutq_shutdown",
     "lutq_quantize", "lutq_quant_error", "lutq_log_base_search", "lutq_matmul_multi",
     "lutq_matmul_zp", "lutq_matmul_typed", "lutq_matmul_bcq",
-    "lutq_quantize_ex", "lutq_quant_error_ex", "lutq_log_base_search_ex",
+    "lutq_quantize_ex", "lutq_quant_error_ex", "lutq_log_base_search_ex", "lutq_tune_table",
 )
 
 MAX_TYPES = 4
@@ -114,6 +114,9 @@ def load_library():
                                             ctypes.POINTER(ctypes.c_int32),
                                             ctypes.POINTER(ctypes.c_double), vp]
     lib.lutq_log_base_search_ex.restype = i32
+    lib.lutq_tune_table.argtypes = [vp, i32, vp, i32, i32, i32, i32, i32, i32, vp,
+                                    ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int32), vp]
+    lib.lutq_tune_table.restype = i32
     lib.lutq_plan.restype = i32
     lib.lutq_strerror.argtypes = [i32]
     lib.lutq_strerror.restype = ctypes.c_char_p
@@ -385,3 +388,21 @@ def log_base_search(w, bits: int, group: int, bases):
     if rc:
         raise LutqError(rc, "lutq_log_base_search")
     return best.value, list(errs)
+
+
+def tune_table(w, lut, bits: int, group: int, rule: str = "absmax", iters: int = 10):
+    """lutq_tune_table: Lloyd iterations on the weight error with fixed scales.
+    Returns (tuned table fp16 [2^bits], fixed scales fp16, [error of each table])."""
+    import torch
+    wdt = _weight_dtype(w)
+    _need_cuda(lut, "lut", torch.float16)
+    N, K = w.shape
+    T = lut.clone()
+    scales = torch.empty((N, K // group) if group else (1,), dtype=torch.float16, device=w.device)
+    errs = (ctypes.c_double * (iters + 1))()
+    upd = ctypes.c_int32(0)
+    rc = _lib().lutq_tune_table(_ptr(w), wdt, _ptr(T), bits, N, K, group, _RULES[rule], iters,
+                                _ptr(scales), errs, ctypes.byref(upd), _stream(w.device))
+    if rc:
+        raise LutqError(rc, "lutq_tune_table")
+    return T, scales, list(errs)[: upd.value + 1]

@@ -458,6 +458,10 @@ int quant_scratch(void* stream, size_t extra, lutq::QuantScratch* sc, void** ext
   b += 3 * lutq::kQuantMaxBlocks * sizeof(float);
   sc->tscale = reinterpret_cast<uint16_t*>(b);
   b += 64;
+  sc->acc_partial = reinterpret_cast<double*>(b);
+  b += lutq::kQuantMaxBlocks * 2 * 16 * sizeof(double);
+  sc->stop = reinterpret_cast<int*>(b);
+  b += 64;
   if (extra_out) *extra_out = b;
   return LUTQ_OK;
 }
@@ -575,6 +579,46 @@ int lutq_log_base_search_ex(const void* w, int wdtype, int bits, int N, int K, i
       best_err = err;
       *best = i;
     }
+  }
+  return LUTQ_OK;
+}
+
+int lutq_tune_table(const void* w, int wdtype, uint16_t* lut, int bits, int N, int K, int group,
+                    int rule, int iters, uint16_t* scales, double* errors, int* updates,
+                    void* stream) {
+  if (!updates || iters < 0) return LUTQ_EINVAL;
+  int rc = check_quant(w, wdtype, lut, bits, N, K, group, rule);
+  if (rc) return rc;
+  *updates = 0;
+  if (N == 0 || K == 0) {
+    if (errors)
+      for (int i = 0; i <= iters; ++i) errors[i] = 0.0;
+    return LUTQ_OK;
+  }
+  if (scales && !aligned(scales, 2)) return LUTQ_EALIGN;
+  // the fixed scales: the caller's buffer, or scratch after the quantizer's
+  const size_t nsc = group ? (size_t)N * (K / group) : 1;
+  lutq::QuantScratch sc;
+  void* extra = nullptr;
+  rc = quant_scratch(stream, scales ? 0 : nsc * sizeof(uint16_t) + 64, &sc, &extra);
+  if (rc) return rc;
+  uint16_t* sbuf = scales ? scales : reinterpret_cast<uint16_t*>(extra);
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = lutq::launch_quantize(sc, w, wdtype, lut, bits, N, K, group, rule, nullptr, sbuf,
+                                       false, s);
+  if (e != hipSuccess) return hip_fail(e);
+  for (int k = 0; k <= iters; ++k) {
+    e = lutq::launch_tune_pass(sc, w, wdtype, lut, bits, N, K, group, sbuf, k < iters, s);
+    if (e != hipSuccess) return hip_fail(e);
+    double err = 0.0;
+    int stop = 0;
+    e = hipMemcpyAsync(&err, sc.err_total, sizeof err, hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipMemcpyAsync(&stop, sc.stop, sizeof stop, hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return hip_fail(e);
+    if (errors) errors[k] = err;
+    if (k == iters || stop) break;
+    ++*updates;
   }
   return LUTQ_OK;
 }

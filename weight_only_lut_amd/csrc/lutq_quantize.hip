@@ -69,6 +69,7 @@ struct QuantParams {
   double* err_partial;     // per workgroup; null: no error
   float* extrema;          // tensor-wise: per-workgroup [max, min]
   uint16_t* tscale;        // tensor-wise: the scale (fp16 bits)
+  double* acc_partial;     // table tuning: per workgroup [2][L] sums (w s, s^2) per code
   long long n;             // weights
   int N, K, group, rule;
   long long nrows;         // groups (grouped) or 128-weight pieces (tensor-wise)
@@ -342,10 +343,20 @@ __device__ __forceinline__ void wave_lds_fence() {
 // Tensor-wise: the same with GL = 8 over 128-weight pieces and one scale.
 // GL == 0: groups of any multiple of 128 over 8 lanes, read twice (extrema,
 // then codes), 8 groups per step.
-template <int L, int GL, bool ERR, bool TENSOR, int WT>
+// ACC (table tuning): the scales are given (p.scales, or the tensor scale),
+// and every weight adds w s and s^2 to its code's sums: each thread keeps its
+// own sums in LDS, [part][code][thread] (lanes never share a bank), summed
+// in a fixed order at the end into the workgroup's partials.
+template <int L, int GL, bool ERR, bool TENSOR, int WT, bool ACC = false>
 __global__ __launch_bounds__(kQuantThreads) void quant_kernel(const QuantParams p) {
   constexpr int ES = WT == kWeightF32 ? 4 : 2;  // bytes per weight
+  static_assert(!ACC || ERR, "table tuning reports the error too");
   __shared__ double tval[L];
+  __shared__ double tacc[ACC ? 2 : 1][ACC ? L : 1][ACC ? kQuantThreads : 1];
+  if constexpr (ACC) {
+#pragma unroll
+    for (int c = 0; c < L; ++c) tacc[0][c][threadIdx.x] = tacc[1][c][threadIdx.x] = 0.0;
+  }
   __shared__ f32x4 areas[kQuantWaves][kMaxAreas][5];
   Table<L> t;
   load_table<L>(p.lut, t, tval);
@@ -403,6 +414,10 @@ __global__ __launch_bounds__(kQuantThreads) void quant_kernel(const QuantParams 
     if (p.scales && j == 0 && gi < p.nrows) p.scales[gi] = s16;
     build(s16);
   };
+  // Table tuning: the group's given scale.
+  auto prepare_given = [&](long long gi) __attribute__((always_inline)) {
+    build(gi < p.nrows ? p.scales[gi] : (uint16_t)0x3C00);
+  };
   auto extrema = [&](f32x4 v, int& kmx, int& kmn) __attribute__((always_inline)) {
     kmx = max(kmx, fkey(fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3]))));
     kmn = min(kmn, fkey(fminf(fminf(v[0], v[1]), fminf(v[2], v[3]))));
@@ -417,6 +432,12 @@ __global__ __launch_bounds__(kQuantThreads) void quant_kernel(const QuantParams 
       if constexpr (ERR) {
         const double d = (double)v[c] - tval[code] * s;
         err += active ? d * d : 0.0;
+      }
+      if constexpr (ACC) {
+        if (active) {
+          tacc[0][code][threadIdx.x] += (double)v[c] * s;
+          tacc[1][code][threadIdx.x] += s * s;
+        }
       }
     }
     return packed;
@@ -439,7 +460,9 @@ __global__ __launch_bounds__(kQuantThreads) void quant_kernel(const QuantParams 
     };
     auto step = [&](const f32x4 (&b)[4], long long unit) __attribute__((always_inline)) {
       const long long gi = unit * kGroups + r;
-      if constexpr (!TENSOR) {
+      if constexpr (!TENSOR && ACC) {
+        prepare_given(gi);
+      } else if constexpr (!TENSOR) {
         int kmx = INT_MIN, kmn = INT_MAX;
 #pragma unroll
         for (int i = 0; i < 4; ++i) extrema(b[i], kmx, kmn);
@@ -473,11 +496,15 @@ __global__ __launch_bounds__(kQuantThreads) void quant_kernel(const QuantParams 
     for (long long unit = wave0; unit < nunits; unit += nwaves) {
       const long long gi = unit * kGroups + r;
       const auto rs = tail_rsrc(p.w, unit * per_step, p.n, ES);
-      int kmx = INT_MIN, kmn = INT_MAX;
-      for (int q = 0; q < pieces; ++q)
+      if constexpr (ACC) {
+        prepare_given(gi);
+      } else {
+        int kmx = INT_MIN, kmn = INT_MAX;
+        for (int q = 0; q < pieces; ++q)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) extrema(load(rs, lane_off + q * kPiece + 32 * i), kmx, kmn);
-      prepare(kmx, kmn, gi);
+          for (int i = 0; i < 4; ++i) extrema(load(rs, lane_off + q * kPiece + 32 * i), kmx, kmn);
+        prepare(kmx, kmn, gi);
+      }
       const bool active = gi < p.nrows;
       const auto rc = tail_rsrc(p.codes, unit * per_step, p.codes ? p.n : 0, 1);
       for (int q = 0; q < pieces; ++q)
@@ -489,7 +516,45 @@ __global__ __launch_bounds__(kQuantThreads) void quant_kernel(const QuantParams 
         }
     }
   }
-  if constexpr (ERR) block_error(err, p.err_partial);
+  if constexpr (ERR) block_error(err, p.err_partial);  // contains a barrier
+  if constexpr (ACC) {
+    if (threadIdx.x < 2 * L) {
+      const int part = threadIdx.x / L, code = threadIdx.x % L;
+      double sum = 0.0;
+      for (int i = 0; i < kQuantThreads; ++i) sum += tacc[part][code][i];
+      p.acc_partial[((size_t)blockIdx.x * 2 + part) * L + code] = sum;
+    }
+  }
+}
+
+// Table tuning: the new table from all workgroups' sums (fixed order), each
+// used entry the fp16 value of sum(w s) / sum(s^2); an unused entry keeps
+// its value. If that would repeat an fp16 value, the table stays and *stop
+// is set. One workgroup.
+template <int L>
+__global__ __launch_bounds__(kQuantThreads) void tune_update_kernel(const double* part, int nblocks,
+                                                                    uint16_t* lut, int* stop) {
+  __shared__ uint16_t nt[L];
+  __shared__ int sstop;
+  const int i = threadIdx.x;
+  if (i < L) {
+    double num = 0.0, den = 0.0;
+    for (int b = 0; b < nblocks; ++b) {
+      num += part[((size_t)b * 2 + 0) * L + i];
+      den += part[((size_t)b * 2 + 1) * L + i];
+    }
+    nt[i] = den > 0.0 ? f64_to_f16_rne(num / den) : lut[i];
+  }
+  __syncthreads();
+  if (i == 0) {
+    bool dup = false;
+    for (int a = 0; a < L; ++a)
+      for (int b = a + 1; b < L; ++b) dup |= h2d(nt[a]) == h2d(nt[b]);
+    sstop = dup ? 1 : 0;
+    *stop = sstop;
+  }
+  __syncthreads();
+  if (i < L && !sstop) lut[i] = nt[i];
 }
 
 // Tensor-wise, pass 1: per-workgroup max and min.
@@ -644,7 +709,76 @@ hipError_t launch_w(const QuantScratch& sc, const QuantParams& p, int bits, bool
   }
 }
 
+// One tuning pass: codes under the given scales, the error and the per-code
+// sums (grouped: p.scales; tensor-wise: the scale already in sc.tscale).
+template <int L, int WT>
+hipError_t launch_tune_l(const QuantScratch& sc, const QuantParams& p0, hipStream_t s, int* nb) {
+  QuantParams p = p0;
+  p.err_partial = sc.err_partial;
+  p.acc_partial = sc.acc_partial;
+  int nblocks;
+  if (p.group != 0) {
+    p.nrows = p.n / p.group;
+    const int gl = p.group / kLaneElems;
+    const int per_step = gl == 8 || gl == 16 || gl == 32 || gl == 64 ? kWave / gl : 8;
+    nblocks = blocks_for((p.nrows + per_step - 1) / per_step);
+    switch (gl) {
+      case 8: quant_kernel<L, 8, true, false, WT, true><<<nblocks, kQuantThreads, 0, s>>>(p); break;
+      case 16: quant_kernel<L, 16, true, false, WT, true><<<nblocks, kQuantThreads, 0, s>>>(p); break;
+      case 32: quant_kernel<L, 32, true, false, WT, true><<<nblocks, kQuantThreads, 0, s>>>(p); break;
+      case 64: quant_kernel<L, 64, true, false, WT, true><<<nblocks, kQuantThreads, 0, s>>>(p); break;
+      default: quant_kernel<L, 0, true, false, WT, true><<<nblocks, kQuantThreads, 0, s>>>(p); break;
+    }
+  } else {
+    p.tscale = sc.tscale;
+    p.nrows = p.n / kPiece;
+    nblocks = blocks_for((p.nrows + kMaxAreas - 1) / kMaxAreas);
+    quant_kernel<L, 8, true, true, WT, true><<<nblocks, kQuantThreads, 0, s>>>(p);
+  }
+  error_sum_kernel<<<1, kQuantThreads, 0, s>>>(sc.err_partial, nblocks, sc.err_total);
+  *nb = nblocks;
+  return hipGetLastError();
+}
+
+template <int WT>
+hipError_t launch_tune_w(const QuantScratch& sc, const QuantParams& p, int bits, hipStream_t s,
+                         int* nb) {
+  switch (bits) {
+    case 2: return launch_tune_l<4, WT>(sc, p, s, nb);
+    case 3: return launch_tune_l<8, WT>(sc, p, s, nb);
+    default: return launch_tune_l<16, WT>(sc, p, s, nb);
+  }
+}
+
 }  // namespace
+
+hipError_t launch_tune_pass(const QuantScratch& sc, const void* w, int wdtype, const uint16_t* lut,
+                            int bits, int N, int K, int group, const uint16_t* scales,
+                            bool update, hipStream_t s) {
+  QuantParams p;
+  __builtin_memset(&p, 0, sizeof p);
+  p.w = w;
+  p.lut = lut;
+  p.scales = const_cast<uint16_t*>(scales);
+  p.n = (long long)N * K;
+  p.N = N;
+  p.K = K;
+  p.group = group;
+  int nb = 0;
+  hipError_t e;
+  switch (wdtype) {
+    case kWeightF16: e = launch_tune_w<kWeightF16>(sc, p, bits, s, &nb); break;
+    case kWeightBf16: e = launch_tune_w<kWeightBf16>(sc, p, bits, s, &nb); break;
+    default: e = launch_tune_w<kWeightF32>(sc, p, bits, s, &nb); break;
+  }
+  if (e != hipSuccess || !update) return e;
+  switch (bits) {
+    case 2: tune_update_kernel<4><<<1, kQuantThreads, 0, s>>>(sc.acc_partial, nb, const_cast<uint16_t*>(lut), sc.stop); break;
+    case 3: tune_update_kernel<8><<<1, kQuantThreads, 0, s>>>(sc.acc_partial, nb, const_cast<uint16_t*>(lut), sc.stop); break;
+    default: tune_update_kernel<16><<<1, kQuantThreads, 0, s>>>(sc.acc_partial, nb, const_cast<uint16_t*>(lut), sc.stop); break;
+  }
+  return hipGetLastError();
+}
 
 hipError_t launch_quantize(const QuantScratch& sc, const void* w, int wdtype, const uint16_t* lut,
                            int bits, int N, int K, int group, int rule, uint8_t* codes,
