@@ -1,0 +1,108 @@
+"""HIP graphs and streams: the launches captured in a graph and replayed
+several times (with eager work and synchronisation between replays) give
+every time the eager results bit for bit, for the plain, split-K, fused,
+zero-point, bf16 and binary-coded paths; split-K launches on two streams at
+once (each stream has its own scratch) give their single-stream results.
+
+A split-K launch allocates its scratch on first use, so each case runs once
+eagerly before capture, as the benchmark does.
+"""
+
+import numpy as np
+import pytest
+
+from synth import draw, workloads
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def lutq():
+    import weight_only_lut_amd as m
+    m.load_library()
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return m
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def bits16(t):
+    return t.view(torch.int16).clone()
+
+
+def _cases(lutq):
+    K = 1024
+    c, T, s, _ = workloads.small_case(4, "nf", 128, 1, 300, K, seed=950)
+    P = lutq.repack(dev(c), 4, 128)
+    Td, sd = dev(T), dev(s)
+    z = dev(np.random.default_rng(951).uniform(-0.5, 0.5, s.shape).astype(np.float16))
+    c2, T2, s2, _ = workloads.small_case(4, "nf", 128, 1, 64, K, seed=952)
+    P2 = lutq.repack(dev(c2), 4, 128)
+    T2d, s2d = dev(T2), dev(s2)
+    a = np.random.default_rng(953).uniform(0.01, 0.03, (3, 300, K // 128)).astype(np.float16)
+    cb = np.random.default_rng(954).integers(0, 8, (300, K)).astype(np.uint8)
+    Pb = lutq.repack(dev(cb), 3, 128)
+    x8 = dev(draw.activations(8, K, (955,)))
+    x32 = dev(draw.activations(32, K, (956,)))
+    xb = x8.to(torch.bfloat16)
+    ad = dev(a)
+    return [
+        ("gemv", lambda: lutq.matmul(x8, P, Td, sd, path="gemv")),
+        ("gemv split-K", lambda: lutq.matmul(x8, P, Td, sd, path="gemv", ksplit=4)),
+        ("mfma split-K", lambda: lutq.matmul(x32, P, Td, sd, path="mfma", ksplit=3)),
+        ("fused", lambda: lutq.matmul_multi(x8, [(P, Td, sd), (P2, T2d, s2d)], ksplit=2)),
+        ("zero points", lambda: lutq.matmul(x32, P, Td, sd, zeros=z, ksplit=2)),
+        ("bf16", lambda: lutq.matmul(xb, P, Td, sd, path="mfma", ksplit=2)),
+        ("bcq", lambda: lutq.matmul_bcq(x8, Pb, ad, ksplit=2)),
+    ]
+
+
+def test_graph_replays_equal_eager(lutq):
+    cases = _cases(lutq)
+    stream = torch.cuda.Stream()
+    eager, outs = {}, {}
+    with torch.cuda.stream(stream):
+        for name, f in cases:
+            r = f()
+            eager[name] = [bits16(t) for t in (r if isinstance(r, list) else [r])]
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        for name, f in cases:
+            r = f()
+            outs[name] = r if isinstance(r, list) else [r]
+    for rep in range(4):
+        for name in outs:                               # poison the outputs
+            for t in outs[name]:
+                t.view(torch.int16).fill_(0x7E00)
+        with torch.cuda.stream(stream):
+            graph.replay()
+        torch.cuda.synchronize()
+        for name in outs:
+            for got, want in zip(outs[name], eager[name]):
+                assert torch.equal(got.view(torch.int16), want), f"{name}, replay {rep}"
+        with torch.cuda.stream(stream):                 # eager work between replays
+            cases[1][1]()
+        torch.cuda.synchronize()
+
+
+def test_split_k_on_two_streams_at_once(lutq):
+    c, T, s, _ = workloads.small_case(4, "nf", 128, 1, 500, 2048, seed=960)
+    P = lutq.repack(dev(c), 4, 128)
+    Td, sd = dev(T), dev(s)
+    xs = [dev(draw.activations(8, 2048, (961, i))) for i in range(2)]
+    want = [bits16(lutq.matmul(x, P, Td, sd, path="gemv", ksplit=5)) for x in xs]
+    streams = [torch.cuda.Stream() for _ in range(2)]
+    for _ in range(3):
+        ys = []
+        for st, x in zip(streams, xs):
+            with torch.cuda.stream(st):
+                ys.append([lutq.matmul(x, P, Td, sd, path="gemv", ksplit=5) for _ in range(10)])
+        torch.cuda.synchronize()
+        for got_list, w in zip(ys, want):
+            for got in got_list:
+                assert torch.equal(got.view(torch.int16), w)
