@@ -184,6 +184,9 @@ __device__ __forceinline__ u32x4 lds_load_bcq(const uint32_t* table, uint32_t by
   if constexpr (BITS == 2) {
     const u32x2 v = *reinterpret_cast<const u32x2*>(b);
     return u32x4{v.x, v.y, 0u, 0u};
+  } else if constexpr (BITS == 3) {
+    const u32x3 v = *reinterpret_cast<const u32x3*>(b);  // the fourth dword is unused
+    return u32x4{v.x, v.y, v.z, 0u};
   } else {
     return *reinterpret_cast<const u32x4*>(b);
   }
