@@ -184,10 +184,9 @@ __device__ __forceinline__ u32x4 lds_load_bcq(const uint32_t* table, uint32_t by
   if constexpr (BITS == 2) {
     const u32x2 v = *reinterpret_cast<const u32x2*>(b);
     return u32x4{v.x, v.y, 0u, 0u};
-  } else if constexpr (BITS == 3) {
-    const u32x3 v = *reinterpret_cast<const u32x3*>(b);  // the fourth dword is unused
-    return u32x4{v.x, v.y, v.z, 0u};
   } else {
+    // 3 planes read 16 bytes too: a 12-byte LDS read measured slower
+    // (12.3 -> 14.6 us on a 14336 x 4096 matrix at batch 1)
     return *reinterpret_cast<const u32x4*>(b);
   }
 }
