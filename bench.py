@@ -635,11 +635,15 @@ def summarize_profile(kt_dir, fetch_dir, write_dir, command=""):
 # algorithmic bytes per launch: weights read, codes and scales written).
 _QN, _QK = 14336, 4096
 QUANT_KERNELS = (
-    ("quant_kernel<16, 8, false, false>", "grouped g128 INT4 (range rule): extrema, scale, codes",
+    ("quant_kernel<16, 8, false, false, 0, false>", "grouped g128 INT4 (range rule): extrema, scale, codes",
      4 * _QN * _QK + _QN * _QK + 2 * _QN * (_QK // 128)),
-    ("tensor_extrema_kernel", "tensor-wise NF4, pass 1: per-workgroup extrema", 4 * _QN * _QK),
+    ("tensor_extrema_kernel<0>", "tensor-wise NF4, pass 1: per-workgroup extrema", 4 * _QN * _QK),
     ("tensor_scale_kernel<16>", "tensor-wise NF4, pass 2: the scale (one workgroup)", None),
-    ("quant_kernel<16, 8, false, true>", "tensor-wise NF4, pass 3: codes", 4 * _QN * _QK + _QN * _QK),
+    ("quant_kernel<16, 8, false, true, 0, false>", "tensor-wise NF4, pass 3: codes",
+     4 * _QN * _QK + _QN * _QK),
+    ("quant_kernel<16, 8, true, false, 0, true>", "NF4 g128 table tuning, one pass: error and per-code sums",
+     4 * _QN * _QK + 2 * _QN * (_QK // 128)),
+    ("tune_update_kernel<16>", "NF4 table tuning: the new table (one workgroup)", None),
 )
 
 
