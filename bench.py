@@ -30,6 +30,7 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 MFMA, published
 CACHE_BYTES = 256 << 20        # Infinity Cache (MALL)
 COLD_SET_BYTES = 2 * CACHE_BYTES
+EXTRA_REPEATS = 3  # timed replays per secondary line (median)
 
 
 def algorithmic_bytes(M, N, K, bits, group):
@@ -79,13 +80,15 @@ class Case:
         lutq.matmul(self.x, self.packed[i % len(self.packed)], self.lut, self.scales, out=self.y)
 
 
-def time_case(lutq, torch, case, steps, warmup):
+def time_case(lutq, torch, case, steps, warmup, repeats=1):
     """Average microseconds per call over exactly `steps` back-to-back calls.
 
     `warmup` eager calls, then the `steps` calls are captured in a HIP graph,
     replayed once untimed, and replayed once more between HIP events recorded
     on the stream the kernels run on (host-side launch cost stays outside the
-    timed region), with a device synchronization on both sides.
+    timed region), with a device synchronization on both sides. With
+    `repeats` > 1 the timed replay is repeated and the median returned (the
+    secondary lines: one replay of a few tens of calls varies by ~10%).
     """
     stream = torch.cuda.Stream()
     with torch.cuda.stream(stream):
@@ -99,13 +102,16 @@ def time_case(lutq, torch, case, steps, warmup):
     with torch.cuda.stream(stream):
         graph.replay()
     torch.cuda.synchronize()
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    with torch.cuda.stream(stream):  # replay() launches on the current stream
-        start.record()
-        graph.replay()
-        stop.record()
-    torch.cuda.synchronize()
-    return start.elapsed_time(stop) * 1e3 / steps
+    times = []
+    for _ in range(repeats):
+        start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(stream):  # replay() launches on the current stream
+            start.record()
+            graph.replay()
+            stop.record()
+        torch.cuda.synchronize()
+        times.append(start.elapsed_time(stop) * 1e3 / steps)
+    return sorted(times)[len(times) // 2]
 
 
 def cpu_baseline(case, budget_s=15.0):
@@ -223,7 +229,7 @@ def variant_section(lutq, torch, args):
         rec = {}
         for mode in ("plain", "bf16", "zeros", "types"):
             vc.mode = mode
-            us = time_case(lutq, torch, vc, steps, args.warmup)
+            us = time_case(lutq, torch, vc, steps, args.warmup, repeats=EXTRA_REPEATS)
             nbytes = vc.base_bytes + vc.extra_bytes[mode]
             rec[mode] = {"us": round(us, 3), "GBps": round(nbytes / (us * 1e-6) / 1e9, 1)}
             log(f"[bench] variants M={M} {mode}: {us:.2f} us")
@@ -231,7 +237,7 @@ def variant_section(lutq, torch, args):
         del vc
         torch.cuda.empty_cache()
         bc = BcqCase(lutq, torch, "int4_up_proj", M, q=3)
-        us = time_case(lutq, torch, bc, steps, args.warmup)
+        us = time_case(lutq, torch, bc, steps, args.warmup, repeats=EXTRA_REPEATS)
         out[f"bcq3_{bc.N}x{bc.K}_M{M}"] = {"us": round(us, 3),
                                            "GBps": round(bc.bytes / (us * 1e-6) / 1e9, 1)}
         log(f"[bench] variants M={M} bcq q=3: {us:.2f} us")
@@ -272,9 +278,9 @@ def fused_section(lutq, torch, args):
         for M in (1, 16):
             fc = FusedCase(lutq, torch, "nf4_layer", mats, M)
             fc.fused = False
-            sep = time_case(lutq, torch, fc, steps, args.warmup)
+            sep = time_case(lutq, torch, fc, steps, args.warmup, repeats=EXTRA_REPEATS)
             fc.fused = True
-            fus = time_case(lutq, torch, fc, steps, args.warmup)
+            fus = time_case(lutq, torch, fc, steps, args.warmup, repeats=EXTRA_REPEATS)
             out[f"{label}_M{M}"] = {
                 "separate_us": round(sep, 3), "fused_us": round(fus, 3),
                 "speedup": round(sep / fus, 3),
@@ -333,7 +339,7 @@ def quantizer_section(lutq, torch, args):
     for label, group, rule, table in (("int4_g128_range", 128, "range", None),
                                       ("nf4_tensor_absmax", 0, "absmax", "nf")):
         qc = QuantCase(lutq, torch, "int4_up_proj", group, rule, table)
-        us = time_case(lutq, torch, qc, max(20, args.steps // 10), args.warmup)
+        us = time_case(lutq, torch, qc, max(20, args.steps // 10), args.warmup, repeats=EXTRA_REPEATS)
         gbps = qc.bytes / (us * 1e-6) / 1e9
         W, T = qc.host
         rows = 256
@@ -431,13 +437,13 @@ def main():
     if not args.no_batch32:
         b32 = Case(lutq, torch, "log4_70b", None, 32, cold=True)
         p32 = lutq.plan(32, b32.N, b32.K, 4)
-        k_us = time_case(lutq, torch, b32, max(20, args.steps // 4), args.warmup)
+        k_us = time_case(lutq, torch, b32, max(20, args.steps // 4), args.warmup, repeats=EXTRA_REPEATS)
         wk_us = None
         if not args.no_warm:
             warm32 = Case.__new__(Case)
             warm32.__dict__.update(b32.__dict__)
             warm32.packed = b32.packed[:1]
-            wk_us = time_case(lutq, torch, warm32, max(20, args.steps // 4), args.warmup)
+            wk_us = time_case(lutq, torch, warm32, max(20, args.steps // 4), args.warmup, repeats=EXTRA_REPEATS)
             del warm32
         tf = b32.flops / (k_us * 1e-6) / 1e12
         extra["batch32"] = {
@@ -549,7 +555,7 @@ def copy_calibration(torch):
 # template arguments: bits, MFMA, batch rows, grouped, zero points, data types,
 # binary coding, bf16, prefetch depth, tiles per wave, waves, occupancy
 HEADLINE_KERNEL = "matmul_kernel<4, false, 1, true, false, false, false, false, 2, 2, 8, 4>"
-BATCH32_KERNEL = "matmul_kernel<4, true, 32, false, false, false, false, false, 2, 8, 4, 2>"
+BATCH32_KERNEL = "matmul_kernel<4, true, 32, false, false, false, false, false, 2, 7, 4, 2>"
 
 
 def _read_csv(path):

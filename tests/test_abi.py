@@ -135,7 +135,7 @@ def test_matmul_validates_before_launching(lib):
     d3 = _desc(bits=3)
     assert lib.lutq_matmul_bcq(x, ctypes.byref(d3), sc, y, 1, 64, 256, ctypes.byref(o),
                                None) == EUNSUP
-    for path, tiles in [(0, 2), (1, 8), (1, 4), (2, 1), (2, 3), (1, -1)]:
+    for path, tiles in [(0, 2), (1, 8), (1, 4), (1, 7), (2, 1), (2, 3), (2, 6), (1, -1)]:
         o = _lib.Options(); o.path, o.tiles = path, tiles
         assert call(opts=ctypes.byref(o)) == EINVAL, (path, tiles)
     # nothing to do: M == 0 (no HIP call is made)
@@ -324,10 +324,17 @@ def test_plan_switches_paths_by_batch():
 
 
 def test_plan_shapes_and_split():
-    # Batch 32 on a wide matrix: 8 tiles per wave, no split.
-    assert lutq.plan(32, 28672, 8192, 4) == {"path": "mfma", "ksplit": 1, "tiles": 8}
-    # A batch slice of 16 rows keeps 4 tiles per wave.
-    assert lutq.plan(16, 28672, 8192, 4)["tiles"] == 4
+    # 28672 rows = 1792 tiles = 7 per CU: 7 tiles per wave (one workgroup
+    # on every CU) at any MFMA batch, no split.
+    assert lutq.plan(32, 28672, 8192, 4) == {"path": "mfma", "ksplit": 1, "tiles": 7}
+    assert lutq.plan(16, 28672, 8192, 4)["tiles"] == 7
+    assert lutq.plan(2, 28672, 4096, 4)["tiles"] == 7
+    # Wider (> 7 tiles per CU): 8 tiles per wave at 32 batch rows, 4 at 16.
+    assert lutq.plan(32, 32768, 8192, 4) == {"path": "mfma", "ksplit": 1, "tiles": 8}
+    assert lutq.plan(16, 32768, 8192, 4)["tiles"] == 4
+    # Exactly 6 tiles per CU keeps the earlier rules: 8 at 32 rows, 4 at 16.
+    assert lutq.plan(32, 24576, 8192, 4)["tiles"] == 8
+    assert lutq.plan(16, 24576, 8192, 4)["tiles"] == 4
     # GEMV: 2 tiles per wave only when that still gives 2 row blocks per CU
     assert lutq.plan(1, 14336, 4096, 4) == {"path": "gemv", "ksplit": 1, "tiles": 2}
     assert lutq.plan(1, 4096, 4096, 4) == {"path": "gemv", "ksplit": 1, "tiles": 1}

@@ -50,7 +50,7 @@ def assert_close(y, x, c, T, s, group, z, rows=None):
     assert ok, f"max err/bound = {worst:.3g}"
 
 
-SHAPES = [("gemv", 1), ("gemv", 2), ("mfma", 2), ("mfma", 4), ("mfma", 8)]
+SHAPES = [("gemv", 1), ("gemv", 2), ("mfma", 2), ("mfma", 4), ("mfma", 7), ("mfma", 8)]
 
 
 @pytest.mark.parametrize("path,tiles", SHAPES)

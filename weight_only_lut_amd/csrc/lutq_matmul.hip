@@ -626,24 +626,29 @@ void matmul_kernel(const MatmulParams pk) {
   if (tid == 0) __hip_atomic_store(p.counters + rb, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Kernel shapes. GEMV: 8 waves, each covering 1 or 2 tiles. MFMA: 8 tiles
-// per wave with 4 waves (batch 32 on wide matrices: each activation fragment
-// feeds 8 tiles), 4 tiles with 4 waves, or 2 tiles with 8 waves (narrow
+// Kernel shapes. GEMV: 8 waves, each covering 1 or 2 tiles. MFMA: 8 or 7
+// tiles per wave with 4 waves (wide matrices: each activation fragment feeds
+// 8 or 7 tiles), 4 tiles with 4 waves, or 2 tiles with 8 waves (narrow
 // matrices, which need many workgroups to fill the device).
 constexpr int kPf = 2;
 
 // Host-side shape rules: compiled once (in the width-4 object).
 #if LUTQ_MATMUL_BITS == 4
 bool tiles_supported(int path, int tiles) {
-  if (path == kPathMfma) return tiles == 2 || tiles == 4 || tiles == 8;
+  if (path == kPathMfma) return tiles == 2 || tiles == 4 || tiles == 7 || tiles == 8;
   return tiles == 1 || tiles == 2;
 }
 
 // Measured on MI355X over the Llama-3-8B and Llama-70B projection shapes: the
 // widest shape that still gives most CUs a workgroup wins, except that 8
-// tiles only pay at 32 batch rows.
+// tiles only pay at 32 batch rows. MFMA workgroups are bound by their own
+// lookups, so the busiest CU sets the time: 7 tiles when that puts exactly
+// one workgroup on every CU (28672 rows: 8 tiles leave 32 of 256 CUs idle,
+// 4 tiles put two workgroups on 192 of them; 31.6 -> 27.4 us at 32 batch
+// rows, 26.6 -> 21.6 us at 16).
 int pick_tiles(int path, int mrows, int ntiles, int cus) {
   if (path != kPathMfma) return ntiles >= 2 * cus ? 2 : 1;
+  if (ntiles > 6 * cus && ntiles <= 7 * cus) return 7;
   if (mrows > 16 && ntiles >= 6 * cus) return 8;
   if (ntiles >= 2 * cus) return 4;
   return 2;
@@ -654,10 +659,10 @@ template <int BITS, bool MFMA, int MROWS, int TPW, int WAVES, int OCC>
 static hipError_t launch_t(const MatmulParams& p, hipStream_t s) {
   const int nrb = p.nseg > 1 ? p.nrb : (p.ntiles + TPW - 1) / TPW;
   const dim3 grid((unsigned)nrb * (unsigned)p.ksplit);
-  // Grouped scales at 32 batch rows x 8 tiles need more than the 256
-  // registers of two waves per SIMD; this shape runs on few enough
-  // workgroups that one wave per SIMD costs little.
-  constexpr int OCC_G = (MFMA && MROWS == 32 && TPW == 8) ? 1 : OCC;
+  // Grouped scales at 32 batch rows x 7 or 8 tiles need more than the 256
+  // registers of two waves per SIMD; these shapes run on at most one
+  // workgroup per CU, so one wave per SIMD costs nothing.
+  constexpr int OCC_G = (MFMA && MROWS == 32 && TPW >= 7) ? 1 : OCC;
   // Chunks in flight per wave: 4 for one-tile GEMV at one batch row (narrow
   // matrices, where each wave has few chunks and little else to overlap the
   // loads with; measured 4.5 -> 4.0 us on a 1024 x 4096 projection, 10.0 ->
@@ -698,6 +703,7 @@ template <int BITS, int MROWS>
 static hipError_t launch_mfma(const MatmulParams& p, int tiles, hipStream_t s) {
   switch (tiles) {
     case 8: return launch_t<BITS, true, MROWS, 8, 4, 2>(p, s);
+    case 7: return launch_t<BITS, true, MROWS, 7, 4, 2>(p, s);
     case 4: return launch_t<BITS, true, MROWS, 4, 4, 2>(p, s);
     default: return launch_t<BITS, true, MROWS, 2, 8, 2>(p, s);
   }

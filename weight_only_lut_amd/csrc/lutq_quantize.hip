@@ -527,26 +527,37 @@ __global__ __launch_bounds__(kQuantThreads) void quant_kernel(const QuantParams 
   }
 }
 
-// Table tuning: the new table from all workgroups' sums (fixed order), each
-// used entry the fp16 value of sum(w s) / sum(s^2); an unused entry keeps
-// its value. If that would repeat an fp16 value, the table stays and *stop
-// is set. One workgroup.
+// Table tuning: the new table from all workgroups' sums, each used entry the
+// fp16 value of sum(w s) / sum(s^2); an unused entry keeps its value. If that
+// would repeat an fp16 value, the table stays and *stop is set. One
+// workgroup of kTuneThreads: thread t adds sum t % 2L of the workgroups
+// t / 2L, t / 2L + S, ... (S = kTuneThreads / 2L slots; neighbouring threads
+// read neighbouring doubles), then the S slot sums are added in slot order,
+// so the result does not depend on timing.
+constexpr int kTuneThreads = 1024;
 template <int L>
-__global__ __launch_bounds__(kQuantThreads) void tune_update_kernel(const double* part, int nblocks,
-                                                                    uint16_t* lut, int* stop) {
+__global__ __launch_bounds__(kTuneThreads) void tune_update_kernel(const double* part, int nblocks,
+                                                                   uint16_t* lut, int* stop) {
+  constexpr int kSums = 2 * L, kSlots = kTuneThreads / kSums;
+  __shared__ double red[kSlots][kSums];
   __shared__ uint16_t nt[L];
   __shared__ int sstop;
-  const int i = threadIdx.x;
-  if (i < L) {
+  const int t = threadIdx.x, sum = t % kSums, slot = t / kSums;
+  double acc = 0.0;
+#pragma unroll 8
+  for (int b = slot; b < nblocks; b += kSlots) acc += part[(size_t)b * kSums + sum];
+  red[slot][sum] = acc;
+  __syncthreads();
+  if (t < L) {
     double num = 0.0, den = 0.0;
-    for (int b = 0; b < nblocks; ++b) {
-      num += part[((size_t)b * 2 + 0) * L + i];
-      den += part[((size_t)b * 2 + 1) * L + i];
+    for (int j = 0; j < kSlots; ++j) {
+      num += red[j][t];
+      den += red[j][L + t];
     }
-    nt[i] = den > 0.0 ? f64_to_f16_rne(num / den) : lut[i];
+    nt[t] = den > 0.0 ? f64_to_f16_rne(num / den) : lut[t];
   }
   __syncthreads();
-  if (i == 0) {
+  if (t == 0) {
     bool dup = false;
     for (int a = 0; a < L; ++a)
       for (int b = a + 1; b < L; ++b) dup |= h2d(nt[a]) == h2d(nt[b]);
@@ -554,7 +565,7 @@ __global__ __launch_bounds__(kQuantThreads) void tune_update_kernel(const double
     *stop = sstop;
   }
   __syncthreads();
-  if (i < L && !sstop) lut[i] = nt[i];
+  if (t < L && !sstop) lut[t] = nt[t];
 }
 
 // Tensor-wise, pass 1: per-workgroup max and min.
@@ -773,9 +784,9 @@ hipError_t launch_tune_pass(const QuantScratch& sc, const void* w, int wdtype, c
   }
   if (e != hipSuccess || !update) return e;
   switch (bits) {
-    case 2: tune_update_kernel<4><<<1, kQuantThreads, 0, s>>>(sc.acc_partial, nb, const_cast<uint16_t*>(lut), sc.stop); break;
-    case 3: tune_update_kernel<8><<<1, kQuantThreads, 0, s>>>(sc.acc_partial, nb, const_cast<uint16_t*>(lut), sc.stop); break;
-    default: tune_update_kernel<16><<<1, kQuantThreads, 0, s>>>(sc.acc_partial, nb, const_cast<uint16_t*>(lut), sc.stop); break;
+    case 2: tune_update_kernel<4><<<1, kTuneThreads, 0, s>>>(sc.acc_partial, nb, const_cast<uint16_t*>(lut), sc.stop); break;
+    case 3: tune_update_kernel<8><<<1, kTuneThreads, 0, s>>>(sc.acc_partial, nb, const_cast<uint16_t*>(lut), sc.stop); break;
+    default: tune_update_kernel<16><<<1, kTuneThreads, 0, s>>>(sc.acc_partial, nb, const_cast<uint16_t*>(lut), sc.stop); break;
   }
   return hipGetLastError();
 }
