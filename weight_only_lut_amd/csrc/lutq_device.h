@@ -123,6 +123,15 @@ __device__ __forceinline__ uint32_t lds_load(const uint32_t* table, uint32_t byt
   return *reinterpret_cast<const uint32_t*>(reinterpret_cast<const char*>(table) + byte_addr);
 }
 
+// Keeps the compiler from moving this wave's memory operations across the
+// call, for data that lanes exchange through LDS. It emits no instruction:
+// LDS executes one wave's operations in issue order.
+__device__ __forceinline__ void wave_lds_order() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // Decode the two codes of a pair index for table building.
 template <int BITS>
 __device__ __forceinline__ void pair_codes(uint32_t idx, uint32_t& c0, uint32_t& c1) {

@@ -8,11 +8,12 @@
 // the per-group partial sum, so table values enter the products unscaled and
 // exact, and each group costs one fp32 multiply-add.
 //
-// Workgroup: 8 waves; the block covers 4 tiles (64 rows) and a range of
-// 128-code chunks, dealt to the waves round-robin. Each wave streams the four
-// 1 KiB (at 4 bits) blocks of a chunk with one coalesced load per lane,
-// keeping several chunks in flight; codes, scales and activations of a chunk are
-// loaded together so the in-order load counter never waits on a prefetch.
+// Workgroup: 4 or 8 waves; the block covers TPW tiles of 16 rows (1 to 8)
+// and a range of 128-code chunks, dealt to the waves round-robin. Each wave
+// streams the TPW 1 KiB (at 4 bits) blocks of a chunk, one coalesced load per
+// lane and tile, keeping several chunks in flight; codes, scales and
+// activations of a chunk are loaded together so the in-order load counter
+// never waits on a prefetch.
 //
 // Two compute policies share that skeleton:
 //  GEMV (batch 1..8): lane L = 16q + r owns row r of a tile and k-quarter q.
@@ -22,8 +23,9 @@
 //    quarter. The four quarters are summed across lanes at the end.
 //  MFMA (batch up to 32): the decoded pairs of k-step j are exactly the B
 //    operand of v_mfma_f32_16x16x32_f16 (lane: row r, k = 32j + 8q .. +7);
-//    the A operand is the matching 16x32 activation tile straight from
-//    global memory (L2-resident).
+//    the A operand is the matching 16x32 activation tile, loaded from
+//    global memory (L2-resident) in fragment order, or at 32 batch rows on
+//    8 waves loaded row-contiguous and rearranged through LDS.
 // Waves are combined in LDS in a fixed order; splits along K across
 // workgroups are combined by the last-arriving workgroup, again in a fixed
 // order, so results are deterministic.
@@ -71,20 +73,30 @@ void matmul_kernel(const MatmulParams pk) {
   constexpr bool XSUM = ZP || BCQ;        // needs the groups' activation sums
   constexpr int ROWS = TPW * kTileRows;
   constexpr int MT = MFMA ? MROWS / 16 : 1;
+  // 32 batch rows on 8 waves (MFMA): activations are loaded row-contiguous
+  // and turned into fragments through a per-wave LDS area (see compute). At
+  // one wave per SIMD (4 waves) the LDS round trip sits in the wave's critical
+  // path and costs more than the scattered loads it replaces (measured).
+  constexpr bool XST = MFMA && MROWS == 32 && WAVES == 8;
+  constexpr int kXRowBytes = 2 * kChunk;                 // one row of a chunk
+  constexpr int kXStageWords = MROWS * kXRowBytes / 4;   // per wave
   constexpr int SLOT = 4 * BITS;
   constexpr int BLOCK = kWave * SLOT;
   static_assert(PF >= 2, "at least one chunk in flight while another is computed");
-  // Cross-wave reduction buffer (reuses the table's LDS): [wave][m][row] with
-  // a row pitch of ROWS + 4, so that the MFMA accumulator stores (lanes r, q
-  // -> rows r, batch rows 4q + e) and the row-contiguous final reads both
-  // spread over distinct banks.
+  // Cross-wave reduction buffer (reuses the LDS of the table and the
+  // activation staging areas): [wave][m][row] with a row pitch of ROWS + 4,
+  // so that the MFMA accumulator stores (lanes r, q -> rows r, batch rows
+  // 4q + e) and the row-contiguous final reads both spread over distinct
+  // banks.
   constexpr int RP = ROWS + 4;
   static_assert(ROWS % 16 == 0, "pitch rule assumes whole tiles");
   constexpr int kRedWords = kWaves * MROWS * RP;
-  constexpr int kLdsWords = kRedWords > kTableWords ? kRedWords : kTableWords;
+  constexpr int kMainWords = kTableWords + (XST ? kWaves * kXStageWords : 0);
+  constexpr int kLdsWords = kRedWords > kMainWords ? kRedWords : kMainWords;
   static_assert(kThreads >= kPairEntries, "table build needs one thread per entry");
 
   __shared__ __attribute__((aligned(16))) uint32_t table[kLdsWords];
+  uint32_t* const xstage = table + kTableWords;  // 32 batch rows: per-wave areas
   __shared__ int arrive_last;
 
   const int tid = threadIdx.x;
@@ -182,6 +194,19 @@ void matmul_kernel(const MatmulParams pk) {
   for (int mt = 0; mt < MT; ++mt)
     aboff[mt] = mt * 16 + r < p.M ? 2u * ((uint32_t)(mt * 16 + r) * (uint32_t)p.K + 8 * q)
                                   : kRowOutOfRange;
+  // 32 batch rows: load i brings rows 4i .. 4i + 3 of the chunk, lane 16v + u
+  // the 16-byte piece u (k = 8u .. 8u + 7) of row 4i + v, so each row is one
+  // contiguous 256-byte run (the fragment order above puts 16 rows in 16
+  // consecutive lanes: 64 separate accesses per load)
+  uint32_t xloff[XST ? 8 : 1];
+  if constexpr (XST) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int row = 4 * i + (lane >> 4);
+      xloff[i] = row < p.M ? 2u * (uint32_t)row * (uint32_t)p.K + 16u * (uint32_t)(lane & 15)
+                           : kRowOutOfRange;
+    }
+  }
 
   SlotRegs<BITS> cbuf[PF][TPW];
   uint32_t scur[QS][TPW], snext[QS][TPW];  // scale (alpha) batches: in use, in flight
@@ -189,6 +214,7 @@ void matmul_kernel(const MatmulParams pk) {
   uint32_t tcur[TYPED ? TPW : 1], tnext[TYPED ? TPW : 1];  // type-id batches
   uint32_t xbuf[PF][MFMA ? 1 : MROWS];
   u32x4 abuf[PF][MT][MFMA ? 4 : 1];
+  u32x4 xl[XST ? PF : 1][XST ? 8 : 1];  // 32 batch rows: the row-contiguous pieces
 
   // chunk of pipeline step i, or -1 past the wave's last chunk
   auto chunk = [&](int i) { return i < nmine ? cw + i * kWaves : -1; };
@@ -204,6 +230,11 @@ void matmul_kernel(const MatmulParams pk) {
 #pragma unroll
       for (int m = 0; m < MROWS; ++m)
         xbuf[s][m] = __builtin_amdgcn_raw_buffer_load_b32(xrsrc, xoff[m] + xb, 0, 0);
+    } else if constexpr (XST) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        xl[s][i] = __builtin_bit_cast(
+            u32x4, __builtin_amdgcn_raw_buffer_load_b128(xrsrc, xloff[i] + xb, 0, 0));
     } else {
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
@@ -382,6 +413,28 @@ void matmul_kernel(const MatmulParams pk) {
           dst[j].w = lds_load(table, pair_addr(idx4, lb, 3));
         }
       };
+      if constexpr (XST) {
+        // The chunk's 32 x 128 activations into this wave's LDS area, then
+        // back out as fragments (lane r, q of fragment mt, j: row 16 mt + r,
+        // piece 4j + q). Row `row` stores piece u at position u ^ (row & 15):
+        // the 16 lanes writing a row cover every bank once, and the 16 lanes
+        // reading one piece of rows 16 mt + 0..15 hit distinct banks.
+        char* xw = reinterpret_cast<char*>(xstage + wave * kXStageWords);
+        wave_lds_order();  // the previous chunk's fragment reads come first
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int row = 4 * i + (lane >> 4);
+          *reinterpret_cast<u32x4*>(xw + row * kXRowBytes + 16 * ((lane & 15) ^ (row & 15))) =
+              xl[s][i];
+        }
+        wave_lds_order();
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            abuf[s][mt][j] = *reinterpret_cast<const u32x4*>(
+                xw + (16 * mt + r) * kXRowBytes + 16 * ((4 * j + q) ^ r));
+      }
       // bf16 activations: each batch row's chunk (32 values per lane, its
       // four quarters in lanes r, r + 16, r + 32, r + 48) to fp16 under the
       // chunk's shift; fe[mt][e] undoes it for accumulator row 4q + e
@@ -628,8 +681,9 @@ void matmul_kernel(const MatmulParams pk) {
 
 // Kernel shapes. GEMV: 8 waves, each covering 1 or 2 tiles. MFMA: 8 or 7
 // tiles per wave with 4 waves (wide matrices: each activation fragment feeds
-// 8 or 7 tiles), 4 tiles with 4 waves, or 2 tiles with 8 waves (narrow
-// matrices, which need many workgroups to fill the device).
+// 8 or 7 tiles), 4 tiles with 4 waves (8 at 32 batch rows, which stage their
+// activations through LDS), or 2 tiles with 8 waves (narrow matrices, which
+// need many workgroups to fill the device).
 constexpr int kPf = 2;
 
 // Host-side shape rules: compiled once (in the width-4 object).
@@ -704,7 +758,7 @@ static hipError_t launch_mfma(const MatmulParams& p, int tiles, hipStream_t s) {
   switch (tiles) {
     case 8: return launch_t<BITS, true, MROWS, 8, 4, 2>(p, s);
     case 7: return launch_t<BITS, true, MROWS, 7, 4, 2>(p, s);
-    case 4: return launch_t<BITS, true, MROWS, 4, 4, 2>(p, s);
+    case 4: return launch_t<BITS, true, MROWS, 4, MROWS == 32 ? 8 : 4, 2>(p, s);
     default: return launch_t<BITS, true, MROWS, 2, 8, 2>(p, s);
   }
 }
