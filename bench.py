@@ -554,8 +554,8 @@ def copy_calibration(torch):
 
 # template arguments: bits, MFMA, batch rows, grouped, zero points, data types,
 # binary coding, bf16, prefetch depth, tiles per wave, waves, occupancy
-HEADLINE_KERNEL = "matmul_kernel<4, false, 1, true, false, false, false, false, 2, 2, 8, 4>"
-BATCH32_KERNEL = "matmul_kernel<4, true, 32, false, false, false, false, false, 2, 7, 4, 2>"
+HEADLINE_KERNEL = "matmul_kernel<4, false, 1, true, false, false, false, false, 2, 2, 8, 4, false>"
+BATCH32_KERNEL = "matmul_kernel<4, true, 32, false, false, false, false, false, 2, 7, 4, 2, false>"
 
 
 def _read_csv(path):

@@ -24,8 +24,8 @@
 //  MFMA (batch up to 32): the decoded pairs of k-step j are exactly the B
 //    operand of v_mfma_f32_16x16x32_f16 (lane: row r, k = 32j + 8q .. +7);
 //    the A operand is the matching 16x32 activation tile, loaded from
-//    global memory (L2-resident) in fragment order, or at 32 batch rows on
-//    8 waves loaded row-contiguous and rearranged through LDS.
+//    global memory (L2-resident) in fragment order, or (8-wave shapes from
+//    9 batch rows) loaded row-contiguous and rearranged through LDS.
 // Waves are combined in LDS in a fixed order; splits along K across
 // workgroups are combined by the last-arriving workgroup, again in a fixed
 // order, so results are deterministic.
@@ -38,9 +38,10 @@ namespace lutq {
 // GROUPED: per-group (else per-tensor) scales; PF: register slots of the load
 // pipeline (PF - 1 chunks in flight while one is computed);
 // TPW: 16-row tiles per wave (and per workgroup); WAVES: waves per workgroup,
-// which split the K range; OCC: waves per SIMD the register budget targets.
+// which split the K range; OCC: waves per SIMD the register budget targets;
+// XS: MFMA activations staged through LDS (see below).
 template <int BITS, bool MFMA, int MROWS, bool GROUPED, bool ZP, bool TYPED, bool BCQ, bool BF16, int PF,
-          int TPW, int WAVES, int OCC>
+          int TPW, int WAVES, int OCC, bool XS>
 __global__ __launch_bounds__(WAVES * kWave) __attribute__((amdgpu_waves_per_eu(OCC)))
 void matmul_kernel(const MatmulParams pk) {
   // A fused launch covers several matrices: this workgroup's row block picks
@@ -73,13 +74,16 @@ void matmul_kernel(const MatmulParams pk) {
   constexpr bool XSUM = ZP || BCQ;        // needs the groups' activation sums
   constexpr int ROWS = TPW * kTileRows;
   constexpr int MT = MFMA ? MROWS / 16 : 1;
-  // 32 batch rows on 8 waves (MFMA): activations are loaded row-contiguous
-  // and turned into fragments through a per-wave LDS area (see compute). At
-  // one wave per SIMD (4 waves) the LDS round trip sits in the wave's critical
-  // path and costs more than the scattered loads it replaces (measured).
-  constexpr bool XST = MFMA && MROWS == 32 && WAVES == 8;
+  // Staged (XS): activations are loaded row-contiguous and turned into
+  // fragments through a per-wave LDS area (see compute), XL loads of 4 rows
+  // per chunk. The launch picks it for 8-wave shapes only: at one wave per
+  // SIMD the LDS round trip sits in the wave's critical path and costs more
+  // than the scattered loads it replaces (measured).
+  static_assert(!XS || MFMA, "staging feeds MFMA fragments");
+  constexpr bool XST = XS;
+  constexpr int XL = MROWS / 4;
   constexpr int kXRowBytes = 2 * kChunk;                 // one row of a chunk
-  constexpr int kXStageWords = MROWS * kXRowBytes / 4;   // per wave
+  constexpr int kXStageWords = MROWS * kXRowBytes / 4;   // per wave (4 or 8 KiB)
   constexpr int SLOT = 4 * BITS;
   constexpr int BLOCK = kWave * SLOT;
   static_assert(PF >= 2, "at least one chunk in flight while another is computed");
@@ -96,7 +100,7 @@ void matmul_kernel(const MatmulParams pk) {
   static_assert(kThreads >= kPairEntries, "table build needs one thread per entry");
 
   __shared__ __attribute__((aligned(16))) uint32_t table[kLdsWords];
-  uint32_t* const xstage = table + kTableWords;  // 32 batch rows: per-wave areas
+  uint32_t* const xstage = table + kTableWords;  // staged: per-wave areas
   __shared__ int arrive_last;
 
   const int tid = threadIdx.x;
@@ -194,14 +198,14 @@ void matmul_kernel(const MatmulParams pk) {
   for (int mt = 0; mt < MT; ++mt)
     aboff[mt] = mt * 16 + r < p.M ? 2u * ((uint32_t)(mt * 16 + r) * (uint32_t)p.K + 8 * q)
                                   : kRowOutOfRange;
-  // 32 batch rows: load i brings rows 4i .. 4i + 3 of the chunk, lane 16v + u
-  // the 16-byte piece u (k = 8u .. 8u + 7) of row 4i + v, so each row is one
+  // Staged: load i brings rows 4i .. 4i + 3 of the chunk, lane 16v + u the
+  // 16-byte piece u (k = 8u .. 8u + 7) of row 4i + v, so each row is one
   // contiguous 256-byte run (the fragment order above puts 16 rows in 16
   // consecutive lanes: 64 separate accesses per load)
-  uint32_t xloff[XST ? 8 : 1];
+  uint32_t xloff[XST ? XL : 1];
   if constexpr (XST) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < XL; ++i) {
       const int row = 4 * i + (lane >> 4);
       xloff[i] = row < p.M ? 2u * (uint32_t)row * (uint32_t)p.K + 16u * (uint32_t)(lane & 15)
                            : kRowOutOfRange;
@@ -214,7 +218,7 @@ void matmul_kernel(const MatmulParams pk) {
   uint32_t tcur[TYPED ? TPW : 1], tnext[TYPED ? TPW : 1];  // type-id batches
   uint32_t xbuf[PF][MFMA ? 1 : MROWS];
   u32x4 abuf[PF][MT][MFMA ? 4 : 1];
-  u32x4 xl[XST ? PF : 1][XST ? 8 : 1];  // 32 batch rows: the row-contiguous pieces
+  u32x4 xl[XST ? PF : 1][XST ? XL : 1];  // staged: the row-contiguous pieces
 
   // chunk of pipeline step i, or -1 past the wave's last chunk
   auto chunk = [&](int i) { return i < nmine ? cw + i * kWaves : -1; };
@@ -232,7 +236,7 @@ void matmul_kernel(const MatmulParams pk) {
         xbuf[s][m] = __builtin_amdgcn_raw_buffer_load_b32(xrsrc, xoff[m] + xb, 0, 0);
     } else if constexpr (XST) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
+      for (int i = 0; i < XL; ++i)
         xl[s][i] = __builtin_bit_cast(
             u32x4, __builtin_amdgcn_raw_buffer_load_b128(xrsrc, xloff[i] + xb, 0, 0));
     } else {
@@ -414,7 +418,7 @@ void matmul_kernel(const MatmulParams pk) {
         }
       };
       if constexpr (XST) {
-        // The chunk's 32 x 128 activations into this wave's LDS area, then
+        // The chunk's MROWS x 128 activations into this wave's LDS area, then
         // back out as fragments (lane r, q of fragment mt, j: row 16 mt + r,
         // piece 4j + q). Row `row` stores piece u at position u ^ (row & 15):
         // the 16 lanes writing a row cover every bank once, and the 16 lanes
@@ -422,7 +426,7 @@ void matmul_kernel(const MatmulParams pk) {
         char* xw = reinterpret_cast<char*>(xstage + wave * kXStageWords);
         wave_lds_order();  // the previous chunk's fragment reads come first
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
+        for (int i = 0; i < XL; ++i) {
           const int row = 4 * i + (lane >> 4);
           *reinterpret_cast<u32x4*>(xw + row * kXRowBytes + 16 * ((lane & 15) ^ (row & 15))) =
               xl[s][i];
@@ -681,9 +685,8 @@ void matmul_kernel(const MatmulParams pk) {
 
 // Kernel shapes. GEMV: 8 waves, each covering 1 or 2 tiles. MFMA: 8 or 7
 // tiles per wave with 4 waves (wide matrices: each activation fragment feeds
-// 8 or 7 tiles), 4 tiles with 4 waves (8 at 32 batch rows, which stage their
-// activations through LDS), or 2 tiles with 8 waves (narrow matrices, which
-// need many workgroups to fill the device).
+// 8 or 7 tiles), 4 tiles with 4 waves (8 at 32 batch rows), or 2 tiles with
+// 8 waves (narrow matrices, which need many workgroups to fill the device).
 constexpr int kPf = 2;
 
 // Host-side shape rules: compiled once (in the width-4 object).
@@ -709,7 +712,7 @@ int pick_tiles(int path, int mrows, int ntiles, int cus) {
 }
 #endif
 
-template <int BITS, bool MFMA, int MROWS, int TPW, int WAVES, int OCC>
+template <int BITS, bool MFMA, int MROWS, int TPW, int WAVES, int OCC, bool XS = false>
 static hipError_t launch_t(const MatmulParams& p, hipStream_t s) {
   const int nrb = p.nseg > 1 ? p.nrb : (p.ntiles + TPW - 1) / TPW;
   const dim3 grid((unsigned)nrb * (unsigned)p.ksplit);
@@ -724,42 +727,56 @@ static hipError_t launch_t(const MatmulParams& p, hipStream_t s) {
   constexpr int PFK = (!MFMA && MROWS == 1 && TPW == 1) ? 4 : kPf;
   const dim3 block(WAVES * kWave);
   // flags: GROUPED, ZP, TYPED, BCQ, BF16
-#define LUTQ_LAUNCH(G, Z, T, Q, H, OCCV)                                                   \
-  matmul_kernel<BITS, MFMA, MROWS, G, Z, T, Q, H, PFK, TPW, WAVES, OCCV><<<grid, block, 0, s>>>(p)
+#define LUTQ_LAUNCH(G, Z, T, Q, H, OCCV, XSV)                                              \
+  matmul_kernel<BITS, MFMA, MROWS, G, Z, T, Q, H, PFK, TPW, WAVES, OCCV, XSV><<<grid, block, 0, s>>>(p)
   if (p.bcq) {
     // binary-coded weights: GEMV shapes and the 2-tile MFMA shape only
+    // (not staged at 16 rows: the plane lookups already load the LDS)
     if constexpr (!MFMA || TPW == 2)
-      LUTQ_LAUNCH(true, false, false, true, false, OCC_G);
+      LUTQ_LAUNCH(true, false, false, true, false, OCC_G, XS && MROWS == 32);
     else
       return hipErrorInvalidValue;
   } else if (p.bf16) {
     // bf16 activations, plain tables
     if (p.group == 0)
-      LUTQ_LAUNCH(false, false, false, false, true, OCC);
+      LUTQ_LAUNCH(false, false, false, false, true, OCC, XS);
     else
-      LUTQ_LAUNCH(true, false, false, false, true, OCC_G);
+      LUTQ_LAUNCH(true, false, false, false, true, OCC_G, XS);
   } else if (p.group == 0) {
-    LUTQ_LAUNCH(false, false, false, false, false, OCC);
+    LUTQ_LAUNCH(false, false, false, false, false, OCC, XS);
   } else if (p.types && p.zp) {
-    LUTQ_LAUNCH(true, true, true, false, false, OCC_G);
+    LUTQ_LAUNCH(true, true, true, false, false, OCC_G, XS);
   } else if (p.types) {
-    LUTQ_LAUNCH(true, false, true, false, false, OCC_G);
+    LUTQ_LAUNCH(true, false, true, false, false, OCC_G, XS);
   } else if (p.zp) {
-    LUTQ_LAUNCH(true, true, false, false, false, OCC_G);
+    LUTQ_LAUNCH(true, true, false, false, false, OCC_G, XS);
   } else {
-    LUTQ_LAUNCH(true, false, false, false, false, OCC_G);
+    LUTQ_LAUNCH(true, false, false, false, false, OCC_G, XS);
   }
 #undef LUTQ_LAUNCH
   return hipGetLastError();
 }
 
+// The 8-wave shapes stage their activations (XS) at 32 batch rows, and at 16
+// when the slice holds more than 8 rows: the direct loads of missing rows
+// cost nothing, so at up to 8 rows the staging round trip does not pay
+// (measured: 5.9 -> 6.5 us at 5 rows, 12.8 -> 11.5 us at 12 on narrow
+// matrices).
 template <int BITS, int MROWS>
 static hipError_t launch_mfma(const MatmulParams& p, int tiles, hipStream_t s) {
   switch (tiles) {
     case 8: return launch_t<BITS, true, MROWS, 8, 4, 2>(p, s);
     case 7: return launch_t<BITS, true, MROWS, 7, 4, 2>(p, s);
-    case 4: return launch_t<BITS, true, MROWS, 4, MROWS == 32 ? 8 : 4, 2>(p, s);
-    default: return launch_t<BITS, true, MROWS, 2, 8, 2>(p, s);
+    case 4:
+      if constexpr (MROWS == 32) return launch_t<BITS, true, MROWS, 4, 8, 2, true>(p, s);
+      else return launch_t<BITS, true, MROWS, 4, 4, 2>(p, s);
+    default:
+      if constexpr (MROWS == 32) {
+        return launch_t<BITS, true, MROWS, 2, 8, 2, true>(p, s);
+      } else {
+        if (p.M > 8) return launch_t<BITS, true, MROWS, 2, 8, 2, true>(p, s);
+        return launch_t<BITS, true, MROWS, 2, 8, 2>(p, s);
+      }
   }
 }
 
