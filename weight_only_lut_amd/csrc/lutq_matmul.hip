@@ -80,7 +80,6 @@ void matmul_kernel(const MatmulParams pk) {
   // SIMD the LDS round trip sits in the wave's critical path and costs more
   // than the scattered loads it replaces (measured).
   static_assert(!XS || MFMA, "staging feeds MFMA fragments");
-  constexpr bool XST = XS;
   constexpr int XL = MROWS / 4;
   constexpr int kXRowBytes = 2 * kChunk;                 // one row of a chunk
   constexpr int kXStageWords = MROWS * kXRowBytes / 4;   // per wave (4 or 8 KiB)
@@ -95,7 +94,7 @@ void matmul_kernel(const MatmulParams pk) {
   constexpr int RP = ROWS + 4;
   static_assert(ROWS % 16 == 0, "pitch rule assumes whole tiles");
   constexpr int kRedWords = kWaves * MROWS * RP;
-  constexpr int kMainWords = kTableWords + (XST ? kWaves * kXStageWords : 0);
+  constexpr int kMainWords = kTableWords + (XS ? kWaves * kXStageWords : 0);
   constexpr int kLdsWords = kRedWords > kMainWords ? kRedWords : kMainWords;
   static_assert(kThreads >= kPairEntries, "table build needs one thread per entry");
 
@@ -202,8 +201,8 @@ void matmul_kernel(const MatmulParams pk) {
   // 16-byte piece u (k = 8u .. 8u + 7) of row 4i + v, so each row is one
   // contiguous 256-byte run (the fragment order above puts 16 rows in 16
   // consecutive lanes: 64 separate accesses per load)
-  uint32_t xloff[XST ? XL : 1];
-  if constexpr (XST) {
+  uint32_t xloff[XS ? XL : 1];
+  if constexpr (XS) {
 #pragma unroll
     for (int i = 0; i < XL; ++i) {
       const int row = 4 * i + (lane >> 4);
@@ -218,7 +217,7 @@ void matmul_kernel(const MatmulParams pk) {
   uint32_t tcur[TYPED ? TPW : 1], tnext[TYPED ? TPW : 1];  // type-id batches
   uint32_t xbuf[PF][MFMA ? 1 : MROWS];
   u32x4 abuf[PF][MT][MFMA ? 4 : 1];
-  u32x4 xl[XST ? PF : 1][XST ? XL : 1];  // staged: the row-contiguous pieces
+  u32x4 xl[XS ? PF : 1][XS ? XL : 1];  // staged: the row-contiguous pieces
 
   // chunk of pipeline step i, or -1 past the wave's last chunk
   auto chunk = [&](int i) { return i < nmine ? cw + i * kWaves : -1; };
@@ -234,7 +233,7 @@ void matmul_kernel(const MatmulParams pk) {
 #pragma unroll
       for (int m = 0; m < MROWS; ++m)
         xbuf[s][m] = __builtin_amdgcn_raw_buffer_load_b32(xrsrc, xoff[m] + xb, 0, 0);
-    } else if constexpr (XST) {
+    } else if constexpr (XS) {
 #pragma unroll
       for (int i = 0; i < XL; ++i)
         xl[s][i] = __builtin_bit_cast(
@@ -417,7 +416,7 @@ void matmul_kernel(const MatmulParams pk) {
           dst[j].w = lds_load(table, pair_addr(idx4, lb, 3));
         }
       };
-      if constexpr (XST) {
+      if constexpr (XS) {
         // The chunk's MROWS x 128 activations into this wave's LDS area, then
         // back out as fragments (lane r, q of fragment mt, j: row 16 mt + r,
         // piece 4j + q). Row `row` stores piece u at position u ^ (row & 15):
