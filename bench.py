@@ -516,7 +516,7 @@ def sweep(lutq, torch, args):
                 case.y = torch.empty((M, base.N), dtype=torch.float16, device="cuda")
                 case.bytes = algorithmic_bytes(M, base.N, base.K, w.bits, w.group)
                 case.flops = 2 * M * base.N * base.K
-                shapes = [("auto", 0)] + [("mfma", t) for t in (2, 4, 8)]
+                shapes = [("auto", 0)] + [("mfma", t) for t in (2, 4, 7, 8)]
                 if M <= 8:
                     shapes += [("gemv", t) for t in (1, 2)]
                 for path, tiles in shapes:
