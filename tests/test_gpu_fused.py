@@ -54,7 +54,7 @@ def check(ys, x, mats, group):
         assert ok, f"max err/bound = {worst:.3g}"
 
 
-SHAPES = [("gemv", 1), ("gemv", 2), ("mfma", 2), ("mfma", 4), ("mfma", 8)]
+SHAPES = [("gemv", 1), ("gemv", 2), ("mfma", 2), ("mfma", 4), ("mfma", 7), ("mfma", 8)]
 
 
 @pytest.mark.parametrize("path,tiles", SHAPES)
@@ -76,7 +76,8 @@ def test_fused_matches_oracle_and_single(lutq, path, tiles, bits, table, group, 
         assert torch.equal(y.view(torch.int16), y1.view(torch.int16))
 
 
-@pytest.mark.parametrize("names,Ms", [(("q", "k", "v"), (1, 8, 16, 32)), (("gate", "up"), (1, 32))])
+# gate + up: 1792 tiles, 7 per wave (one workgroup per CU) from 2 batch rows
+@pytest.mark.parametrize("names,Ms", [(("q", "k", "v"), (1, 8, 16, 32)), (("gate", "up"), (1, 8, 16, 32))])
 def test_fused_llama_layer(lutq, names, Ms):
     w = workloads.WORKLOADS["nf4_layer"]
     mats, dm = [], []

@@ -248,7 +248,8 @@ def test_full_lm3(lutq, mat):
 
 
 def test_full_log4_70b_sampled(lutq):
-    _full(lutq, "log4_70b", None, (1, 8, 32), sample_rows=1024)
+    # 28672 rows: the 7-tile MFMA shape at 8, 16 and 32 batch rows
+    _full(lutq, "log4_70b", None, (1, 8, 16, 32), sample_rows=1024)
 
 
 @pytest.mark.parametrize("mat", ["q", "k", "v", "o", "gate", "up", "down"])
