@@ -435,8 +435,14 @@ __global__ __launch_bounds__(kQuantThreads) void quant_kernel(const QuantParams 
       }
       if constexpr (ACC) {
         if (active) {
-          tacc[0][code][threadIdx.x] += (double)v[c] * s;
-          tacc[1][code][threadIdx.x] += s * s;
+          // LDS fp64 adds without a returned value (ds_add_f64): one LDS
+          // operation each instead of a read and a write. The slots are this
+          // thread's own and updated in program order, so the sums are those
+          // of plain adds (no operand comes near the fp64 denormal range).
+          __hip_atomic_fetch_add(&tacc[0][code][threadIdx.x], (double)v[c] * s, __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_WORKGROUP);
+          __hip_atomic_fetch_add(&tacc[1][code][threadIdx.x], s * s, __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_WORKGROUP);
         }
       }
     }
