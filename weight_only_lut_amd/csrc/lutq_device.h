@@ -380,6 +380,26 @@ __device__ __forceinline__ uint32_t bf16x2_absmax(uint32_t v) {
   const uint32_t a = v & 0x7FFFu, b = (v >> 16) & 0x7FFFu;
   return a > b ? a : b;
 }
+// Running magnitude maximum of bf16 pairs, per half (v_pk_max_u16), and its
+// final value: on sign-cleared bf16 bits the integer order is the order of
+// magnitudes.
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ u16x2 bf16x2_absmax_acc(u16x2 acc, uint32_t v) {
+  return __builtin_elementwise_max(acc, __builtin_bit_cast(u16x2, v & 0x7FFF7FFFu));
+}
+__device__ __forceinline__ uint32_t u16x2_max(u16x2 v) {
+  return v[0] > v[1] ? (uint32_t)v[0] : (uint32_t)v[1];
+}
+// Maximum over the lanes l, l ^ 16, l ^ 32 and l ^ 48, with the gfx950 lane
+// swaps (VALU, no LDS): each swap exchanges half of one copy with half of
+// the other, so the larger of the pair is the maximum with the partner
+// lane, whichever way round the halves moved.
+__device__ __forceinline__ uint32_t max_over_quarters(uint32_t a) {
+  const auto h = __builtin_amdgcn_permlane32_swap(a, a, false, false);
+  const uint32_t b = h[0] > h[1] ? h[0] : h[1];
+  const auto r = __builtin_amdgcn_permlane16_swap(b, b, false, false);
+  return r[0] > r[1] ? r[0] : r[1];
+}
 
 __device__ __forceinline__ float f16_bits_to_f32(uint16_t h) {
   return (float)__builtin_bit_cast(f16, h);

@@ -445,14 +445,12 @@ void matmul_kernel(const MatmulParams pk) {
       if constexpr (BF16) {
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
-          uint32_t a = 0;
+          u16x2 m2 = {0, 0};
 #pragma unroll
           for (int j = 0; j < 4; ++j)
 #pragma unroll
-            for (int w = 0; w < 4; ++w) a = max(a, bf16x2_absmax(abuf[s][mt][j][w]));
-          a = max(a, (uint32_t)__shfl_xor((int)a, 16));
-          a = max(a, (uint32_t)__shfl_xor((int)a, 32));
-          const int sh = bf16_chunk_shift(a);
+            for (int w = 0; w < 4; ++w) m2 = bf16x2_absmax_acc(m2, abuf[s][mt][j][w]);
+          const int sh = bf16_chunk_shift(max_over_quarters(u16x2_max(m2)));
 #pragma unroll
           for (int j = 0; j < 4; ++j)
 #pragma unroll
