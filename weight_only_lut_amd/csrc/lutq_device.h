@@ -393,7 +393,9 @@ __device__ __forceinline__ uint32_t u16x2_max(u16x2 v) {
 // Maximum over the lanes l, l ^ 16, l ^ 32 and l ^ 48, with the gfx950 lane
 // swaps (VALU, no LDS): each swap exchanges half of one copy with half of
 // the other, so the larger of the pair is the maximum with the partner
-// lane, whichever way round the halves moved.
+// lane, whichever way round the halves moved. (A float sum written the same
+// way compiled here to x + x, dropping the swapped copy; this integer form
+// reads both registers, and the bf16 parity tests fail if it does not.)
 __device__ __forceinline__ uint32_t max_over_quarters(uint32_t a) {
   const auto h = __builtin_amdgcn_permlane32_swap(a, a, false, false);
   const uint32_t b = h[0] > h[1] ? h[0] : h[1];
