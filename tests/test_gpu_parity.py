@@ -104,6 +104,8 @@ CASES = [
     (3, "lloyd_max", 256, 48, 768),
     (2, "int", 0, 33, 256),
     (4, "nf", 512, 80, 1024),
+    (4, "int", 384, 45, 1152),        # 3 chunks per group
+    (3, "lloyd_max", 640, 29, 1280),  # 5 chunks per group
 ]
 
 
@@ -123,7 +125,8 @@ SHAPES = [("gemv", 1), ("gemv", 2), ("mfma", 2), ("mfma", 4), ("mfma", 7), ("mfm
 
 
 @pytest.mark.parametrize("path,tiles", SHAPES)
-@pytest.mark.parametrize("bits,table,group", [(4, "nf", 128), (3, "lloyd_max", 0), (2, "int", 256)])
+@pytest.mark.parametrize("bits,table,group", [(4, "nf", 128), (3, "lloyd_max", 0), (2, "int", 256),
+                                              (4, "int", 384)])
 @pytest.mark.parametrize("M", [1, 5, 16, 32, 45])
 @pytest.mark.parametrize("ksplit", [1, 3])
 def test_parity_every_shape(lutq, path, tiles, bits, table, group, M, ksplit):

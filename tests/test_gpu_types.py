@@ -58,7 +58,8 @@ SHAPES = [("gemv", 1), ("gemv", 2), ("mfma", 2), ("mfma", 4), ("mfma", 7), ("mfm
 
 
 @pytest.mark.parametrize("path,tiles", SHAPES)
-@pytest.mark.parametrize("bits,ntypes,group", [(4, 4, 128), (3, 3, 256), (2, 2, 128), (4, 1, 128)])
+@pytest.mark.parametrize("bits,ntypes,group", [(4, 4, 128), (3, 3, 256), (2, 2, 128), (4, 1, 128),
+                                               (3, 4, 384)])
 @pytest.mark.parametrize("M", [1, 5, 16, 45])
 @pytest.mark.parametrize("ksplit,zeros", [(1, False), (3, True)])
 def test_types_every_shape(lutq, path, tiles, bits, ntypes, group, M, ksplit, zeros):

@@ -54,7 +54,8 @@ SHAPES = [("gemv", 1), ("gemv", 2), ("mfma", 2), ("mfma", 4), ("mfma", 7), ("mfm
 
 
 @pytest.mark.parametrize("path,tiles", SHAPES)
-@pytest.mark.parametrize("bits,table,group", [(4, "nf", 128), (3, "lloyd_max", 256), (2, "int", 128)])
+@pytest.mark.parametrize("bits,table,group", [(4, "nf", 128), (3, "lloyd_max", 256), (2, "int", 128),
+                                              (4, "int", 384)])
 @pytest.mark.parametrize("M", [1, 5, 16, 45])
 @pytest.mark.parametrize("ksplit", [1, 3])
 def test_zero_points_every_shape(lutq, path, tiles, bits, table, group, M, ksplit):
