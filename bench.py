@@ -328,6 +328,46 @@ class QuantCase:
             raise _lib.LutqError(rc, "lutq_quantize")
 
 
+class DenseCase:
+    """The same product with dense fp16 weights through torch (the vendor GEMM
+    library): the baseline that a weight-only quantized kernel is measured
+    against (FLUTE abstract: speedups over existing GEMM kernels at batch
+    sizes below 32). Cold: rotating copies, as the quantized cases."""
+
+    def __init__(self, torch, N, K, M, seed):
+        g = torch.Generator(device="cuda").manual_seed(seed)
+        w = (torch.randn(N, K, generator=g, device="cuda") * 0.02).half()
+        self.ws = [w] + [w.clone() for _ in range(max(2, -(-COLD_SET_BYTES // w.nbytes)) - 1)]
+        self.x = torch.randn(M, K, generator=g, device="cuda").half()
+        self.bytes = N * K * 2 + M * K * 2 + M * N * 2
+        self.flops = 2 * M * N * K
+        self.linear = torch.nn.functional.linear
+        torch.cuda.synchronize()
+
+    def call(self, lutq, i):
+        self.linear(self.x, self.ws[i % len(self.ws)])
+
+
+def dense_section(torch, args, quantized_us):
+    """Dense fp16 at the headline shapes, beside the LUT kernel's time."""
+    out = {}
+    for label, (N, K, M) in (("int4_up_proj_M1", (14336, 4096, 1)), ("log4_70b_M32", (28672, 8192, 32))):
+        if quantized_us.get(label) is None:
+            continue
+        dc = DenseCase(torch, N, K, M, seed=11)
+        us = time_case(None, torch, dc, max(20, args.steps // 4), args.warmup, repeats=EXTRA_REPEATS)
+        q = quantized_us[label]
+        out[label] = {"N": N, "K": K, "M": M, "dense_us": round(us, 3),
+                      "dense_GBps": round(dc.bytes / (us * 1e-6) / 1e9, 1),
+                      "dense_TFLOPs": round(dc.flops / (us * 1e-6) / 1e12, 1),
+                      "lutq_us": round(q, 3), "speedup": round(us / q, 2),
+                      "copies": len(dc.ws)}
+        log(f"[bench] dense fp16 {label}: {us:.2f} us (lutq {q:.2f} us, {us / q:.2f}x)")
+        del dc
+        torch.cuda.empty_cache()
+    return out
+
+
 def quantizer_section(lutq, torch, args):
     """The quantizer (the step before repack) on the headline matrix: grouped
     INT (range rule) and tensor-wise NormalFloat (absmax), cold weights, with
@@ -380,6 +420,8 @@ def main():
     ap.add_argument("--no-batch32", action="store_true")
     ap.add_argument("--no-quantizer", action="store_true")
     ap.add_argument("--no-fused", action="store_true")
+    ap.add_argument("--no-dense", action="store_true",
+                    help="skip the dense fp16 (torch) context timings")
     ap.add_argument("--no-variants", action="store_true",
                     help="skip the zero-point and data-type timings")
     ap.add_argument("--no-warm", action="store_true",
@@ -466,6 +508,10 @@ def main():
         extra["fused"] = fused_section(lutq, torch, args)
     if not args.no_variants:
         extra["variants"] = variant_section(lutq, torch, args)
+    if not args.no_dense:
+        extra["dense_fp16"] = dense_section(
+            torch, args, {"int4_up_proj_M1": region_us,
+                          "log4_70b_M32": None if args.no_batch32 else k_us})
 
     if args.sweep:
         extra["sweep"] = sweep(lutq, torch, args)
