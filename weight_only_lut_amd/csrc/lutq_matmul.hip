@@ -671,10 +671,23 @@ void matmul_kernel(const MatmulParams pk) {
   for (int it = tid; it < items; it += kThreads) {
     const int m = it / ROWS, row = it - m * ROWS;
     const int n = tile0 * kTileRows + row;
+    // The splits' partials in split order, eight loads in flight at a time
+    // (a load-then-add loop waits out one device round trip per split).
+    // Past the last split the load repeats a valid address and its value is
+    // not added, so every load is unconditional and the sum is the plain
+    // in-order one.
+    const float* part = p.partial + ((size_t)rb * p.ksplit * MROWS + m) * ROWS + row;
+    const size_t kstride = (size_t)MROWS * ROWS;
     float v = 0.f;
-    for (int k2 = 0; k2 < p.ksplit; ++k2)
-      v += __hip_atomic_load(p.partial + (((size_t)rb * p.ksplit + k2) * MROWS + m) * ROWS + row,
-                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (int k0 = 0; k0 < p.ksplit; k0 += 8) {
+      float t[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        t[u] = __hip_atomic_load(part + (size_t)min(k0 + u, p.ksplit - 1) * kstride,
+                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v = k0 + u < p.ksplit ? v + t[u] : v;
+    }
     if (n < p.N) p.y[(size_t)m * p.N + n] = BF16 ? f32_to_bf16_bits(v) : f32_to_f16_bits(v);
   }
   if (tid == 0) __hip_atomic_store(p.counters + rb, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
