@@ -624,6 +624,9 @@ template <int L>
 __global__ __launch_bounds__(kQuantThreads) void tensor_scale_kernel(const QuantParams p, int nparts) {
   __shared__ float part[2][kQuantWaves];
   float mx = -__builtin_huge_valf(), mn = __builtin_huge_valf();
+  // (unrolled so that the loads are in flight together; max and min do not
+  // depend on the order)
+#pragma unroll 8
   for (int i = threadIdx.x; i < nparts; i += kQuantThreads) {
     mx = fmaxf(mx, p.extrema[2 * i + 0]);
     mn = fminf(mn, p.extrema[2 * i + 1]);
@@ -659,8 +662,19 @@ __global__ __launch_bounds__(kQuantThreads) void tensor_scale_kernel(const Quant
 __global__ __launch_bounds__(kQuantThreads) void error_sum_kernel(const double* part, int nparts,
                                                                    double* out) {
   __shared__ double s[kQuantThreads];
+  // thread i adds parts i, i + 256, ... in that order, eight loads in flight
+  // at a time (past the end a load repeats part 0 and is not added)
   double t = 0.0;
-  for (int i = threadIdx.x; i < nparts; i += kQuantThreads) t += part[i];
+  for (int i0 = threadIdx.x; i0 < nparts; i0 += 8 * kQuantThreads) {
+    double v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = i0 + u * kQuantThreads;
+      v[u] = part[i < nparts ? i : 0];
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) t = i0 + u * kQuantThreads < nparts ? t + v[u] : t;
+  }
   s[threadIdx.x] = t;
   __syncthreads();
   if (threadIdx.x == 0) {
