@@ -403,6 +403,25 @@ __device__ __forceinline__ uint32_t max_over_quarters(uint32_t a) {
   return r[0] > r[1] ? r[0] : r[1];
 }
 
+// The sum over the lanes r, r + 16, r + 32, r + 48 (r < 16), in lane r:
+// (x_r + x_r+16) + (x_r+32 + x_r+48), the order of a shuffle butterfly over
+// lane distance 16 then 32. v_permlane16_swap exchanges the odd 16-lane rows
+// of its first operand with the even rows of its second, v_permlane32_swap
+// the upper half of the first with the lower half of the second; pairing x
+// with zero leaves each lane r of row 0 (and of row 2) with x_r and its
+// partner. Only lanes 0..15 hold the sum. (VALU; no LDS round trips.)
+// (Written in assembly: with the builtins this compiler added the first
+// swapped register to itself instead of to the second. The s_nop covers the
+// wait states between a VALU write and a lane swap reading it.)
+__device__ __forceinline__ float sum_over_quarters_r(float x) {
+  uint32_t a0 = __builtin_bit_cast(uint32_t, x), a1 = 0u;
+  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(a0), "+v"(a1));
+  uint32_t c0 = __builtin_bit_cast(uint32_t, __builtin_bit_cast(float, a0) + __builtin_bit_cast(float, a1));
+  uint32_t c1 = 0u;
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(c0), "+v"(c1));
+  return __builtin_bit_cast(float, c0) + __builtin_bit_cast(float, c1);
+}
+
 __device__ __forceinline__ float f16_bits_to_f32(uint16_t h) {
   return (float)__builtin_bit_cast(f16, h);
 }

@@ -619,9 +619,7 @@ void matmul_kernel(const MatmulParams pk) {
     if constexpr (!MFMA) {
 #pragma unroll
       for (int m = 0; m < MROWS; ++m) {
-        float v = gacc[t][m];
-        v += __shfl_xor(v, 16);
-        v += __shfl_xor(v, 32);
+        const float v = sum_over_quarters_r(gacc[t][m]);
         if (q == 0) red[(wave * MROWS + m) * RP + t * kTileRows + r] = v;
       }
     } else {
