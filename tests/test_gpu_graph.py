@@ -76,10 +76,12 @@ def test_graph_replays_equal_eager(lutq):
             r = f()
             outs[name] = r if isinstance(r, list) else [r]
     for rep in range(4):
-        for name in outs:                               # poison the outputs
-            for t in outs[name]:
-                t.view(torch.int16).fill_(0x7E00)
         with torch.cuda.stream(stream):
+            # poison the outputs, on the replay's stream: the side stream does
+            # not wait for work queued on the default one
+            for name in outs:
+                for t in outs[name]:
+                    t.view(torch.int16).fill_(0x7E00)
             graph.replay()
         torch.cuda.synchronize()
         for name in outs:
