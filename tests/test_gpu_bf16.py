@@ -108,7 +108,7 @@ def test_bf16_fused_equals_single(lutq, M):
     xb, xv = bf16(draw.activations(M, K, (921, M)).astype(np.float32))
     xd = dev_bf16(xb)
     dm = [(lutq.repack(dev(c), 4, 128), dev(T), dev(s)) for c, T, s in mats]
-    for path, tiles in (("gemv", 1), ("mfma", 2)):
+    for path, tiles in (("gemv", 1), ("mfma", 2), ("mfma", 7)):
         ys = lutq.matmul_multi(xd, dm, path=path, tiles=tiles)
         for y, (c, T, s), d in zip(ys, mats, dm):
             check(from_bf16(y), xv, c, T, s, 128)

@@ -105,7 +105,7 @@ def test_fused_mixed_zero_points(lutq, M):
     for c, T, s, z in mats:
         item = (lutq.repack(dev(c), 4, 128), dev(T), dev(s))
         dm.append(item + ((dev(z),) if z is not None else ()))
-    for path, tiles in (("gemv", 2), ("mfma", 4)):
+    for path, tiles in (("gemv", 2), ("mfma", 4), ("mfma", 7)):
         ys = lutq.matmul_multi(xd, dm, path=path, tiles=tiles)
         torch.cuda.synchronize()
         for y, (c, T, s, z), d in zip(ys, mats, dm):
