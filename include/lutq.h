@@ -26,6 +26,20 @@
  *  - On any error nothing is enqueued and outputs are untouched.
  *  - fp16 values are passed as raw IEEE binary16 bit patterns (uint16_t).
  *  - No C++ exception crosses this boundary.
+ *
+ * Scratch memory. A product split along K across workgroups (see
+ * lutq_options_t.ksplit; the automatic plan splits narrow matrices with a
+ * long K) and the tensor-wise quantizer keep fp32 partial results and
+ * arrival counters in a scratch buffer that the library allocates, one per
+ * (device, stream), on the first call that needs it. A later call needing
+ * more gets a larger buffer; the outgrown one is not freed until
+ * lutq_shutdown, so work still queued and HIP graphs captured earlier keep
+ * using it safely. No memory is allocated while the stream is being
+ * captured: such a call returns LUTQ_ECAPTURE and enqueues nothing, so run
+ * each call once eagerly on a stream before capturing it there. A graph
+ * holding split launches uses the buffer of the stream it was captured on:
+ * do not replay it concurrently with other lutq work on that stream (or
+ * with another replay of itself).
  */
 #ifndef LUTQ_H
 #define LUTQ_H
@@ -51,7 +65,10 @@ enum {
                             layout version                                  */
   LUTQ_ESIZE = -6,       /* destination buffer too small                    */
   LUTQ_EHIP = -7,        /* a HIP runtime call failed (see lutq_last_hip_error) */
-  LUTQ_EUNSUPPORTED = -8 /* a size beyond the limits below                  */
+  LUTQ_EUNSUPPORTED = -8, /* a size beyond the limits below                 */
+  LUTQ_ECAPTURE = -9      /* the call needs new scratch memory while its
+                             stream is being captured into a HIP graph
+                             (see "Scratch memory" below)                   */
 };
 
 /* Limits: 0 <= M; 0 <= N <= 2^24; 0 <= K <= 2^20; N*K <= 2^36 (32 GiB of
@@ -131,7 +148,7 @@ int lutq_unpack(const lutq_packed_t* packed, uint8_t* codes_out, void* stream);
  * multiplied by its scale. Results are deterministic (no float atomics).
  * M == 0 or N == 0: nothing to do (LUTQ_OK). K == 0: y is set to zero.
  * Errors: LUTQ_EINVAL, LUTQ_EMISMATCH, LUTQ_EALIGN, LUTQ_EUNSUPPORTED,
- * LUTQ_EHIP. Calls may run concurrently on different streams. */
+ * LUTQ_ECAPTURE, LUTQ_EHIP. Calls may run concurrently on different streams. */
 int lutq_matmul(const uint16_t* x, const lutq_packed_t* packed, const uint16_t* lut,
                 const uint16_t* scales, uint16_t* y, int M, int N, int K, void* stream);
 
@@ -180,9 +197,8 @@ int lutq_matmul_ex(const uint16_t* x, const lutq_packed_t* packed, const uint16_
 int lutq_plan(int M, int N, int K, int bits, const lutq_options_t* req, lutq_options_t* out);
 
 /* ---- fused launch of several matrices ---------------------------------------
- * The products of one layer that read the same activations (the q, k and v
- * projections, or gate and up; FLUTE abstract: fused kernels for the linear
- * layers of an LLM) in one launch per batch slice:
+ * The products of one decoder layer that read the same activations (the q,
+ * k and v projections, or gate and up) in one launch per batch slice:
  *     y_i = x . W_i^T,   i < count <= LUTQ_MAX_FUSED.
  * Narrow matrices (k, v at batch 1) cannot fill the device alone; sharing a
  * launch also saves the launches themselves. Every matrix has the same K,
@@ -353,8 +369,9 @@ const char* lutq_strerror(int status);
 /* The last HIP error code seen by this thread (hipError_t as int). */
 int lutq_last_hip_error(void);
 
-/* Frees the library's split-K scratch buffers (per device and stream). Call
- * only when no lutq work is in flight. */
+/* Frees the library's scratch buffers (per device and stream, including
+ * outgrown ones kept for earlier graphs). Call only when no lutq work is in
+ * flight and no graph that used them will be replayed again. */
 void lutq_shutdown(void);
 
 #ifdef __cplusplus

@@ -5,7 +5,10 @@ zero-point, bf16 and binary-coded paths; split-K launches on two streams at
 once (each stream has its own scratch) give their single-stream results.
 
 A split-K launch allocates its scratch on first use, so each case runs once
-eagerly before capture, as the benchmark does.
+eagerly before capture, as the benchmark does. A capture that would need new
+scratch is refused (LUTQ_ECAPTURE) with nothing enqueued, and a graph keeps
+working after a later eager call on its stream has outgrown the scratch it
+was captured with (the outgrown buffer is retired, not freed).
 """
 
 import numpy as np
@@ -108,3 +111,67 @@ def test_split_k_on_two_streams_at_once(lutq):
         for got_list, w in zip(ys, want):
             for got in got_list:
                 assert torch.equal(got.view(torch.int16), w)
+
+
+def test_graph_survives_scratch_growth(lutq):
+    K = 1024
+    c, T, s, _ = workloads.small_case(4, "nf", 128, 1, 200, K, seed=970)
+    P = lutq.repack(dev(c), 4, 128)
+    Td, sd = dev(T), dev(s)
+    x = dev(draw.activations(32, K, (971,)))
+    # a large split: 256 row blocks x 16 splits x 32 rows x 32 batch rows of
+    # fp32 partials is 16 MiB, more than the stream's first buffer holds
+    Kb = 2048
+    cb, Tb, sb, _ = workloads.small_case(4, "nf", 128, 1, 8192, Kb, seed=972)
+    Pb = lutq.repack(dev(cb), 4, 128)
+    Tbd, sbd = dev(Tb), dev(sb)
+    xb = dev(draw.activations(32, Kb, (973,)))
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        want = bits16(lutq.matmul(x, P, Td, sd, path="mfma", tiles=2, ksplit=3))
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        out = lutq.matmul(x, P, Td, sd, path="mfma", tiles=2, ksplit=3)
+    for rep in range(3):
+        with torch.cuda.stream(stream):
+            big = lutq.matmul(xb, Pb, Tbd, sbd, path="mfma", tiles=2, ksplit=16)  # grows the scratch
+            out.view(torch.int16).fill_(0x7E00)
+            graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), want), f"replay {rep}"
+    # the growing call itself is right as well (against its unsplit launch)
+    ref = lutq.matmul(xb, Pb, Tbd, sbd, path="mfma", tiles=2, ksplit=1).float()
+    torch.cuda.synchronize()
+    assert torch.allclose(big.float(), ref, rtol=2e-3, atol=1e-4)
+
+
+def test_capture_refuses_new_scratch(lutq):
+    c, T, s, _ = workloads.small_case(4, "nf", 128, 1, 64, 512, seed=980)
+    P = lutq.repack(dev(c), 4, 128)
+    Td, sd = dev(T), dev(s)
+    x = dev(draw.activations(4, 512, (981,)))
+    y = torch.zeros((4, 64), dtype=torch.float16, device="cuda")
+    other = torch.zeros(16, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.Stream()   # a stream with no scratch yet
+    graph = torch.cuda.CUDAGraph()
+    err = None
+    with torch.cuda.graph(graph, stream=stream):
+        try:
+            lutq.matmul(x, P, Td, sd, path="gemv", ksplit=2, out=y)
+        except lutq.LutqError as e:
+            err = e
+        other.add_(1.0)
+    assert err is not None and err.code == -9, err
+    graph.replay()                 # the refused call enqueued nothing
+    torch.cuda.synchronize()
+    assert int(y.abs().max().item()) == 0 and float(other[0].item()) == 1.0
+    with torch.cuda.stream(stream):  # eagerly it runs, and a capture after it works
+        want = bits16(lutq.matmul(x, P, Td, sd, path="gemv", ksplit=2))
+    torch.cuda.synchronize()
+    g2 = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g2, stream=stream):
+        out = lutq.matmul(x, P, Td, sd, path="gemv", ksplit=2)
+    g2.replay()
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), want)

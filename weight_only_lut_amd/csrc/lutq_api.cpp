@@ -8,6 +8,7 @@
 #include <map>
 #include <mutex>
 #include <utility>
+#include <vector>
 
 #include "../../include/lutq.h"
 #include "lutq_quant.h"
@@ -52,15 +53,23 @@ int check_desc(const lutq_packed_t* p) {
 }
 
 // Split-K scratch: one buffer per (device, stream), allocated on first need
-// and kept until lutq_shutdown. Counters start at zero (hipMemset at
-// allocation) and every launch leaves them at zero.
+// and grown when a call needs more. An outgrown buffer is retired, not freed:
+// work still queued on the stream, or a HIP graph captured earlier, may hold
+// its address, so retired buffers are freed only by lutq_shutdown. Nothing is
+// allocated while the stream is being captured (LUTQ_ECAPTURE): a call that
+// needs new scratch must run once eagerly on that stream first. The counters
+// are zeroed at allocation by the library's fill kernel on the caller's
+// stream (ordered before the launches that use them), and every launch
+// leaves them at zero.
 struct Scratch {
   void* base = nullptr;
   size_t bytes = 0;
 };
 std::mutex g_mu;
 std::map<std::pair<int, void*>, Scratch> g_scratch;
-constexpr size_t kCounterBytes = 64 * 1024;  // up to 16384 row blocks
+std::vector<std::pair<int, void*>> g_retired;  // (device, base), freed by lutq_shutdown
+constexpr size_t kCounterBytes = lutq::kSplitCounterBytes;
+constexpr size_t kMinScratchBytes = 8u << 20;
 
 int get_scratch(void* stream, size_t partial_bytes, float** partial, uint32_t** counters) {
   int dev = 0;
@@ -70,19 +79,23 @@ int get_scratch(void* stream, size_t partial_bytes, float** partial, uint32_t** 
   Scratch& s = g_scratch[{dev, stream}];
   const size_t need = kCounterBytes + partial_bytes;
   if (s.bytes < need) {
-    if (s.base) {
-      // the old buffer may still be in use by work queued on this stream
-      e = hipStreamSynchronize((hipStream_t)stream);
-      if (e != hipSuccess) return hip_fail(e);
-      (void)hipFree(s.base);
-      s.base = nullptr;
-      s.bytes = 0;
+    hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+    e = hipStreamIsCapturing((hipStream_t)stream, &st);
+    if (e != hipSuccess) return hip_fail(e);
+    if (st != hipStreamCaptureStatusNone) return LUTQ_ECAPTURE;
+    size_t bytes = need > 2 * s.bytes ? need : 2 * s.bytes;
+    if (bytes < kMinScratchBytes) bytes = kMinScratchBytes;
+    void* base = nullptr;
+    e = hipMalloc(&base, bytes);
+    if (e != hipSuccess) return hip_fail(e);
+    e = lutq::launch_fill_u16(reinterpret_cast<uint16_t*>(base), (long long)(kCounterBytes / 2), 0,
+                              (hipStream_t)stream);
+    if (e != hipSuccess) {
+      (void)hipFree(base);  // nothing was enqueued
+      return hip_fail(e);
     }
-    size_t bytes = need < (8u << 20) ? (8u << 20) : need;
-    e = hipMalloc(&s.base, bytes);
-    if (e != hipSuccess) return hip_fail(e);
-    e = hipMemset(s.base, 0, kCounterBytes);
-    if (e != hipSuccess) return hip_fail(e);
+    if (s.base) g_retired.emplace_back(dev, s.base);
+    s.base = base;
     s.bytes = bytes;
   }
   *counters = reinterpret_cast<uint32_t*>(s.base);
@@ -90,17 +103,20 @@ int get_scratch(void* stream, size_t partial_bytes, float** partial, uint32_t** 
   return LUTQ_OK;
 }
 
+// Compute units of the current device, cached per device ordinal.
 int cu_count() {
-  static int n = 0;
-  if (n == 0) {
-    int dev = 0, v = 0;
-    if (hipGetDevice(&dev) == hipSuccess &&
-        hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
-      n = v;
-    else
-      n = 256;
-  }
-  return n;
+  static std::mutex mu;
+  static std::map<int, int> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  std::lock_guard<std::mutex> lk(mu);
+  auto it = cache.find(dev);
+  if (it != cache.end()) return it->second;
+  int v = 0;
+  if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
+    v = 256;
+  cache[dev] = v;
+  return v;
 }
 
 int rows_per_launch(int path) {
@@ -640,6 +656,9 @@ const char* lutq_strerror(int status) {
     case LUTQ_ESIZE: return "destination buffer too small";
     case LUTQ_EHIP: return "HIP runtime error";
     case LUTQ_EUNSUPPORTED: return "size beyond the supported limits";
+    case LUTQ_ECAPTURE:
+      return "the call needs new scratch memory while its stream is being captured into a graph "
+             "(run it once eagerly on that stream first)";
     default: return "unknown lutq status";
   }
 }
@@ -648,16 +667,18 @@ int lutq_last_hip_error(void) { return g_last_hip; }
 
 void lutq_shutdown(void) {
   std::lock_guard<std::mutex> lk(g_mu);
-  for (auto& kv : g_scratch) {
-    if (kv.second.base) {
-      int cur = 0;
-      (void)hipGetDevice(&cur);
-      (void)hipSetDevice(kv.first.first);
-      (void)hipFree(kv.second.base);
-      (void)hipSetDevice(cur);
-    }
-  }
+  int cur = 0;
+  (void)hipGetDevice(&cur);
+  auto release = [](int dev, void* base) {
+    (void)hipSetDevice(dev);
+    (void)hipFree(base);
+  };
+  for (auto& kv : g_scratch)
+    if (kv.second.base) release(kv.first.first, kv.second.base);
+  for (auto& r : g_retired) release(r.first, r.second);
+  (void)hipSetDevice(cur);
   g_scratch.clear();
+  g_retired.clear();
 }
 
 }  // extern "C"

@@ -50,6 +50,10 @@ struct MatmulParams {
 
 enum Path { kPathGemv = 1, kPathMfma = 2 };
 
+// Split-K arrival counters at the start of a scratch buffer: one 32-bit
+// counter per row block of a launch (up to 16384), zero between launches.
+constexpr size_t kSplitCounterBytes = 64 * 1024;
+
 // Rows of x one launch of each path handles.
 constexpr int kGemvMaxRows = 8;
 constexpr int kMfmaMaxRows = 32;

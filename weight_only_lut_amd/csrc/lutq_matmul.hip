@@ -651,13 +651,27 @@ void matmul_kernel(const MatmulParams pk) {
   if (p.ksplit == 1) return;
 
   // ---- split-K: the last workgroup of this row block sums the splits ------
-  // Partials are written and read with agent-scope atomics, which go to the
-  // device-coherent level of the memory system and so are seen across XCDs
-  // without writing back or invalidating whole L2 caches (the cost of an
-  // agent-scope fence). Each thread waits for its partial stores to be
-  // acknowledged before the barrier; only then does one thread bump the
-  // row block's arrival counter.
-  __builtin_amdgcn_s_waitcnt(0);
+  // Ordering without agent-scope fences. An agent-scope release fence on
+  // gfx950 writes back the whole L2 of the XCD (buffer_wbl2), which costs
+  // ~100 us over a few hundred workgroups, so the hand-off is built from
+  // these rules of the AMDGPU memory model for this target instead:
+  //  1. every partial is stored with an agent-scope atomic store, which the
+  //     hardware writes through to the device-coherent level (not left dirty
+  //     in this XCD's L2), and the last workgroup reads them with
+  //     agent-scope atomic loads, which read that level (no stale L2 copy);
+  //  2. a store's vmcnt slot is released only when the store is
+  //     acknowledged, i.e. visible at that level: the wait below (inline
+  //     assembly with a memory clobber, so the compiler cannot sink the
+  //     stores below it) makes all of this thread's partials visible
+  //     before the barrier;
+  //  3. the arrival counter is bumped (agent-scope atomic, performed at the
+  //     same level) by one thread after the barrier, i.e. after every
+  //     thread's wait; the workgroup that sees the last count reads the
+  //     partials only after a second barrier, which the compiler does not
+  //     move memory operations across.
+  // So a partial is visible before its workgroup's arrival is counted, and
+  // read only after every arrival was counted.
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   if (tid == 0) {
     const uint32_t old =
