@@ -17,7 +17,7 @@ from . import layout_spec
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "lutq.h")
 
-OK, EINVAL, EBITS, EGROUP, EALIGN, EMISMATCH, ESIZE, EHIP, EUNSUP = 0, -1, -2, -3, -4, -5, -6, -7, -8
+OK, EINVAL, EBITS, EGROUP, EALIGN, EMISMATCH, ESIZE, EHIP, EUNSUP, ECAPTURE = 0, -1, -2, -3, -4, -5, -6, -7, -8, -9
 
 
 @pytest.fixture(scope="module")
@@ -39,9 +39,76 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_strerror_covers_every_code(lib):
-    for c in (OK, EINVAL, EBITS, EGROUP, EALIGN, EMISMATCH, ESIZE, EHIP, EUNSUP):
+    for c in (OK, EINVAL, EBITS, EGROUP, EALIGN, EMISMATCH, ESIZE, EHIP, EUNSUP, ECAPTURE):
         assert lutq.strerror(c) != "unknown lutq status"
     assert lutq.strerror(-99) == "unknown lutq status"
+
+
+def _cpu_packed(N, K, bits, group):
+    import torch
+    d = _desc(N=N, K=K, bits=bits, group=group)
+    return _lib.Packed(torch.zeros(max(1, N * K * bits // 8), dtype=torch.uint8), d)
+
+
+def test_binding_checks_every_tensor_before_calling():
+    """Shapes, sizes and dtypes of every tensor argument are checked before
+    any call into the library (here on CPU tensors, which are then refused
+    for not being on the GPU)."""
+    import torch
+    f16, u8 = torch.float16, torch.uint8
+    N, K = 64, 256
+    P = _cpu_packed(N, K, 4, 128)
+    x = torch.zeros((2, K), dtype=f16)
+    lut = torch.zeros(16, dtype=f16)
+    sc = torch.zeros((N, K // 128), dtype=f16)
+    bad = [
+        dict(x=torch.zeros((2, K + 128), dtype=f16)),          # K differs from the packed matrix
+        dict(lut=torch.zeros(8, dtype=f16)),                   # 2^bits entries
+        dict(scales=torch.zeros((N, 1), dtype=f16)),           # N * K / group entries
+        dict(zeros=torch.zeros((N,), dtype=f16)),
+        dict(types=torch.zeros((N, 1), dtype=u8)),
+        dict(types=torch.zeros((N, 2), dtype=u8), lut=torch.zeros((5, 16), dtype=f16)),  # <= 4 tables
+        dict(out=torch.zeros((2, N + 1), dtype=f16)),
+    ]
+    for over in bad:
+        kw = dict(x=x, lut=lut, scales=sc)
+        kw.update(over)
+        with pytest.raises(ValueError):
+            lutq.matmul(kw.pop("x"), P, kw.pop("lut"), kw.pop("scales"), **kw)
+    with pytest.raises(TypeError):
+        lutq.matmul(x, P, lut.float(), sc)
+    with pytest.raises(TypeError):                             # right shapes, but on the CPU
+        lutq.matmul(x, P, lut, sc)
+    with pytest.raises(TypeError):
+        lutq.matmul(x, "not packed", lut, sc)
+    # binary coding: q planes of alphas and the output shape
+    Pq = _cpu_packed(N, K, 3, 128)
+    with pytest.raises(ValueError):
+        lutq.matmul_bcq(x, Pq, torch.zeros((2, N, K // 128), dtype=f16))
+    with pytest.raises(ValueError):
+        lutq.matmul_bcq(x, Pq, torch.zeros((3, N, K // 128), dtype=f16),
+                        out=torch.zeros((2, N - 1), dtype=f16))
+    with pytest.raises(TypeError):
+        lutq.matmul_bcq(x, Pq, torch.zeros((3, N, K // 128), dtype=f16))
+    # the fused launch: per-matrix checks and K across matrices
+    P2 = _cpu_packed(32, K, 4, 128)
+    sc2 = torch.zeros((32, K // 128), dtype=f16)
+    with pytest.raises(ValueError):
+        lutq.matmul_multi(x, [(P, lut, sc), (P2, lut, sc)])
+    with pytest.raises(ValueError):
+        lutq.matmul_multi(x, [(P, lut, sc), (_cpu_packed(32, 2 * K, 4, 128), lut, sc2)])
+    with pytest.raises(ValueError):
+        lutq.matmul_multi(x, [(P, lut, sc)], outs=[])
+    with pytest.raises(TypeError):
+        lutq.matmul_multi(x, [(P, lut, sc), (P2, lut, sc2)])
+    # the quantizer: 2-D weights and a 2^bits table
+    w = torch.zeros((N, K), dtype=torch.float32)
+    with pytest.raises(ValueError):
+        lutq.quantize(w, torch.zeros(8, dtype=f16), 4, 128)
+    with pytest.raises(ValueError):
+        lutq.quantize(w.view(-1), lut, 4, 128)
+    with pytest.raises(TypeError):
+        lutq.quantize(w, lut, 4, 128)
 
 
 def test_packed_bytes():

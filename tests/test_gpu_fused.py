@@ -123,7 +123,8 @@ def test_fused_degenerate(lutq):
                            [(Pk[0], lut, sc), (Pk[1], lut, sc)], outs=outs)
     torch.cuda.synchronize()
     assert all(bool((y == 0).all()) for y in ys)
-    # mismatched K is rejected
+    # mismatched K is rejected (by the binding; the C entry point's own check is
+    # covered on the CPU in test_abi.py)
     Pbad = lutq.repack(dev(mats[0][0][:, :128]), 4, 128)
-    with pytest.raises(lutq.LutqError):
+    with pytest.raises(ValueError):
         lutq.matmul_multi(xd, [dm[0], (Pbad, dm[0][1], dm[0][2])])

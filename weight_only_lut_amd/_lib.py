@@ -187,14 +187,48 @@ def _ptr(t):
     return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
 
 
-def _need_cuda(t, name, dtype):
+def _check(t, name, dtype, shape=None, numel=None):
+    """Type, dtype, contiguity and size of one tensor argument (no device
+    check: see _on_device). ``shape`` is the exact shape, ``numel`` the exact
+    element count, either may be None."""
     import torch
-    if not isinstance(t, torch.Tensor) or not t.is_cuda:
-        raise TypeError(f"{name} must be a CUDA (HIP) tensor")
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
     if t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if numel is not None and numel > 0 and t.numel() != numel:   # 0: nothing is read
+        raise ValueError(f"{name} has {t.numel()} elements, expected {numel}")
+
+
+def _on_device(*tensors):
+    """Every tensor is a CUDA (HIP) tensor on the device of the first."""
+    dev = None
+    for name, t in tensors:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise TypeError(f"{name} must be a CUDA (HIP) tensor")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, the other arguments on {dev}")
+
+
+def _need_cuda(t, name, dtype):
+    _check(t, name, dtype)
+    _on_device((name, t))
+
+
+def _groups(p) -> int:
+    """Scale-like entries per matrix: N * K / group, or 1 for one scale per
+    tensor; 0 for an empty matrix (nothing is read)."""
+    if p.N == 0 or p.K == 0:
+        return 0
+    return p.N * (p.K // p.group) if p.group else 1
 
 
 class Packed:
@@ -214,6 +248,8 @@ class Packed:
 def repack(codes, bits: int, group: int) -> Packed:
     """lutq_repack: uint8 codes [N, K] on the GPU -> Packed (wave-block layout)."""
     import torch
+    if not isinstance(codes, torch.Tensor) or codes.dim() != 2:
+        raise ValueError("codes must be a 2-D tensor [N, K]")
     _need_cuda(codes, "codes", torch.uint8)
     N, K = codes.shape
     nbytes = packed_bytes(N, K, bits, group)
@@ -243,22 +279,32 @@ def matmul(x, p: Packed, lut, scales, *, zeros=None, types=None, path: str = "au
     y[M, N] = x[M, K] . dequant(p, lut, scales[, zeros][, types])^T, fp16 out."""
     import torch
     tdt, ldt = _act_dtype(x)
-    _need_cuda(x, "x", tdt)
-    _need_cuda(lut, "lut", torch.float16)
-    _need_cuda(scales, "scales", torch.float16)
+    if not isinstance(p, Packed):
+        raise TypeError("p must be a Packed (from repack)")
+    if not isinstance(x, torch.Tensor) or x.dim() != 2:
+        raise ValueError("x must be a 2-D tensor [M, K]")
     M, K = x.shape
+    _check(x, "x", tdt, shape=(M, p.K))
+    L = 1 << p.bits
+    if types is not None:
+        _check(lut, "lut", torch.float16)
+        nt = lut.shape[0] if lut.dim() == 2 else 1
+        if lut.numel() != nt * L or not 1 <= nt <= MAX_TYPES:
+            raise ValueError(f"lut must be [ntypes, {L}] with 1 <= ntypes <= {MAX_TYPES}")
+        _check(types, "types", torch.uint8, numel=_groups(p))
+    else:
+        _check(lut, "lut", torch.float16, numel=L)
+    _check(scales, "scales", torch.float16, numel=_groups(p))
+    if zeros is not None:
+        _check(zeros, "zeros", torch.float16, numel=_groups(p))
+    if out is not None:
+        _check(out, "out", tdt, shape=(M, p.N))
+    _on_device(("x", x), ("packed data", p.data), ("lut", lut), ("scales", scales),
+               ("zeros", zeros), ("types", types), ("out", out))
     if out is None:
         out = torch.empty((M, p.N), dtype=tdt, device=x.device)
-    else:
-        _need_cuda(out, "out", tdt)
-        if tuple(out.shape) != (M, p.N):
-            raise ValueError("out has the wrong shape")
     opts = _options(path, ksplit, tiles, ldt)
     if types is not None:
-        _need_cuda(types, "types", torch.uint8)
-        if zeros is not None:
-            _need_cuda(zeros, "zeros", torch.float16)
-        nt = lut.shape[0] if lut.dim() == 2 else 1
         rc = _lib().lutq_matmul_typed(_ptr(x), ctypes.byref(p.desc), _ptr(lut), nt, _ptr(types),
                                       _ptr(scales), _ptr(zeros), _ptr(out), M, p.N, K,
                                       ctypes.byref(opts), _stream(x.device))
@@ -266,7 +312,6 @@ def matmul(x, p: Packed, lut, scales, *, zeros=None, types=None, path: str = "au
         rc = _lib().lutq_matmul_ex(_ptr(x), ctypes.byref(p.desc), _ptr(lut), _ptr(scales),
                                    _ptr(out), M, p.N, K, ctypes.byref(opts), _stream(x.device))
     else:
-        _need_cuda(zeros, "zeros", torch.float16)
         rc = _lib().lutq_matmul_zp(_ptr(x), ctypes.byref(p.desc), _ptr(lut), _ptr(scales),
                                    _ptr(zeros), _ptr(out), M, p.N, K, ctypes.byref(opts),
                                    _stream(x.device))
@@ -281,27 +326,39 @@ def matmul_multi(x, mats, *, path: str = "auto", ksplit: int = 0, tiles: int = 0
     (Packed, lut, scales, zeros); returns the list of fp16 outputs y_i [M, N_i]."""
     import torch
     tdt, ldt = _act_dtype(x)
-    _need_cuda(x, "x", tdt)
+    if not isinstance(x, torch.Tensor) or x.dim() != 2:
+        raise ValueError("x must be a 2-D tensor [M, K]")
     M, K = x.shape
+    _check(x, "x", tdt)
     if not 1 <= len(mats) <= MAX_FUSED:
         raise ValueError(f"1 to {MAX_FUSED} matrices per fused launch")
+    if outs is not None and len(outs) != len(mats):
+        raise ValueError("one output per matrix")
     items = (MatmulItem * len(mats))()
     ys = []
-    for i, mat in enumerate(mats):
+    args = []
+    for i, mat in enumerate(mats):       # shapes and sizes of every matrix first
         p, lut, scales = mat[:3]
         zeros = mat[3] if len(mat) > 3 else None
-        _need_cuda(lut, "lut", torch.float16)
-        _need_cuda(scales, "scales", torch.float16)
+        if not isinstance(p, Packed):
+            raise TypeError(f"matrix {i}: the first entry must be a Packed (from repack)")
+        if p.K != K:
+            raise ValueError(f"matrix {i} has K = {p.K}, x has K = {K}")
+        _check(lut, f"lut[{i}]", torch.float16, numel=1 << p.bits)
+        _check(scales, f"scales[{i}]", torch.float16, numel=_groups(p))
         if zeros is not None:
-            _need_cuda(zeros, "zeros", torch.float16)
+            _check(zeros, f"zeros[{i}]", torch.float16, numel=_groups(p))
+        y = None if outs is None else outs[i]
+        if y is not None:
+            _check(y, f"out[{i}]", tdt, shape=(M, p.N))
+        args.append((p, lut, scales, zeros, y))
+    for i, (p, lut, scales, zeros, y) in enumerate(args):
+        _on_device(("x", x), (f"packed data[{i}]", p.data), (f"lut[{i}]", lut),
+                   (f"scales[{i}]", scales), (f"zeros[{i}]", zeros), (f"out[{i}]", y))
+        if zeros is not None:
             items[i].zeros = zeros.data_ptr()
-        if outs is None:
+        if y is None:
             y = torch.empty((M, p.N), dtype=tdt, device=x.device)
-        else:
-            y = outs[i]
-            _need_cuda(y, "out", tdt)
-            if tuple(y.shape) != (M, p.N):
-                raise ValueError("out has the wrong shape")
         ys.append(y)
         items[i].packed = ctypes.pointer(p.desc)
         items[i].lut, items[i].scales, items[i].y = lut.data_ptr(), scales.data_ptr(), y.data_ptr()
@@ -318,9 +375,16 @@ def matmul_bcq(x, p: Packed, alphas, *, path: str = "auto", ksplit: int = 0, til
     """lutq_matmul_bcq: binary-coded weights (p packed with bits = q planes,
     alphas fp16 [q, N, K/group]) -> y[M, N] fp16."""
     import torch
-    _need_cuda(x, "x", torch.float16)
-    _need_cuda(alphas, "alphas", torch.float16)
+    if not isinstance(p, Packed):
+        raise TypeError("p must be a Packed (from repack)")
+    if not isinstance(x, torch.Tensor) or x.dim() != 2:
+        raise ValueError("x must be a 2-D tensor [M, K]")
     M, K = x.shape
+    _check(x, "x", torch.float16, shape=(M, p.K))
+    _check(alphas, "alphas", torch.float16, numel=p.bits * _groups(p))
+    if out is not None:
+        _check(out, "out", torch.float16, shape=(M, p.N))
+    _on_device(("x", x), ("packed data", p.data), ("alphas", alphas), ("out", out))
     if out is None:
         out = torch.empty((M, p.N), dtype=torch.float16, device=x.device)
     opts = _options(path, ksplit, tiles)
@@ -335,12 +399,14 @@ WEIGHT_F32, WEIGHT_F16, WEIGHT_BF16 = 0, 1, 2
 
 
 def _weight_dtype(w) -> int:
-    """The LUTQ_WEIGHT_* value of a weight tensor (fp32, fp16 or bf16 on the GPU)."""
+    """The LUTQ_WEIGHT_* value of a weight tensor (fp32, fp16 or bf16 [N, K] on the GPU)."""
     import torch
     codes = {torch.float32: WEIGHT_F32, torch.float16: WEIGHT_F16, torch.bfloat16: WEIGHT_BF16}
     if not isinstance(w, torch.Tensor) or w.dtype not in codes:
         raise TypeError("w must be a float32, float16 or bfloat16 tensor")
-    _need_cuda(w, "w", w.dtype)
+    if w.dim() != 2:
+        raise ValueError("w must be a 2-D tensor [N, K]")
+    _check(w, "w", w.dtype)
     return codes[w.dtype]
 
 
@@ -349,7 +415,8 @@ def quantize(w, lut, bits: int, group: int, rule: str = "absmax"):
     [N, K/group] or [1]), round-to-nearest onto the table ``lut``."""
     import torch
     wdt = _weight_dtype(w)
-    _need_cuda(lut, "lut", torch.float16)
+    _check(lut, "lut", torch.float16, numel=1 << bits)
+    _on_device(("w", w), ("lut", lut))
     N, K = w.shape
     codes = torch.empty((N, K), dtype=torch.uint8, device=w.device)
     scales = torch.empty((N, K // group) if group else (1,), dtype=torch.float16, device=w.device)
@@ -364,7 +431,8 @@ def quant_error(w, lut, bits: int, group: int, rule: str = "absmax") -> float:
     """lutq_quant_error: sum (w - s * T[c])^2 (fp64) of that quantization."""
     import torch
     wdt = _weight_dtype(w)
-    _need_cuda(lut, "lut", torch.float16)
+    _check(lut, "lut", torch.float16, numel=1 << bits)
+    _on_device(("w", w), ("lut", lut))
     N, K = w.shape
     err = ctypes.c_double(0.0)
     rc = _lib().lutq_quant_error_ex(_ptr(w), wdt, _ptr(lut), bits, N, K, group, _RULES[rule],
@@ -376,8 +444,8 @@ def quant_error(w, lut, bits: int, group: int, rule: str = "absmax") -> float:
 
 def log_base_search(w, bits: int, group: int, bases):
     """lutq_log_base_search: (index of the best base, [error of each base])."""
-    import torch
     wdt = _weight_dtype(w)
+    _on_device(("w", w))
     N, K = w.shape
     nb = len(bases)
     arr = (ctypes.c_double * nb)(*[float(b) for b in bases])
@@ -395,7 +463,8 @@ def tune_table(w, lut, bits: int, group: int, rule: str = "absmax", iters: int =
     Returns (tuned table fp16 [2^bits], fixed scales fp16, [error of each table])."""
     import torch
     wdt = _weight_dtype(w)
-    _need_cuda(lut, "lut", torch.float16)
+    _check(lut, "lut", torch.float16, numel=1 << bits)
+    _on_device(("w", w), ("lut", lut))
     N, K = w.shape
     T = lut.clone()
     scales = torch.empty((N, K // group) if group else (1,), dtype=torch.float16, device=w.device)
