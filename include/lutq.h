@@ -39,7 +39,8 @@
  * each call once eagerly on a stream before capturing it there. A graph
  * holding split launches uses the buffer of the stream it was captured on:
  * do not replay it concurrently with other lutq work on that stream (or
- * with another replay of itself).
+ * with another replay of itself). lutq_matmul_noalloc (below) uses a fixed
+ * array instead and never allocates.
  */
 #ifndef LUTQ_H
 #define LUTQ_H
@@ -188,6 +189,28 @@ enum { LUTQ_DTYPE_F16 = 0, LUTQ_DTYPE_BF16 = 1 };
 int lutq_matmul_ex(const uint16_t* x, const lutq_packed_t* packed, const uint16_t* lut,
                    const uint16_t* scales, uint16_t* y, int M, int N, int K,
                    const lutq_options_t* opts, void* stream);
+
+/* lutq_matmul_ex for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * The split-K partial sums and arrival counters live in a fixed array in the
+ * library's device image (LUTQ_NOALLOC_SCRATCH_BYTES per GPU, each GPU the
+ * library runs on holding its own copy until the process ends) instead of
+ * the per-stream buffer lutq_matmul_ex allocates; the call allocates no
+ * device memory at all. Arguments, options and numerics are those of
+ * lutq_matmul_ex, and the result is bit-identical to lutq_matmul_ex with the
+ * same options. A call whose K split needs more partial sums than the array
+ * holds (only an explicit large ksplit does: the automatic plan needs at
+ * most 2 MiB) returns LUTQ_EUNSUPPORTED and enqueues nothing.
+ * Every call on one GPU shares that GPU's array: calls that overlap in time
+ * on one GPU (on different streams, or a graph replayed alongside other
+ * lutq_matmul_noalloc work) race and give wrong results, so serialize them.
+ * The array is zero when the library is loaded; each launch leaves its
+ * counters at zero, and the first call on a device clears them once more
+ * on its stream. */
+#define LUTQ_NOALLOC_SCRATCH_BYTES (8u << 20)
+int lutq_matmul_noalloc(const uint16_t* x, const lutq_packed_t* packed, const uint16_t* lut,
+                        const uint16_t* scales, uint16_t* y, int M, int N, int K,
+                        const lutq_options_t* opts, void* stream);
 
 /* The options lutq_matmul_ex resolves for this call (host-side heuristic
  * only, no device work): `req` (host, may be NULL = all automatic) is

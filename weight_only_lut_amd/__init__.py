@@ -23,6 +23,7 @@ from ._lib import (  # noqa: F401
     matmul,
     matmul_bcq,
     matmul_multi,
+    matmul_noalloc,
     packed_bytes,
     plan,
     quant_error,

@@ -24,6 +24,7 @@ EXPORTS = (
     "lutq_quantize", "lutq_quant_error", "lutq_log_base_search", "lutq_matmul_multi",
     "lutq_matmul_zp", "lutq_matmul_typed", "lutq_matmul_bcq",
     "lutq_quantize_ex", "lutq_quant_error_ex", "lutq_log_base_search_ex", "lutq_tune_table",
+    "lutq_matmul_noalloc",
 )
 
 MAX_TYPES = 4
@@ -91,6 +92,9 @@ def load_library():
     lib.lutq_matmul_ex.argtypes = [vp, ctypes.POINTER(PackedDesc), vp, vp, vp, i32, i32, i32,
                                    ctypes.POINTER(Options), vp]
     lib.lutq_matmul_ex.restype = i32
+    lib.lutq_matmul_noalloc.argtypes = [vp, ctypes.POINTER(PackedDesc), vp, vp, vp, i32, i32, i32,
+                                        ctypes.POINTER(Options), vp]
+    lib.lutq_matmul_noalloc.restype = i32
     lib.lutq_plan.argtypes = [i32, i32, i32, i32, ctypes.POINTER(Options), ctypes.POINTER(Options)]
     lib.lutq_matmul_multi.argtypes = [vp, ctypes.POINTER(MatmulItem), i32, i32, i32,
                                       ctypes.POINTER(Options), vp]
@@ -317,6 +321,34 @@ def matmul(x, p: Packed, lut, scales, *, zeros=None, types=None, path: str = "au
                                    _stream(x.device))
     if rc:
         raise LutqError(rc, "lutq_matmul")
+    return out
+
+
+def matmul_noalloc(x, p: Packed, lut, scales, *, path: str = "auto", ksplit: int = 0,
+                   tiles: int = 0, out=None):
+    """lutq_matmul_noalloc: lutq_matmul_ex with its split-K scratch in the
+    library's fixed per-GPU array (no device allocation by the library);
+    bit-identical to ``matmul`` with the same options."""
+    import torch
+    tdt, ldt = _act_dtype(x)
+    if not isinstance(p, Packed):
+        raise TypeError("p must be a Packed (from repack)")
+    if not isinstance(x, torch.Tensor) or x.dim() != 2:
+        raise ValueError("x must be a 2-D tensor [M, K]")
+    M, K = x.shape
+    _check(x, "x", tdt, shape=(M, p.K))
+    _check(lut, "lut", torch.float16, numel=1 << p.bits)
+    _check(scales, "scales", torch.float16, numel=_groups(p))
+    if out is not None:
+        _check(out, "out", tdt, shape=(M, p.N))
+    _on_device(("x", x), ("packed data", p.data), ("lut", lut), ("scales", scales), ("out", out))
+    if out is None:
+        out = torch.empty((M, p.N), dtype=tdt, device=x.device)
+    opts = _options(path, ksplit, tiles, ldt)
+    rc = _lib().lutq_matmul_noalloc(_ptr(x), ctypes.byref(p.desc), _ptr(lut), _ptr(scales), _ptr(out),
+                                    M, p.N, K, ctypes.byref(opts), _stream(x.device))
+    if rc:
+        raise LutqError(rc, "lutq_matmul_noalloc")
     return out
 
 

@@ -191,7 +191,7 @@ void plan(int M, int N, int K, int cus, lutq_options_t* o) {
 // per batch slice covers every matrix with N > 0.
 int run_matmul(const uint16_t* x, const lutq_matmul_item_t* items, int count, int M, int K,
                const lutq_options_t* opts, void* stream, const uint8_t* types = nullptr,
-               int ntypes = 0, bool bcq = false) {
+               int ntypes = 0, bool bcq = false, bool noalloc = false) {
   lutq_options_t o;
   int rc = read_options(opts, &o);
   if (rc) return rc;
@@ -281,8 +281,18 @@ int run_matmul(const uint16_t* x, const lutq_matmul_item_t* items, int count, in
     if ((size_t)nrb * sizeof(uint32_t) > kCounterBytes) return LUTQ_EUNSUPPORTED;
     const size_t rows = (size_t)o.tiles * lutq::kTileRows;
     const size_t pbytes = (size_t)nrb * (size_t)ksplit * rl * rows * sizeof(float);
-    rc = get_scratch(stream, pbytes, &p.partial, &p.counters);
-    if (rc) return rc;
+    if (noalloc) {
+      // the fixed array of lutq_static.hip: counters, then partial sums
+      if (pbytes > lutq::kStaticScratchBytes - kCounterBytes) return LUTQ_EUNSUPPORTED;
+      void* base = nullptr;
+      hipError_t e = lutq::static_scratch(&base, (hipStream_t)stream);
+      if (e != hipSuccess) return hip_fail(e);
+      p.counters = reinterpret_cast<uint32_t*>(base);
+      p.partial = reinterpret_cast<float*>(reinterpret_cast<char*>(base) + kCounterBytes);
+    } else {
+      rc = get_scratch(stream, pbytes, &p.partial, &p.counters);
+      if (rc) return rc;
+    }
   }
   const int bits = d0->bits;
   for (int m0 = 0; m0 < M; m0 += rl) {
@@ -374,6 +384,17 @@ int lutq_matmul_ex(const uint16_t* x, const lutq_packed_t* packed, const uint16_
   return run_matmul(x, &item, 1, M, K, opts, stream);
 }
 
+int lutq_matmul_noalloc(const uint16_t* x, const lutq_packed_t* packed, const uint16_t* lut,
+                        const uint16_t* scales, uint16_t* y, int M, int N, int K,
+                        const lutq_options_t* opts, void* stream) {
+  int rc = check_desc(packed);
+  if (rc) return rc;
+  if (M < 0 || N < 0 || K < 0) return LUTQ_EINVAL;
+  if (N != packed->N || K != packed->K) return LUTQ_EMISMATCH;
+  const lutq_matmul_item_t item = {packed, lut, scales, nullptr, y};
+  return run_matmul(x, &item, 1, M, K, opts, stream, nullptr, 0, false, true);
+}
+
 int lutq_matmul_typed(const uint16_t* x, const lutq_packed_t* packed, const uint16_t* luts,
                       int ntypes, const uint8_t* types, const uint16_t* scales,
                       const uint16_t* zeros, uint16_t* y, int M, int N, int K,
@@ -437,6 +458,7 @@ int lutq_matmul(const uint16_t* x, const lutq_packed_t* packed, const uint16_t* 
 namespace {
 
 static_assert(LUTQ_MAX_FUSED == lutq::kMaxSegments, "one kernel segment per fused matrix");
+static_assert(LUTQ_NOALLOC_SCRATCH_BYTES == lutq::kStaticScratchBytes, "the fixed scratch array");
 static_assert(LUTQ_MAX_TYPES == lutq::kMaxTypes, "tables the pair table holds");
 static_assert(LUTQ_RULE_ABSMAX == lutq::kRuleAbsmax && LUTQ_RULE_RANGE == lutq::kRuleRange,
               "rule values");

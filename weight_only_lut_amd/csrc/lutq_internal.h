@@ -54,6 +54,12 @@ enum Path { kPathGemv = 1, kPathMfma = 2 };
 // counter per row block of a launch (up to 16384), zero between launches.
 constexpr size_t kSplitCounterBytes = 64 * 1024;
 
+// The fixed scratch of lutq_matmul_noalloc (counters, then partial sums), per
+// device; static_scratch returns the current device's copy, looked up (and
+// its counters cleared on stream s) on the first call for that device.
+constexpr size_t kStaticScratchBytes = 8u << 20;
+hipError_t static_scratch(void** out, hipStream_t s);
+
 // Rows of x one launch of each path handles.
 constexpr int kGemvMaxRows = 8;
 constexpr int kMfmaMaxRows = 32;
