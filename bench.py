@@ -5,12 +5,20 @@ Headline step: one lutq_matmul call on the Llama-3-8B MLP up-projection shape
 weights, batch M = 1 -- the HBM-bound GEMV. Weights are "cold": every call
 reads a different copy of the packed matrix, and the copies together exceed
 the 256 MB Infinity Cache, so the bytes come from HBM. Also measured in the
-same run (reported beside the headline):
+same run (reported under "extra"):
 
 - the same call with one warm copy (Infinity-Cache resident);
 - batch 32 on the Llama-70B-shaped log table (N = 28672, K = 8192,
   tensor-wise scale): TFLOP/s against the fp16 MFMA peak;
-- the CPU oracle on a bounded sample of the headline workload.
+- the machine's measured floors (peak microbenchmarks of liblutq.so): the
+  launch cost, streaming reads of several sizes, the fp16 MFMA issue rate
+  and the random LDS read rate;
+- every workload matrix at every batch size of its config, and the
+  Llama-3-8B layer as 7 calls and as 4 (fused q/k/v and gate + up), each
+  against the roofline that bounds it, at published and at measured peaks;
+- the quantizer, fused launches, variants and a dense fp16 context row;
+- the CPU oracle on the headline workload (all cores) and on the small
+  configs with all cores and with one.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--sweep]
 """
@@ -30,7 +38,8 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 MFMA, published
 CACHE_BYTES = 256 << 20        # Infinity Cache (MALL)
 COLD_SET_BYTES = 2 * CACHE_BYTES
-EXTRA_REPEATS = 3  # timed replays per secondary line (median)
+EXTRA_REPEATS = 3    # timed replays per secondary line (median)
+HEADLINE_REPEATS = 7  # timed replays of the headline (median, spread reported)
 
 
 def algorithmic_bytes(M, N, K, bits, group):
@@ -79,16 +88,249 @@ class Case:
     def call(self, lutq, i):
         lutq.matmul(self.x, self.packed[i % len(self.packed)], self.lut, self.scales, out=self.y)
 
+    def at(self, torch, M):
+        """The same device inputs at batch M <= self.M (the first M rows of x)."""
+        c = Case.__new__(Case)
+        c.__dict__.update(self.__dict__)
+        c.M = M
+        c.x = self.x[:M].contiguous()
+        c.y = torch.empty((M, self.N), dtype=torch.float16, device="cuda")
+        c.bytes = algorithmic_bytes(M, self.N, self.K, self.w.bits, self.w.group)
+        c.flops = 2 * M * self.N * self.K
+        c.host = self.host[:3] + (self.host[3][:M],)
+        return c
 
-def time_case(lutq, torch, case, steps, warmup, repeats=1):
-    """Average microseconds per call over exactly `steps` back-to-back calls.
+
+class Inputs:
+    """Device inputs of every workload matrix, generated once at the largest
+    batch of its workload (cold copies), shared by the sections below."""
+
+    def __init__(self, lutq, torch):
+        self.lutq, self.torch, self.cases = lutq, torch, {}
+
+    def get(self, wname, mat, M):
+        from synth import workloads
+        w = workloads.WORKLOADS[wname]
+        key = (wname, mat or w.matrices[0].name)
+        if key not in self.cases:
+            self.cases[key] = Case(self.lutq, self.torch, wname, key[1], max(max(w.batches), M))
+        base = self.cases[key]
+        if M > base.M:
+            raise ValueError(f"{key} was generated for batch {base.M}")
+        return base if M == base.M else base.at(self.torch, M)
+
+
+def roof_time_us(nbytes, flops, gbps, tflops):
+    """Time at the bounding roofline: the larger of the memory and the MFMA time."""
+    return max(nbytes / (gbps * 1e3), flops / (tflops * 1e6))
+
+
+class StreamFloor:
+    """Measured time of a streaming read (with its final store) of a given
+    byte count, from the peak microbenchmark at several sizes: linear
+    between measured sizes, never below the launch floor."""
+
+    def __init__(self, points, empty_us):
+        self.pts = sorted(points)  # (bytes, us)
+        self.empty = empty_us
+
+    def __call__(self, nbytes):
+        pts = self.pts
+        if nbytes <= pts[0][0]:
+            b0, t0 = pts[0]
+            return max(self.empty, t0 * nbytes / b0) if nbytes < b0 else t0
+        for (b0, t0), (b1, t1) in zip(pts, pts[1:]):
+            if nbytes <= b1:
+                return t0 + (t1 - t0) * (nbytes - b0) / (b1 - b0)
+        (b0, t0), (b1, t1) = pts[-2], pts[-1]
+        return t1 + (t1 - t0) * (nbytes - b1) / (b1 - b0)
+
+    def gbps(self):
+        """The asymptotic rate: the slope between the two largest sizes."""
+        (b0, t0), (b1, t1) = self.pts[-2], self.pts[-1]
+        return (b1 - b0) / ((t1 - t0) * 1e3)
+
+
+STREAM_SIZES = (1 << 20, 4 << 20, 16 << 20, 30314528 & ~15, 64 << 20, 119799842 & ~15, 256 << 20,
+                512 << 20)
+
+
+def peaks_section(lutq, torch, args):
+    """The measured floors (include/lutq_peaks.h), timed like the matmul."""
+    out = {}
+    steps, warm = 50, 5
+    out["empty_launch_us"] = round(time_case(lutq, torch, Fn(lambda i: lutq.peak_empty()), 200, warm,
+                                             repeats=5), 3)
+    log(f"[bench] peaks: empty launch {out['empty_launch_us']} us")
+    pool_bytes = 3 * (512 << 20)
+    pool = torch.zeros(pool_bytes, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(lutq.peak_stream_sink_bytes(), dtype=torch.uint8, device="cuda")
+    rows, floor_pts = [], []
+    for nbytes in STREAM_SIZES:
+        ncopy = max(2, min(pool_bytes // nbytes, -(-(3 * CACHE_BYTES) // nbytes)))
+        rec = {"bytes": nbytes, "copies": ncopy}
+        for store in (False, True):
+            fn = Fn(lambda i, b=nbytes, st=store, n=ncopy:
+                    lutq.peak_stream(pool[(i % n) * b:], b, st, sink))
+            us = time_case(lutq, torch, fn, max(10, steps // (1 + nbytes // (64 << 20))), warm,
+                           repeats=EXTRA_REPEATS)
+            rec["with_store" if store else "read_only"] = {"us": round(us, 3),
+                                                          "GBps": round(nbytes / (us * 1e3), 1)}
+        floor_pts.append((nbytes, rec["with_store"]["us"]))
+        rows.append(rec)
+        log(f"[bench] peaks: stream {nbytes / 1e6:.1f} MB: {rec['read_only']['us']} us read, "
+            f"{rec['with_store']['us']} us with store")
+    del pool
+    torch.cuda.empty_cache()
+    floor = StreamFloor(floor_pts, out["empty_launch_us"])
+    out["stream"] = rows
+    out["stream_asymptotic_GBps"] = round(floor.gbps(), 1)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    fsink = torch.zeros(cus * 16, dtype=torch.float32, device="cuda")
+    mf = {}
+    for kind, name in ((lutq.PEAK_MFMA_16X16X32, "16x16x32_f16"),
+                       (lutq.PEAK_MFMA_32X32X16, "32x32x16_f16")):
+        for wps in (1, 2, 4):
+            iters = 400
+            us = time_case(lutq, torch, Fn(lambda i, k=kind, w=wps: lutq.peak_mfma(k, w, iters, fsink)),
+                           20, warm, repeats=EXTRA_REPEATS)
+            flops = cus * 4 * wps * iters * lutq.PEAK_MFMA_FLOPS_PER_ROUND
+            mf[f"{name}_waves_per_simd{wps}"] = {"us": round(us, 3),
+                                                 "TFLOPs": round(flops / (us * 1e6), 1)}
+    out["mfma"] = mf
+    out["mfma_best_TFLOPs"] = max(v["TFLOPs"] for v in mf.values())
+    log(f"[bench] peaks: fp16 MFMA best {out['mfma_best_TFLOPs']} TFLOP/s")
+    isink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    lds = {}
+    for wpc in (4, 8, 16):
+        iters = 200
+        us = time_case(lutq, torch, Fn(lambda i, w=wpc: lutq.peak_lds(w, iters, isink)), 20, warm,
+                       repeats=EXTRA_REPEATS)
+        instrs = cus * wpc * 16 * iters
+        lds[f"waves_per_cu{wpc}"] = {"us": round(us, 3),
+                                     "ds_read_b32_per_us_per_cu": round(instrs / cus / us, 1),
+                                     "lane_reads_per_s": round(instrs * 64 / (us * 1e-6), 0)}
+    out["lds_random_read"] = lds
+    out["note"] = ("stream: 2048 workgroups of 256 threads read the buffer once (16-byte nontemporal "
+                   "loads), cold (rotating copies); with_store adds one 16-byte store per wave at "
+                   "the end, as a matmul writing y. Each row of extra.configs is compared with the "
+                   "with_store time interpolated at its algorithmic bytes.")
+    return out, floor
+
+
+def row_stats(us, nbytes, flops):
+    """µs, GB/s, TFLOP/s and the fraction of the bounding roofline of one case."""
+    spec = roof_time_us(nbytes, flops, HBM_PEAK_GBS, MFMA_F16_PEAK_TFLOPS)
+    hbm_t, mfma_t = nbytes / (HBM_PEAK_GBS * 1e3), flops / (MFMA_F16_PEAK_TFLOPS * 1e6)
+    return {"us": round(us, 3), "GBps": round(nbytes / (us * 1e3), 1),
+            "TFLOPs": round(flops / (us * 1e6), 2), "bytes": nbytes, "flops": flops,
+            "bound": "hbm" if hbm_t >= mfma_t else "mfma",
+            "frac_of_roof": round(spec / us, 4)}
+
+
+def measured_roof(rec, floor, mfma_meas):
+    """Adds the roofline at the measured floors to a row of row_stats: the
+    streaming read with its store at the same bytes, or the measured MFMA
+    rate, whichever takes longer."""
+    meas = max(floor(rec["bytes"]), rec["flops"] / (mfma_meas * 1e6))
+    rec["measured_roof_us"] = round(meas, 3)
+    rec["frac_of_measured_roof"] = round(meas / rec["us"], 4)
+
+
+def add_measured_roofs(extra, floor, mfma_meas):
+    for rec in extra.get("configs", []):
+        measured_roof(rec, floor, mfma_meas)
+    for rec in extra.get("layer_totals", []):
+        measured_roof(rec["separate"], floor, mfma_meas)
+        measured_roof(rec["fused"], floor, mfma_meas)
+    b = extra.get("batch32")
+    if b:
+        r = {"us": b["us_per_call"], "bytes": b["bytes"], "flops": b["flops"]}
+        measured_roof(r, floor, mfma_meas)
+        b["measured_roof_us"], b["frac_of_measured_roof"] = r["measured_roof_us"], r["frac_of_measured_roof"]
+
+
+class LayerCase:
+    """The seven projections of the Llama-3-8B layer at batch M, cold: either
+    one call per matrix, or q/k/v and gate + up as fused launches (4 calls)."""
+
+    def __init__(self, inputs, torch, M):
+        from synth import workloads
+        w = workloads.WORKLOADS["nf4_layer"]
+        self.parts = {m.name: inputs.get("nf4_layer", m.name, M) for m in w.matrices}
+        self.fused = False
+        x_q, x_g = self.parts["q"].x, self.parts["gate"].x
+        K = self.parts["q"].K
+        self.bytes = sum(p.bytes for p in self.parts.values())
+        # q, k, v read the same x; gate and up read the same x
+        self.fused_bytes = self.bytes - 2 * M * K * 2 - M * K * 2
+        self.flops = sum(p.flops for p in self.parts.values())
+        self.xs = {"qkv": x_q, "gate_up": x_g}
+
+    def call(self, lutq, i):
+        P = self.parts
+        if not self.fused:
+            for p in P.values():
+                p.call(lutq, i)
+            return
+        for key, names in (("qkv", ("q", "k", "v")), ("gate_up", ("gate", "up"))):
+            lutq.matmul_multi(self.xs[key], [(P[n].packed[i % len(P[n].packed)], P[n].lut, P[n].scales)
+                                             for n in names], outs=[P[n].y for n in names])
+        P["o"].call(lutq, i)
+        P["down"].call(lutq, i)
+
+
+def configs_section(lutq, torch, args, inputs):
+    """Every matrix of every config at each of its batch sizes (automatic plan,
+    cold weights), then the Llama-3-8B layer totals."""
+    from synth import workloads
+    steps = max(20, args.steps // 10)
+    rows = []
+    for wname, w in workloads.WORKLOADS.items():
+        for m in w.matrices:
+            for M in w.batches:
+                case = inputs.get(wname, m.name, M)
+                us = time_case(lutq, torch, case, steps, args.warmup, repeats=EXTRA_REPEATS)
+                rec = {"workload": wname, "matrix": m.name, "N": m.N, "K": m.K, "M": M,
+                       "bits": w.bits, "table": w.table, "group": w.group,
+                       "plan": lutq.plan(M, m.N, m.K, w.bits)}
+                rec.update(row_stats(us, case.bytes, case.flops))
+                rows.append(rec)
+                log(f"[bench] config {wname}/{m.name} M={M}: {us:.2f} us, {rec['GBps']} GB/s, "
+                    f"{rec['frac_of_roof']:.3f} of roof")
+    layer = []
+    for M in workloads.WORKLOADS["nf4_layer"].batches:
+        lc = LayerCase(inputs, torch, M)
+        rec = {"M": M, "calls_separate": 7, "calls_fused": 4}
+        for fused in (False, True):
+            lc.fused = fused
+            us = time_case(lutq, torch, lc, max(10, steps // 2), args.warmup, repeats=EXTRA_REPEATS)
+            nbytes = lc.fused_bytes if fused else lc.bytes
+            rec["fused" if fused else "separate"] = row_stats(us, nbytes, lc.flops)
+        rec["floor_us_at_8TBps"] = round(lc.bytes / (HBM_PEAK_GBS * 1e3), 3)
+        layer.append(rec)
+        log(f"[bench] layer M={M}: 7 calls {rec['separate']['us']} us, 4 calls {rec['fused']['us']} us")
+    return rows, layer
+
+
+class Fn:
+    """A timed step that calls f(i) (i = the call's index in the graph)."""
+
+    def __init__(self, f):
+        self.f = f
+
+    def call(self, lutq, i):
+        self.f(i)
+
+
+def time_replays(lutq, torch, case, steps, warmup, repeats=1):
+    """Microseconds per call of every timed replay of `steps` back-to-back calls.
 
     `warmup` eager calls, then the `steps` calls are captured in a HIP graph,
-    replayed once untimed, and replayed once more between HIP events recorded
-    on the stream the kernels run on (host-side launch cost stays outside the
-    timed region), with a device synchronization on both sides. With
-    `repeats` > 1 the timed replay is repeated and the median returned (the
-    secondary lines: one replay of a few tens of calls varies by ~10%).
+    replayed once untimed, and replayed `repeats` more times, each between
+    HIP events recorded on the stream the kernels run on (host-side launch
+    cost stays outside the timed region), with a device synchronization on
+    both sides.
     """
     stream = torch.cuda.Stream()
     with torch.cuda.stream(stream):
@@ -111,7 +353,15 @@ def time_case(lutq, torch, case, steps, warmup, repeats=1):
             stop.record()
         torch.cuda.synchronize()
         times.append(start.elapsed_time(stop) * 1e3 / steps)
-    return sorted(times)[len(times) // 2]
+    del graph
+    return times
+
+
+def time_case(lutq, torch, case, steps, warmup, repeats=1):
+    """The median of time_replays (one replay of a few tens of calls varies by
+    up to ~10%, hence the median for every line)."""
+    times = sorted(time_replays(lutq, torch, case, steps, warmup, repeats))
+    return times[len(times) // 2]
 
 
 def cpu_baseline(case, budget_s=15.0):
@@ -251,8 +501,8 @@ class FusedCase:
     or gate and up), cold, called either as one lutq_matmul per matrix or as
     one fused lutq_matmul_multi."""
 
-    def __init__(self, lutq, torch, wname, mats, M):
-        self.parts = [Case(lutq, torch, wname, m, M) for m in mats]
+    def __init__(self, inputs, wname, mats, M):
+        self.parts = [inputs.get(wname, m, M) for m in mats]
         for part in self.parts[1:]:
             part.x = self.parts[0].x
         self.fused = False
@@ -269,14 +519,14 @@ class FusedCase:
                 p.call(lutq, i)
 
 
-def fused_section(lutq, torch, args):
+def fused_section(lutq, torch, args, inputs):
     """One fused launch against one launch per matrix, for q/k/v and gate/up
     of the Llama-3-8B layer at batch 1 and 16 (cold weights)."""
     out = {}
     steps = max(20, args.steps // 4)
     for label, mats in (("qkv", ("q", "k", "v")), ("gate_up", ("gate", "up"))):
         for M in (1, 16):
-            fc = FusedCase(lutq, torch, "nf4_layer", mats, M)
+            fc = FusedCase(inputs, "nf4_layer", mats, M)
             fc.fused = False
             sep = time_case(lutq, torch, fc, steps, args.warmup, repeats=EXTRA_REPEATS)
             fc.fused = True
@@ -287,8 +537,49 @@ def fused_section(lutq, torch, args):
                 "fused_GBps": round(fc.bytes / (fus * 1e-6) / 1e9, 1),
                 "plan": lutq.plan(M, sum(-(-p.N // 16) * 16 for p in fc.parts), fc.parts[0].K, 4)}
             log(f"[bench] fused {label} M={M}: separate {sep:.2f} us, fused {fus:.2f} us")
-            del fc
-            torch.cuda.empty_cache()
+    return out
+
+
+def cpu_oracle_section(inputs, budget_s=4.0):
+    """The oracle on the small configs (batch 1), with all host cores and with
+    one BLAS thread: seconds per call and GB/s of algorithmic bytes."""
+    import numpy as np
+
+    import oracle
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:   # threadpoolctl missing: all-cores numbers only
+        threadpool_limits = None
+    out = {}
+    for wname, mat in (("nf4_1k", "w"), ("int4_up_proj", "up"), ("lm3", "sq"), ("lm3", "wide")):
+        case = inputs.cases[(wname, mat)]
+        c, T, s, x = case.host
+        w = case.w
+        x1 = x[:1]
+        nbytes = algorithmic_bytes(1, case.N, case.K, w.bits, w.group)
+        packed = oracle.pack_codes(c, w.bits)
+        rec = {"N": case.N, "K": case.K, "M": 1, "bits": w.bits}
+
+        def run():
+            times, t_all = [], time.time()
+            while (time.time() - t_all < budget_s and len(times) < 5) or len(times) < 1:
+                t0 = time.time()
+                codes = oracle.unpack_codes(packed, case.N, case.K, w.bits)
+                oracle.reference(x1, codes, T, s, w.group)
+                times.append(time.time() - t0)
+            return float(np.median(times)), len(times)
+
+        sec, n = run()
+        rec["all_cores"] = {"seconds": round(sec, 4), "GBps": round(nbytes / sec / 1e9, 4), "runs": n,
+                            "cores": len(os.sched_getaffinity(0))}
+        if threadpool_limits is not None:
+            with threadpool_limits(limits=1):
+                sec1, n1 = run()
+            rec["one_core"] = {"seconds": round(sec1, 4), "GBps": round(nbytes / sec1 / 1e9, 4),
+                               "runs": n1, "cores": 1}
+        out[f"{wname}/{mat}"] = rec
+        log(f"[bench] cpu oracle {wname}/{mat}: {rec['all_cores']['seconds']} s all cores, "
+            f"{rec.get('one_core', {}).get('seconds')} s one core")
     return out
 
 
@@ -418,6 +709,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-batch32", action="store_true")
+    ap.add_argument("--no-peaks", action="store_true", help="skip the peak microbenchmarks")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the per-config rows and the layer totals")
     ap.add_argument("--no-quantizer", action="store_true")
     ap.add_argument("--no-fused", action="store_true")
     ap.add_argument("--no-dense", action="store_true",
@@ -427,14 +721,22 @@ def main():
     ap.add_argument("--no-warm", action="store_true",
                     help="skip the Infinity-Cache-warm repeats (so a kernel trace holds cold calls only)")
     ap.add_argument("--sweep", action="store_true", help="also time every workload (stderr)")
+    ap.add_argument("--profile-set", action="store_true",
+                    help="only the profiled cases (headline, batch 32, 3-bit, batch 16), cold, "
+                         "plus the copy calibration: the workload of the committed rocprofv3 summaries")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy (for scaling memory counters)")
     ap.add_argument("--summarize-profile", nargs=3, metavar=("KERNEL_TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
                     help="write profiles/ summaries from rocprofv3 output and exit")
+    ap.add_argument("--summarize-sq", metavar="SQ_DIR",
+                    help="write the SQ-counter summary from a rocprofv3 --pmc run and exit")
     ap.add_argument("--profile-command", default="", help="command line recorded in the summary")
     args = ap.parse_args()
     if args.summarize_profile:
         summarize_profile(*args.summarize_profile, command=args.profile_command)
+        return
+    if args.summarize_sq:
+        summarize_sq(args.summarize_sq, command=args.profile_command)
         return
     if args.gpus != 1:
         print(json.dumps({"error": "runs on one GPU only: --gpus above 1 is not supported "
@@ -448,19 +750,25 @@ def main():
     lutq.load_library()
     if not torch.cuda.is_available():
         raise SystemExit("bench.py needs a GPU")
+    if args.profile_set:
+        profile_set(lutq, torch, args)
+        return
+    inputs = Inputs(lutq, torch)
 
     # ---- headline: batch-1 4-bit g128 GEMV, cold weights ------------------
-    head = Case(lutq, torch, "int4_up_proj", None, 1, cold=True)
+    head = inputs.get("int4_up_proj", None, 1)
     hplan = lutq.plan(1, head.N, head.K, 4)
     log(f"[bench] headline: {len(head.packed)} rotating copies, plan={hplan}")
-    region_us = time_case(lutq, torch, head, args.steps, args.warmup)
+    head_times = time_replays(lutq, torch, head, args.steps, args.warmup, repeats=HEADLINE_REPEATS)
+    region_us = sorted(head_times)[len(head_times) // 2]
     w_region_us = None
     if not args.no_warm:
         warm = Case.__new__(Case)
         warm.__dict__.update(head.__dict__)
         warm.packed = head.packed[:1]
-        w_region_us = time_case(lutq, torch, warm, args.steps, args.warmup)
-    log(f"[bench] headline cold: {region_us:.2f} us/call; warm: {w_region_us} us/call")
+        w_region_us = time_case(lutq, torch, warm, args.steps, args.warmup, repeats=EXTRA_REPEATS)
+    log(f"[bench] headline cold: {region_us:.3f} us/call (replays {[round(t, 3) for t in head_times]}); "
+        f"warm: {w_region_us} us/call")
 
     value = head.bytes / (region_us * 1e-6) / 1e9
     achieved = value
@@ -468,6 +776,8 @@ def main():
 
     extra = {
         "us_per_call": round(region_us, 3),
+        "replays_us": [round(t, 3) for t in head_times],
+        "spread_us": [round(min(head_times), 3), round(max(head_times), 3)],
         "bits_read_per_weight": round(head.bytes * 8 / (head.N * head.K), 4),
         "warm": None if w_region_us is None else {
             "us_per_call": round(w_region_us, 3),
@@ -476,51 +786,78 @@ def main():
     }
 
     # ---- batch 32: log table, Llama-70B up-projection shape ---------------
+    k_us = None
     if not args.no_batch32:
-        b32 = Case(lutq, torch, "log4_70b", None, 32, cold=True)
+        b32 = inputs.get("log4_70b", None, 32)
         p32 = lutq.plan(32, b32.N, b32.K, 4)
-        k_us = time_case(lutq, torch, b32, max(20, args.steps // 4), args.warmup, repeats=EXTRA_REPEATS)
+        k_us = time_case(lutq, torch, b32, max(20, args.steps // 4), args.warmup, repeats=5)
         wk_us = None
         if not args.no_warm:
             warm32 = Case.__new__(Case)
             warm32.__dict__.update(b32.__dict__)
             warm32.packed = b32.packed[:1]
-            wk_us = time_case(lutq, torch, warm32, max(20, args.steps // 4), args.warmup, repeats=EXTRA_REPEATS)
+            wk_us = time_case(lutq, torch, warm32, max(20, args.steps // 4), args.warmup,
+                              repeats=EXTRA_REPEATS)
             del warm32
         tf = b32.flops / (k_us * 1e-6) / 1e12
+        gbps = b32.bytes / (k_us * 1e-6) / 1e9
         extra["batch32"] = {
             "workload": "log4_70b", "N": b32.N, "K": b32.K, "M": 32, "plan": p32,
             "us_per_call": round(k_us, 3),
             "TFLOPs": round(tf, 1), "mfma_frac": round(tf / MFMA_F16_PEAK_TFLOPS, 4),
-            "effective_GBps": round(b32.bytes / (k_us * 1e-6) / 1e9, 1),
+            "effective_GBps": round(gbps, 1), "hbm_frac": round(gbps / HBM_PEAK_GBS, 4),
+            "bytes": b32.bytes, "flops": b32.flops,
+            "bound": "hbm (cold: arithmetic intensity below the machine balance)",
+            "frac_of_roof": round(roof_time_us(b32.bytes, b32.flops, HBM_PEAK_GBS,
+                                               MFMA_F16_PEAK_TFLOPS) / k_us, 4),
             "warm": None if wk_us is None else {
                 "us_per_call": round(wk_us, 3),
                 "TFLOPs": round(b32.flops / (wk_us * 1e-6) / 1e12, 1),
                 "mfma_frac": round(b32.flops / (wk_us * 1e-6) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4)},
         }
         log(f"[bench] batch32 cold {k_us:.2f} us = {tf:.1f} TFLOP/s; warm {wk_us} us")
-        del b32
-        torch.cuda.empty_cache()
 
+    if not args.no_configs:
+        extra["configs"], extra["layer_totals"] = configs_section(lutq, torch, args, inputs)
+    if not args.no_fused:
+        extra["fused"] = fused_section(lutq, torch, args, inputs)
     if not args.no_quantizer:
         extra["quantizer"] = quantizer_section(lutq, torch, args)
-    if not args.no_fused:
-        extra["fused"] = fused_section(lutq, torch, args)
     if not args.no_variants:
         extra["variants"] = variant_section(lutq, torch, args)
     if not args.no_dense:
         extra["dense_fp16"] = dense_section(
-            torch, args, {"int4_up_proj_M1": region_us,
-                          "log4_70b_M32": None if args.no_batch32 else k_us})
+            torch, args, {"int4_up_proj_M1": region_us, "log4_70b_M32": k_us})
 
     if args.sweep:
         extra["sweep"] = sweep(lutq, torch, args)
 
+    # The measured floors last: the MFMA microbenchmark runs the matrix pipes
+    # flat out, and nothing timed above should run right after it.
+    floor = None
+    if not args.no_peaks:
+        extra["peaks"], floor = peaks_section(lutq, torch, args)
+        mfma_meas = extra["peaks"]["mfma_best_TFLOPs"]
+        stream_us = floor(head.bytes)
+        extra["peaks"]["headline"] = {
+            "stream_with_store_us_at_headline_bytes": round(stream_us, 3),
+            "frac_of_measured": round(stream_us / region_us, 4)}
+        add_measured_roofs(extra, floor, mfma_meas)
+
     if args.copy_calibration:
         copy_calibration(torch)
 
-    cpu = None if args.no_cpu_baseline else cpu_baseline(head)
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(head, budget_s=10.0)
+        if not args.no_configs:
+            extra["cpu_oracle"] = cpu_oracle_section(inputs)
 
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic}
+    if floor is not None:
+        roofline["measured_peak"] = round(head.bytes / (floor(head.bytes) * 1e3), 1)
+        roofline["frac_of_measured"] = round(achieved / roofline["measured_peak"], 4)
     out = {
         "metric": "batch-1 4-bit g128 GEMV us + effective GB/s (% HBM peak); batch-32 TFLOP/s",
         "value": round(value, 1),
@@ -536,9 +873,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": "int4_up_proj", "N": head.N, "K": head.K, "M": 1, "bits": 4,
                    "group": 128, "table": "int", "weights": f"cold, {len(head.packed)} rotating copies"},
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic},
+        "roofline": roofline,
         "cpu_baseline": cpu,
         "extra": extra,
     }
@@ -598,10 +933,63 @@ def copy_calibration(torch):
     torch.cuda.synchronize()
 
 
-# template arguments: bits, MFMA, batch rows, grouped, zero points, data types,
-# binary coding, bf16, prefetch depth, tiles per wave, waves, occupancy
-HEADLINE_KERNEL = "matmul_kernel<4, false, 1, true, false, false, false, false, 2, 2, 8, 4, false>"
-BATCH32_KERNEL = "matmul_kernel<4, true, 32, false, false, false, false, false, 2, 7, 4, 2, false>"
+# The cases of the committed rocprofv3 summaries (label, workload, matrix, M):
+# the headline GEMV, the batch-32 MFMA kernel, the 3-bit GEMV and 3-bit MFMA
+# kernels (the non-evenly-divisible width), and a batch-16 MFMA launch. Each
+# runs a distinct kernel instantiation, so kernel names identify the cases.
+PROFILE_CASES = (
+    ("int4_up_proj", "int4_up_proj", "up", 1),
+    ("log4_70b_batch32", "log4_70b", "up", 32),
+    ("lm3_wide_M1", "lm3", "wide", 1),
+    ("lm3_wide_M8", "lm3", "wide", 8),
+    ("nf4_gate_M16", "nf4_layer", "gate", 16),
+)
+
+
+def kernel_signature(bits, group, M, plan):
+    """The matmul_kernel instantiation lutq_matmul launches for this plan (the
+    launch rules of lutq_matmul.hip for plain tables and fp16 activations):
+    template arguments bits, MFMA, batch rows, grouped, zero points, data
+    types, binary coding, bf16, prefetch depth, tiles per wave, waves,
+    occupancy, staged activations."""
+    tiles, grouped = plan["tiles"], group > 0
+    if plan["path"] == "gemv":
+        mrows = 1 if M <= 1 else 2 if M <= 2 else 4 if M <= 4 else 8
+        occ = 4 if mrows <= 2 else 2
+        pf = 4 if (mrows == 1 and tiles == 1) else 2
+        waves, xs = 8, False
+        mfma = False
+    else:
+        mfma, pf = True, 2
+        mrows = 16 if M <= 16 else 32
+        if tiles in (7, 8):
+            waves, occ, xs = 4, 2, False
+            if grouped and mrows == 32:
+                occ = 1
+        elif tiles == 4:
+            waves, occ, xs = (8, 2, True) if mrows == 32 else (4, 2, False)
+        else:
+            waves, occ, xs = (8, 2, mrows == 32 or M > 8)
+    b = lambda v: "true" if v else "false"
+    return (f"matmul_kernel<{bits}, {b(mfma)}, {mrows}, {b(grouped)}, false, false, false, false, "
+            f"{pf}, {tiles}, {waves}, {occ}, {b(xs)}>")
+
+
+def profile_set(lutq, torch, args):
+    """The profiled workload: each case of PROFILE_CASES timed as in the
+    benchmark (cold weights, graph replays), the quantizer section, then the
+    256 MiB copy that calibrates the memory counters."""
+    inputs = Inputs(lutq, torch)
+    for label, wname, mat, M in PROFILE_CASES:
+        case = inputs.get(wname, mat, M)
+        us = time_case(lutq, torch, case, args.steps, args.warmup, repeats=EXTRA_REPEATS)
+        log(f"[profile-set] {label}: {us:.3f} us per call")
+        del inputs.cases[(wname, mat)], case
+        torch.cuda.empty_cache()
+    quantizer_section(lutq, torch, args)
+    copy_calibration(torch)
+    torch.cuda.synchronize()
+    print(json.dumps({"profile_set": [c[0] for c in PROFILE_CASES]}), flush=True)
 
 
 def _read_csv(path):
@@ -630,13 +1018,13 @@ def _counter_per_dispatch(dirpath, counter, name_part):
 def summarize_profile(kt_dir, fetch_dir, write_dir, command=""):
     """profiles/*: kernel durations (rocprofv3 --kernel-trace --stats) and HBM
     traffic per launch (FETCH_SIZE, WRITE_SIZE in KiB, scaled by what the same
-    counters read for the COPY_BYTES copy)."""
+    counters read for the COPY_BYTES copy) of the PROFILE_CASES kernels, one
+    summary per kernel and workload, plus the counters json."""
     from weight_only_lut_amd.build import source_digest
     stats = _read_csv(_find(kt_dir, "kernel_stats.csv"))
-    rows = [r for r in stats if "lutq::" in r["Name"] or "copy" in r["Name"].lower()]
     copy_name = "neg_kernel"
-    f_copy, n1 = _counter_per_dispatch(fetch_dir, "FETCH_SIZE", copy_name)
-    w_copy, n2 = _counter_per_dispatch(write_dir, "WRITE_SIZE", copy_name)
+    f_copy, _ = _counter_per_dispatch(fetch_dir, "FETCH_SIZE", copy_name)
+    w_copy, _ = _counter_per_dispatch(write_dir, "WRITE_SIZE", copy_name)
     f_scale = COPY_BYTES / (f_copy * 1024) if f_copy else None
     w_scale = COPY_BYTES / (w_copy * 1024) if w_copy else None
     out = {"source_digest": source_digest(), "copy_bytes": COPY_BYTES,
@@ -644,42 +1032,107 @@ def summarize_profile(kt_dir, fetch_dir, write_dir, command=""):
     import weight_only_lut_amd as lutq
     from synth import workloads
     lutq.load_library()
-    for label, part, wname, M in (("int4_up_proj", HEADLINE_KERNEL, "int4_up_proj", 1),
-                                  ("log4_70b_batch32", BATCH32_KERNEL, "log4_70b", 32)):
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    for label, wname, mat, M in PROFILE_CASES:
+        wl = workloads.WORKLOADS[wname]
+        _, m = wl.matrix(mat)
+        plan = lutq.plan(M, m.N, m.K, wl.bits)
+        part = kernel_signature(wl.bits, wl.group, M, plan)
         f, nf = _counter_per_dispatch(fetch_dir, "FETCH_SIZE", part)
         w, nw = _counter_per_dispatch(write_dir, "WRITE_SIZE", part)
         dur = [r for r in stats if part in r["Name"]]
-        wl = workloads.WORKLOADS[wname]
-        mat = wl.matrices[0]
-        rec = {"kernel": part, "fetch_kib_raw": f, "write_kib_raw": w, "dispatches": [nf, nw],
-               "avg_duration_us": float(dur[0]["AverageNs"]) / 1e3 if dur else None,
-               "plan": lutq.plan(M, mat.N, mat.K, wl.bits)}
+        nbytes = algorithmic_bytes(M, m.N, m.K, wl.bits, wl.group)
+        flops = 2 * M * m.N * m.K
+        avg = float(dur[0]["AverageNs"]) / 1e3 if dur else None
+        rec = {"kernel": part, "workload": wname, "matrix": mat, "N": m.N, "K": m.K, "M": M,
+               "fetch_kib_raw": f, "write_kib_raw": w, "dispatches": [nf, nw],
+               "calls": int(dur[0]["Calls"]) if dur else 0, "avg_duration_us": avg,
+               "min_duration_us": float(dur[0]["MinNs"]) / 1e3 if dur else None,
+               "max_duration_us": float(dur[0]["MaxNs"]) / 1e3 if dur else None,
+               "plan": plan, "algorithmic_bytes": nbytes, "flops": flops}
+        if avg:
+            rec["achieved_GBps"] = round(nbytes / (avg * 1e3), 1)
+            rec["achieved_TFLOPs"] = round(flops / (avg * 1e6), 2)
+            rec["frac_of_roof"] = round(roof_time_us(nbytes, flops, HBM_PEAK_GBS,
+                                                     MFMA_F16_PEAK_TFLOPS) / avg, 4)
         if f is not None and w is not None and f_scale and w_scale:
             rec["traffic_bytes_per_launch"] = round(f * 1024 * f_scale + w * 1024 * w_scale)
+            rec["traffic_over_algorithmic"] = round(rec["traffic_bytes_per_launch"] / nbytes, 4)
         out["kernels"][label] = rec
-    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+        lines = [f"# `{part}` on `{wname}` {mat} (N = {m.N}, K = {m.K}), batch {M}: rocprofv3 summary", "",
+                 f"Source digest of the matmul kernel sources: `{out['source_digest']}`; plan {plan}.", "",
+                 "Command (cold weights, rotating copies; `<repo>` is the repository root):", "", "```",
+                 command or "(not recorded)", "```", "",
+                 "| quantity | value |", "|---|---|",
+                 f"| calls traced | {rec['calls']} |",
+                 f"| average duration (kernel trace) | {avg if avg is None else round(avg, 3)} us |",
+                 f"| min / max duration | {rec['min_duration_us']} / {rec['max_duration_us']} us |",
+                 f"| algorithmic bytes per launch | {nbytes:,} |",
+                 f"| achieved (algorithmic bytes / average duration) | {rec.get('achieved_GBps')} GB/s, "
+                 f"{rec.get('achieved_TFLOPs')} TFLOP/s |",
+                 f"| fraction of the bounding roof (8 TB/s, 2.5 PFLOP/s) | {rec.get('frac_of_roof')} |",
+                 f"| FETCH_SIZE / WRITE_SIZE per dispatch (raw KiB, median) | {f} / {w} |",
+                 f"| HBM traffic per launch (scaled) | {rec.get('traffic_bytes_per_launch')} bytes "
+                 f"({rec.get('traffic_over_algorithmic')} of algorithmic) |", "",
+                 f"Counter calibration: a {COPY_BYTES >> 20} MiB device copy reads FETCH_SIZE = {f_copy} "
+                 f"KiB and WRITE_SIZE = {w_copy} KiB per dispatch; scale factors {f_scale} (fetch) and "
+                 f"{w_scale} (write) turn counter KiB into bytes."]
+        with open(os.path.join(ROOT, "profiles", f"matmul_kernel_{label}.md"), "w") as fh:
+            fh.write("\n".join(lines) + "\n")
     with open(os.path.join(ROOT, "profiles", "matmul_kernel_counters.json"), "w") as fh:
         json.dump(out, fh, indent=1)
-    lines = ["# lutq matmul kernels: rocprofv3 summary", "",
-             f"Source digest of weight_only_lut_amd/csrc: `{out['source_digest']}`", "",
-             "Command:", "", "```", command or "(not recorded)", "```", "",
-             "## Kernel durations (rocprofv3 --kernel-trace --stats)", "",
-             "| kernel | calls | average us | min us | max us |", "|---|---|---|---|---|"]
-    for r in rows:
-        lines.append(f"| `{r['Name'][:110]}` | {r['Calls']} | {float(r['AverageNs'])/1e3:.3f} | "
-                     f"{float(r['MinNs'])/1e3:.3f} | {float(r['MaxNs'])/1e3:.3f} |")
-    lines += ["", "## HBM traffic per launch (rocprofv3 --pmc FETCH_SIZE, then WRITE_SIZE)", "",
-              f"Calibration: a {COPY_BYTES >> 20} MiB device copy reads FETCH_SIZE = {f_copy} KiB and "
-              f"WRITE_SIZE = {w_copy} KiB per dispatch; scale factors {f_scale} (fetch) and "
-              f"{w_scale} (write) turn counter KiB into bytes.", "",
-              "| workload | raw FETCH KiB | raw WRITE KiB | scaled bytes / launch |", "|---|---|---|---|"]
-    for label, rec in out["kernels"].items():
-        lines.append(f"| {label} | {rec['fetch_kib_raw']} | {rec['write_kib_raw']} | "
-                     f"{rec.get('traffic_bytes_per_launch')} |")
-    with open(os.path.join(ROOT, "profiles", "matmul_kernel_int4_up_proj_log4_70b.md"), "w") as fh:
-        fh.write("\n".join(lines) + "\n")
     print(json.dumps(out, indent=1))
-    summarize_quantizer(stats, fetch_dir, write_dir, f_copy, w_copy, f_scale, w_scale, command)
+    if any("quant_kernel" in r["Name"] for r in stats):
+        summarize_quantizer(stats, fetch_dir, write_dir, f_copy, w_copy, f_scale, w_scale, command)
+
+
+SQ_COUNTERS = ("SQ_WAVES", "SQ_BUSY_CU_CYCLES", "SQ_WAVE_CYCLES", "SQ_WAIT_INST_ANY", "SQ_INSTS_LDS",
+               "SQ_LDS_BANK_CONFLICT", "SQ_INSTS_MFMA", "SQ_VALU_MFMA_BUSY_CYCLES")
+
+
+def summarize_sq(sq_dir, command=""):
+    """profiles/matmul_kernel_sq_counters.md: the SQ counters of the
+    PROFILE_CASES kernels (median per dispatch)."""
+    import weight_only_lut_amd as lutq
+    from synth import workloads
+    from weight_only_lut_amd.build import source_digest
+    lutq.load_library()
+    cols = []
+    for label, wname, mat, M in PROFILE_CASES:
+        wl = workloads.WORKLOADS[wname]
+        _, m = wl.matrix(mat)
+        part = kernel_signature(wl.bits, wl.group, M, lutq.plan(M, m.N, m.K, wl.bits))
+        vals = {c: _counter_per_dispatch(sq_dir, c, part) for c in SQ_COUNTERS}
+        cols.append((label, part, vals))
+    lines = ["# lutq matmul kernels: SQ counters (rocprofv3 --pmc)", "",
+             f"Source digest of the matmul kernel sources: `{source_digest()}`. Medians per dispatch "
+             "over the run; kernels as in the per-case summaries `matmul_kernel_<case>.md`.", "",
+             "Command (`<repo>` is the repository root):", "", "```", command or "(not recorded)", "```", "",
+             "| counter | " + " | ".join(f"`{c[0]}`" for c in cols) + " |",
+             "|---|" + "---|" * len(cols)]
+    for cname in SQ_COUNTERS:
+        row = []
+        for _, _, vals in cols:
+            v, n = vals[cname]
+            if v is None:
+                row.append("-")
+                continue
+            cell = f"{v:,.0f}"
+            waves, wave_cycles, busy = (vals["SQ_WAVES"][0], vals["SQ_WAVE_CYCLES"][0],
+                                        vals["SQ_BUSY_CU_CYCLES"][0])
+            if cname == "SQ_WAIT_INST_ANY" and wave_cycles:
+                cell += f" ({v / wave_cycles:.0%} of wave cycles)"
+            elif cname in ("SQ_INSTS_LDS", "SQ_INSTS_MFMA") and waves:
+                cell += f" ({v / waves:,.1f} per wave)"
+            elif cname == "SQ_LDS_BANK_CONFLICT" and vals["SQ_INSTS_LDS"][0]:
+                cell += f" ({v / vals['SQ_INSTS_LDS'][0]:.2f} per LDS instruction)"
+            elif cname == "SQ_VALU_MFMA_BUSY_CYCLES" and busy:
+                cell += f" ({v / (4 * busy):.1%} of the SIMDs' busy cycles)"
+            row.append(cell)
+        lines.append(f"| {cname} | " + " | ".join(row) + " |")
+    lines += ["", "Kernels:", ""] + [f"- `{c[0]}`: `{c[1]}`" for c in cols]
+    with open(os.path.join(ROOT, "profiles", "matmul_kernel_sq_counters.md"), "w") as fh:
+        fh.write("\n".join(lines) + "\n")
 
 
 # The quantizer's kernels on the 14336 x 4096 matrix of fp32 weights, as the

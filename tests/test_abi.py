@@ -15,7 +15,8 @@ from weight_only_lut_amd import _lib
 from . import layout_spec
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "lutq.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in sorted(os.listdir(os.path.join(ROOT, "include")))
+           if h.endswith(".h")]
 
 OK, EINVAL, EBITS, EGROUP, EALIGN, EMISMATCH, ESIZE, EHIP, EUNSUP, ECAPTURE = 0, -1, -2, -3, -4, -5, -6, -7, -8, -9
 
@@ -26,9 +27,12 @@ def lib():
 
 
 def _declared():
-    src = open(HEADER).read()
-    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(lutq_[a-z_]+)\s*\(", src)))
+    """Every function any header in include/ declares."""
+    names = set()
+    for h in HEADERS:
+        src = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"\b(lutq_[a-z_]+)\s*\(", src))
+    return sorted(names)
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -109,6 +113,23 @@ def test_binding_checks_every_tensor_before_calling():
         lutq.quantize(w.view(-1), lut, 4, 128)
     with pytest.raises(TypeError):
         lutq.quantize(w, lut, 4, 128)
+
+
+def test_peaks_validate_before_launching(lib):
+    P = ctypes.c_void_p
+    assert lib.lutq_peak_stream_sink_bytes() == 2048 * 4 * 16
+    assert lib.lutq_peak_stream(P(0), 1024, 0, P(0x1000), None) == EINVAL
+    assert lib.lutq_peak_stream(P(0x1000), 0, 0, P(0x1000), None) == EINVAL
+    assert lib.lutq_peak_stream(P(0x1000), 1000, 0, P(0x1000), None) == EINVAL   # not 16-byte units
+    assert lib.lutq_peak_stream(P(0x1008), 1024, 1, P(0x1000), None) == EALIGN
+    assert lib.lutq_peak_stream(P(0x1000), 1024, 1, P(0), None) == EINVAL
+    assert lib.lutq_peak_mfma(2, 1, 10, P(0x1000), None) == EINVAL              # unknown kind
+    assert lib.lutq_peak_mfma(0, 5, 10, P(0x1000), None) == EINVAL              # waves per SIMD
+    assert lib.lutq_peak_mfma(0, 1, 0, P(0x1000), None) == EINVAL
+    assert lib.lutq_peak_mfma(0, 1, 10, P(0), None) == EINVAL
+    assert lib.lutq_peak_lds(17, 10, P(0x1000), None) == EINVAL
+    assert lib.lutq_peak_lds(4, 0, P(0x1000), None) == EINVAL
+    assert lib.lutq_peak_lds(4, 10, P(0), None) == EINVAL
 
 
 def test_packed_bytes():

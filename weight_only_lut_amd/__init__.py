@@ -25,6 +25,14 @@ from ._lib import (  # noqa: F401
     matmul_multi,
     matmul_noalloc,
     packed_bytes,
+    peak_empty,
+    peak_lds,
+    peak_mfma,
+    peak_stream,
+    peak_stream_sink_bytes,
+    PEAK_MFMA_16X16X32,
+    PEAK_MFMA_32X32X16,
+    PEAK_MFMA_FLOPS_PER_ROUND,
     plan,
     quant_error,
     quantize,

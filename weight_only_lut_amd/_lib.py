@@ -25,6 +25,9 @@ EXPORTS = (
     "lutq_matmul_zp", "lutq_matmul_typed", "lutq_matmul_bcq",
     "lutq_quantize_ex", "lutq_quant_error_ex", "lutq_log_base_search_ex", "lutq_tune_table",
     "lutq_matmul_noalloc",
+    # include/lutq_peaks.h
+    "lutq_peak_empty", "lutq_peak_stream_sink_bytes", "lutq_peak_stream", "lutq_peak_mfma",
+    "lutq_peak_lds",
 )
 
 MAX_TYPES = 4
@@ -135,6 +138,16 @@ def load_library():
     lib.lutq_log_base_search.argtypes = [vp, i32, i32, i32, i32, ctypes.POINTER(ctypes.c_double), i32,
                                          ctypes.POINTER(i32), ctypes.POINTER(ctypes.c_double), vp]
     lib.lutq_log_base_search.restype = i32
+    lib.lutq_peak_empty.argtypes = [vp]
+    lib.lutq_peak_empty.restype = i32
+    lib.lutq_peak_stream_sink_bytes.argtypes = []
+    lib.lutq_peak_stream_sink_bytes.restype = sz
+    lib.lutq_peak_stream.argtypes = [vp, sz, i32, vp, vp]
+    lib.lutq_peak_stream.restype = i32
+    lib.lutq_peak_mfma.argtypes = [i32, i32, i32, vp, vp]
+    lib.lutq_peak_mfma.restype = i32
+    lib.lutq_peak_lds.argtypes = [i32, i32, vp, vp]
+    lib.lutq_peak_lds.restype = i32
     _LIB = lib
     return lib
 
@@ -507,3 +520,54 @@ def tune_table(w, lut, bits: int, group: int, rule: str = "absmax", iters: int =
     if rc:
         raise LutqError(rc, "lutq_tune_table")
     return T, scales, list(errs)[: upd.value + 1]
+
+
+# ---- peak microbenchmarks (include/lutq_peaks.h) ------------------------------
+
+PEAK_MFMA_16X16X32, PEAK_MFMA_32X32X16 = 0, 1
+PEAK_MFMA_FLOPS_PER_ROUND = 131072   # per wave and round, either kind
+
+
+def _peak_rc(rc, where):
+    if rc:
+        raise LutqError(rc, where)
+
+
+def peak_empty():
+    """lutq_peak_empty on the current stream."""
+    import torch
+    _peak_rc(_lib().lutq_peak_empty(_stream(torch.cuda.current_device())), "lutq_peak_empty")
+
+
+def peak_stream_sink_bytes() -> int:
+    return int(_lib().lutq_peak_stream_sink_bytes())
+
+
+def peak_stream(buf, nbytes: int, store: bool, sink):
+    """lutq_peak_stream: read ``nbytes`` of the uint8 device tensor ``buf``."""
+    import torch
+    _check(buf, "buf", torch.uint8)
+    _check(sink, "sink", torch.uint8)
+    _on_device(("buf", buf), ("sink", sink))
+    if nbytes > buf.numel() or sink.numel() < peak_stream_sink_bytes():
+        raise ValueError("buffer or sink too small")
+    _peak_rc(_lib().lutq_peak_stream(_ptr(buf), nbytes, int(bool(store)), _ptr(sink),
+                                     _stream(buf.device)), "lutq_peak_stream")
+
+
+def peak_mfma(kind: int, waves_per_simd: int, iters: int, sink):
+    """lutq_peak_mfma: ``sink`` fp32, at least CUs * 16 entries."""
+    import torch
+    _check(sink, "sink", torch.float32)
+    _on_device(("sink", sink))
+    _peak_rc(_lib().lutq_peak_mfma(kind, waves_per_simd, iters, _ptr(sink), _stream(sink.device)),
+             "lutq_peak_mfma")
+
+
+def peak_lds(waves_per_cu: int, iters: int, sink):
+    """lutq_peak_lds: ``sink`` int32 (one entry used)."""
+    import torch
+    _check(sink, "sink", torch.int32)
+    _on_device(("sink", sink))
+    _peak_rc(_lib().lutq_peak_lds(waves_per_cu, iters, _ptr(sink), _stream(sink.device)),
+             "lutq_peak_lds")

@@ -16,7 +16,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 # (source, extra flags): the matmul is compiled once per code width
 SOURCES = [("lutq_api.cpp", []), ("lutq_layout.hip", []), ("lutq_quantize.hip", []),
-           ("lutq_static.hip", []),
+           ("lutq_static.hip", []), ("lutq_peaks.hip", []),
            ("lutq_matmul.hip", ["-DLUTQ_MATMUL_BITS=2"]), ("lutq_matmul.hip", ["-DLUTQ_MATMUL_BITS=3"]),
            ("lutq_matmul.hip", ["-DLUTQ_MATMUL_BITS=4"])]
 LIB = os.path.join(HERE, "liblutq.so")
