@@ -50,12 +50,13 @@ int lutq_peak_stream(const void* buf, size_t bytes, int store, uint32_t* sink, v
 enum { LUTQ_PEAK_MFMA_16X16X32 = 0, LUTQ_PEAK_MFMA_32X32X16 = 1 };
 int lutq_peak_mfma(int kind, int waves_per_simd, int iters, float* sink, void* stream);
 
-/* Random 32-bit reads from a 64 KiB LDS table in the access pattern of the
- * lutq pair table (256 entries of 64 copies; lane L reads copy L of a random
- * entry, so an instruction's 64 lanes hit 64 distinct banks): one workgroup
- * of waves_per_cu waves (1..16) per compute unit; each lane reads 16 * iters
- * entries of its own xorshift sequence, 16 in flight at a time. Wave-wide
- * ds_read_b32 instructions per launch = CUs * waves_per_cu * 16 * iters.
+/* 32-bit LDS reads in the access pattern of the lutq pair table (256
+ * entries of 64 copies, 64 KiB; lane L reads copy L of its entry, so an
+ * instruction's 64 lanes hit 64 distinct banks): one workgroup of
+ * waves_per_cu waves (1..16) per compute unit; each lane holds 16 random
+ * entries and reads them all every round, one ds_read_b32 each (16 in
+ * flight), `iters` rounds. Wave-wide ds_read_b32 instructions per launch =
+ * CUs * waves_per_cu * 16 * iters.
  * `sink`: device, one uint32. Errors: LUTQ_EINVAL, LUTQ_EHIP. */
 int lutq_peak_lds(int waves_per_cu, int iters, uint32_t* sink, void* stream);
 

@@ -75,28 +75,38 @@ __global__ void peak_mfma_kernel(float* __restrict__ sink, int iters) {
 
 // Random 32-bit LDS reads in the access pattern of the duplicated pair
 // table: 256 entries of 64 copies (64 KiB), entry (idx, copy) at byte
-// (idx << 8) | (copy << 2); each lane draws entries from its own xorshift
-// sequence and always reads its own copy (lane L, copy L), so the 64 lanes
-// of an instruction hit 64 distinct banks. 16 reads per round are in flight
-// before they are combined.
+// (idx << 8) | (copy << 2), lane L always reading its own copy (so the 64
+// lanes of an instruction hit 64 distinct banks). Each lane holds 16 random
+// entries, one address register each, and reads all 16 every round (LDS has
+// no cache, so repeating them costs what new ones would). An empty asm
+// statement marks the address registers as changed every round, so the
+// compiler reissues each read as its own ds_read_b32 (different base
+// registers cannot merge into a two-address read); the values are summed
+// three at a time.
 __global__ void peak_lds_kernel(uint32_t* __restrict__ sink, int iters) {
   __shared__ uint32_t table[16384];
   for (int i = threadIdx.x; i < 16384; i += blockDim.x) table[i] = (uint32_t)i * 2654435761u;
   __syncthreads();
-  const uint32_t copy = threadIdx.x & 63u;
-  uint32_t st = (uint32_t)(blockIdx.x * blockDim.x + threadIdx.x) * 0x9E3779B9u + 1u;
+  const uint32_t lane = threadIdx.x & 63u;
+  uint32_t h = (uint32_t)(blockIdx.x * blockDim.x + threadIdx.x) * 0x9E3779B9u + 1u;
+  uint32_t addr[16];
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    h ^= h << 13;
+    h ^= h >> 17;
+    h ^= h << 5;
+    addr[k] = ((h & 255u) << 8) | (lane << 2);  // byte address of (entry, own copy)
+  }
   uint32_t acc = 0;
   for (int it = 0; it < iters; ++it) {
     uint32_t v[16];
 #pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      st ^= st << 13;
-      st ^= st >> 17;
-      st ^= st << 5;
-      v[k] = table[((st & 255u) << 6) | copy];
-    }
+    for (int k = 0; k < 16; ++k) asm volatile("" : "+v"(addr[k]));  // no instruction
 #pragma unroll
-    for (int k = 0; k < 16; ++k) acc += v[k];
+    for (int k = 0; k < 16; ++k)
+      v[k] = *reinterpret_cast<const uint32_t*>(reinterpret_cast<const char*>(table) + addr[k]);
+#pragma unroll
+    for (int k = 0; k < 16; k += 2) acc = acc + v[k] + v[k + 1];
   }
   if (acc == 0x9E3779B9u) sink[0] = acc;  // practically never; keeps the reads
 }
