@@ -20,7 +20,15 @@ SOURCES = [("lutq_api.cpp", []), ("lutq_layout.hip", []), ("lutq_quantize.hip", 
            ("lutq_matmul.hip", ["-DLUTQ_MATMUL_BITS=2"]), ("lutq_matmul.hip", ["-DLUTQ_MATMUL_BITS=3"]),
            ("lutq_matmul.hip", ["-DLUTQ_MATMUL_BITS=4"])]
 LIB = os.path.join(HERE, "liblutq.so")
+# The same library with AddressSanitizer and UndefinedBehaviorSanitizer in
+# its host code only (argument validation, planning, scratch management);
+# device code is compiled exactly as in LIB. Loaded by the host-sanitizer
+# test in place of LIB, with the clang ASan runtime preloaded.
+SAN_LIB = os.path.join(HERE, "liblutq_san.so")
 ARCH = "gfx950"
+# each -fsanitize= applies to the host pass only (-Xarch_host right before it)
+SAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+             "-shared-libasan", "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-g"]
 
 FLAGS = [
     f"--offload-arch={ARCH}",
@@ -50,18 +58,22 @@ def _run(cmd, verbose):
     return res.returncode, msgs
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source to an object (in parallel), then link liblutq.so."""
+def build(verbose: bool = False, sanitized: bool = True) -> str:
+    """Compile every source to an object (in parallel), then link liblutq.so
+    and, with `sanitized`, liblutq_san.so (host code under ASan + UBSan)."""
     import tempfile
     from concurrent.futures import ThreadPoolExecutor
     cc = hipcc()
     inc = ["-I", os.path.join(ROOT, "include")]
+    variants = [(LIB, [])] + ([(SAN_LIB, SAN_FLAGS)] if sanitized else [])
     with tempfile.TemporaryDirectory(prefix="lutq_build_") as tmpdir:
-        jobs = []
-        for i, (src, extra) in enumerate(SOURCES):
-            obj = os.path.join(tmpdir, f"{i}_{os.path.splitext(src)[0]}.o")
-            cflags = [f for f in FLAGS if f != "-shared"]
-            jobs.append((obj, [cc, *cflags, *extra, *inc, "-c", "-o", obj, os.path.join(CSRC, src)]))
+        jobs, objs = [], {lib: [] for lib, _ in variants}
+        for v, (lib, vflags) in enumerate(variants):
+            for i, (src, extra) in enumerate(SOURCES):
+                obj = os.path.join(tmpdir, f"{v}_{i}_{os.path.splitext(src)[0]}.o")
+                cflags = [f for f in FLAGS if f != "-shared"] + vflags
+                jobs.append((obj, [cc, *cflags, *extra, *inc, "-c", "-o", obj, os.path.join(CSRC, src)]))
+                objs[lib].append(obj)
         workers = max(1, min(len(jobs), os.cpu_count() or 1, 8))
         with ThreadPoolExecutor(max_workers=workers) as ex:
             results = list(ex.map(lambda j: _run(j[1], verbose), jobs))
@@ -72,14 +84,28 @@ def build(verbose: bool = False) -> str:
             for rc, m in results:
                 if m:
                     print("\n".join(m))
-        tmp = LIB + f".tmp{os.getpid()}"
-        rc, msgs = _run([cc, *FLAGS, "-o", tmp, *[o for o, _ in jobs]], verbose)
-        if rc != 0:
-            if os.path.exists(tmp):
-                os.remove(tmp)
-            raise RuntimeError("hipcc link failed:\n" + "\n".join(msgs))
-    os.replace(tmp, LIB)
+        for lib, vflags in variants:
+            tmp = lib + f".tmp{os.getpid()}"
+            rc, msgs = _run([cc, *FLAGS, *vflags, "-o", tmp, *objs[lib]], verbose)
+            if rc != 0:
+                if os.path.exists(tmp):
+                    os.remove(tmp)
+                raise RuntimeError("hipcc link failed:\n" + "\n".join(msgs))
+            os.replace(tmp, lib)
     return LIB
+
+
+def asan_runtime() -> str | None:
+    """The clang AddressSanitizer runtime that liblutq_san.so links against."""
+    clang = os.path.join(os.path.dirname(os.path.realpath(hipcc())), "..", "llvm", "bin", "clang")
+    for cand in (clang, shutil.which("clang"), "/opt/rocm/llvm/bin/clang"):
+        if not cand or not os.path.exists(cand):
+            continue
+        res = subprocess.run([cand, "-print-resource-dir"], capture_output=True, text=True)
+        path = os.path.join(res.stdout.strip(), "lib", "linux", "libclang_rt.asan-x86_64.so")
+        if res.returncode == 0 and os.path.exists(path):
+            return path
+    return None
 
 
 # Sources of the matmul device code: a stored kernel profile is current while
