@@ -897,7 +897,7 @@ def sweep(lutq, torch, args):
                 case.y = torch.empty((M, base.N), dtype=torch.float16, device="cuda")
                 case.bytes = algorithmic_bytes(M, base.N, base.K, w.bits, w.group)
                 case.flops = 2 * M * base.N * base.K
-                shapes = [("auto", 0)] + [("mfma", t) for t in (2, 4, 7, 8)]
+                shapes = [("auto", 0)] + [("mfma", t) for t in (1, 2, 4, 7, 8)]
                 if M <= 8:
                     shapes += [("gemv", t) for t in (1, 2)]
                 for path, tiles in shapes:
@@ -935,14 +935,16 @@ def copy_calibration(torch):
 
 # The cases of the committed rocprofv3 summaries (label, workload, matrix, M):
 # the headline GEMV, the batch-32 MFMA kernel, the 3-bit GEMV and 3-bit MFMA
-# kernels (the non-evenly-divisible width), and a batch-16 MFMA launch. Each
-# runs a distinct kernel instantiation, so kernel names identify the cases.
+# kernels (the non-evenly-divisible width), and batch-16 MFMA launches of the
+# 4-tile and 1-tile shapes. Each runs a distinct kernel instantiation, so
+# kernel names identify the cases.
 PROFILE_CASES = (
     ("int4_up_proj", "int4_up_proj", "up", 1),
     ("log4_70b_batch32", "log4_70b", "up", 32),
     ("lm3_wide_M1", "lm3", "wide", 1),
     ("lm3_wide_M8", "lm3", "wide", 8),
     ("nf4_gate_M16", "nf4_layer", "gate", 16),
+    ("nf4_q_M16", "nf4_layer", "q", 16),
 )
 
 

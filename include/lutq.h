@@ -166,7 +166,7 @@ typedef struct lutq_options {
                      Clamped to the number of 128-code chunks.               */
   int32_t tiles;  /* 16-row output tiles per wave (the workgroup covers
                      16 * tiles rows); 0 = automatic. Needs an explicit
-                     path: GEMV takes 1 or 2, MFMA 2, 4, 7 or 8; anything
+                     path: GEMV takes 1 or 2, MFMA 1, 2, 4, 7 or 8; anything
                      else gives LUTQ_EINVAL.                                 */
   int32_t dtype;  /* activations x and output y: LUTQ_DTYPE_F16 (0) or
                      LUTQ_DTYPE_BF16 (1); bf16 works with plain tables

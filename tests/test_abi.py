@@ -223,7 +223,7 @@ def test_matmul_validates_before_launching(lib):
     d3 = _desc(bits=3)
     assert lib.lutq_matmul_bcq(x, ctypes.byref(d3), sc, y, 1, 64, 256, ctypes.byref(o),
                                None) == EUNSUP
-    for path, tiles in [(0, 2), (1, 8), (1, 4), (1, 7), (2, 1), (2, 3), (2, 6), (1, -1)]:
+    for path, tiles in [(0, 2), (1, 8), (1, 4), (1, 7), (2, 5), (2, 3), (2, 6), (1, -1)]:
         o = _lib.Options(); o.path, o.tiles = path, tiles
         assert call(opts=ctypes.byref(o)) == EINVAL, (path, tiles)
     # nothing to do: M == 0 (no HIP call is made)
@@ -334,8 +334,9 @@ def test_matmul_bcq_validates_before_launching(lib):
     assert call(desc=_desc(bits=3, group=0)) == EGROUP
     assert call(alphas=P(0)) == EINVAL
     assert call(alphas=P(0x3001)) == EALIGN
-    o = _lib.Options(); o.path, o.tiles = 2, 4
-    assert call(opts=ctypes.byref(o)) == EINVAL          # MFMA runs 2 tiles per wave
+    for tiles in (1, 4):
+        o = _lib.Options(); o.path, o.tiles = 2, tiles
+        assert call(opts=ctypes.byref(o)) == EINVAL      # MFMA runs 2 tiles per wave
     assert call(M=0) == OK
 
 
@@ -433,12 +434,20 @@ def test_plan_shapes_and_split():
     assert lutq.plan(1, 16, 1 << 20, 4)["ksplit"] == 256
     assert lutq.plan(1, 16, 16384, 4)["ksplit"] == 4
     assert lutq.plan(2, 4096, 14336, 3) == {"path": "gemv", "ksplit": 1, "tiles": 1}
-    # MFMA: split once the row blocks cover at most half the CUs, from 9
-    # batch rows or on a long K (1024 rows = 32 blocks of 32 -> 8;
-    # 4096 rows = 128 blocks -> 2)
-    assert lutq.plan(16, 1024, 4096, 4) == {"path": "mfma", "ksplit": 8, "tiles": 2}
-    assert lutq.plan(8, 1024, 4096, 4) == {"path": "mfma", "ksplit": 1, "tiles": 2}
+    # MFMA, at most one tile per CU on a short K (< 64 chunks): one tile per
+    # wave; K split only above 16 batch rows on at most a quarter of the
+    # CUs, until half of them are covered (1024 rows = 64 blocks -> 2)
+    assert lutq.plan(16, 1024, 4096, 4) == {"path": "mfma", "ksplit": 1, "tiles": 1}
+    assert lutq.plan(8, 1024, 4096, 4) == {"path": "mfma", "ksplit": 1, "tiles": 1}
+    assert lutq.plan(32, 1024, 4096, 4) == {"path": "mfma", "ksplit": 2, "tiles": 1}
+    assert lutq.plan(32, 4096, 4096, 4) == {"path": "mfma", "ksplit": 1, "tiles": 1}
+    assert lutq.plan(32, 256, 4096, 4) == {"path": "mfma", "ksplit": 8, "tiles": 1}
+    # 257 tiles (more than one per CU) keep two tiles per wave
+    assert lutq.plan(8, 4112, 4096, 4)["tiles"] == 2
+    # MFMA, 2 tiles: split once the row blocks cover at most half the CUs,
+    # from 9 batch rows or on a long K (4096 rows = 128 blocks -> 2)
     assert lutq.plan(4, 4096, 14336, 3) == {"path": "mfma", "ksplit": 2, "tiles": 2}
+    assert lutq.plan(16, 4096, 14336, 4) == {"path": "mfma", "ksplit": 2, "tiles": 2}
     assert lutq.plan(32, 14336, 4096, 4) == {"path": "mfma", "ksplit": 1, "tiles": 4}
     # explicit fields are kept (the split is clamped to the chunk count)
     assert lutq.plan(1, 14336, 4096, 4, path="mfma", tiles=8, ksplit=3) == \

@@ -89,7 +89,7 @@ def test_bcq_rejects_other_mfma_shapes(lutq):
     c, a = make(3, 64, 256, 128, 820)
     P = lutq.repack(dev(c), 3, 128)
     x = dev(draw.activations(4, 256, (821,)))
-    for tiles in (4, 8):
+    for tiles in (1, 4, 8):
         with pytest.raises(lutq.LutqError):
             lutq.matmul_bcq(x, P, dev(a), path="mfma", tiles=tiles)
 

@@ -121,7 +121,7 @@ def test_parity_random(lutq, bits, table, group, N, K, M, path):
     assert_close(y, x, c, T, s, group)
 
 
-SHAPES = [("gemv", 1), ("gemv", 2), ("mfma", 2), ("mfma", 4), ("mfma", 7), ("mfma", 8)]
+SHAPES = [("gemv", 1), ("gemv", 2), ("mfma", 1), ("mfma", 2), ("mfma", 4), ("mfma", 7), ("mfma", 8)]
 
 
 @pytest.mark.parametrize("path,tiles", SHAPES)

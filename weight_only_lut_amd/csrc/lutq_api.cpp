@@ -147,8 +147,9 @@ int read_options(const lutq_options_t* opts, lutq_options_t* o) {
 }
 
 // Fills the automatic fields of *o (checked by read_options) for an
-// M x N x K product (M, N, K > 0).
-void plan(int M, int N, int K, int cus, lutq_options_t* o) {
+// M x N x K product (M, N, K > 0). Binary-coded weights (bcq) take the
+// 2-tile MFMA shape.
+void plan(int M, int N, int K, int cus, lutq_options_t* o, bool bcq = false) {
   const int nchunks = K / lutq::kChunk;
   const int ntiles = (N + lutq::kTileRows - 1) / lutq::kTileRows;
   if (o->path == LUTQ_PATH_AUTO) {
@@ -162,7 +163,9 @@ void plan(int M, int N, int K, int cus, lutq_options_t* o) {
   const int kpath = kernel_path(o->path);
   if (o->tiles == 0) {
     const int rl = rows_per_launch(o->path);
-    o->tiles = lutq::pick_tiles(kpath, M < rl ? M : rl, ntiles, cus);
+    o->tiles = (bcq && o->path == LUTQ_PATH_MFMA)
+                   ? 2
+                   : lutq::pick_tiles(kpath, M < rl ? M : rl, ntiles, nchunks, cus);
   }
   const int nrb = (ntiles + o->tiles - 1) / o->tiles;
   if (o->ksplit == 0) {
@@ -170,11 +173,16 @@ void plan(int M, int N, int K, int cus, lutq_options_t* o) {
     // the last workgroup's reads) on the critical path: a few microseconds.
     // MFMA workgroups at more than 8 batch rows (or on a long K) carry
     // enough compute that splitting pays as soon as the row blocks cover at
-    // most half the CUs. GEMV workgroups are light: split only a long K
+    // most half the CUs. One-tile MFMA workgroups (a short K) are lighter:
+    // split only above 16 batch rows on at most a quarter of the CUs, until
+    // half of them are covered (1024 x 4096 at 32 rows: 7.78 us unsplit,
+    // 7.22 in 2, 7.41 in 4). GEMV workgroups are light: split only a long K
     // (each split keeping at least kSplitChunks chunks) on fewer row blocks
     // than CUs.
     int k = 1;
-    if (o->path == LUTQ_PATH_MFMA) {
+    if (o->path == LUTQ_PATH_MFMA && o->tiles == 1) {
+      if (M > 16 && 4 * nrb <= cus) k = cus / (2 * nrb);
+    } else if (o->path == LUTQ_PATH_MFMA) {
       if (2 * nrb <= cus && (M > 8 || nchunks >= kSplitMinChunks)) k = cus / nrb;
     } else if (nrb < cus && nchunks >= kSplitMinChunks) {
       k = cus / nrb;
@@ -235,8 +243,7 @@ int run_matmul(const uint16_t* x, const lutq_matmul_item_t* items, int count, in
   if (!x) return LUTQ_EINVAL;
   if (!aligned(x, 16)) return LUTQ_EALIGN;
 
-  plan(M, ntiles_all * lutq::kTileRows, K, cu_count(), &o);
-  if (bcq && o.path == LUTQ_PATH_MFMA) o.tiles = 2;
+  plan(M, ntiles_all * lutq::kTileRows, K, cu_count(), &o, bcq);
   const int path = kernel_path(o.path);
   const int ksplit = o.ksplit;
   const int rl = rows_per_launch(o.path);

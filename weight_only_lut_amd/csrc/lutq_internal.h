@@ -71,8 +71,8 @@ constexpr int kMfmaMaxRows = 32;
 // workgroups.
 bool tiles_supported(int path, int tiles);
 // The shape the automatic plan picks for a launch of `mrows` batch rows over
-// `ntiles` tiles on a device with `cus` compute units.
-int pick_tiles(int path, int mrows, int ntiles, int cus);
+// `ntiles` tiles and `nchunks` K chunks on a device with `cus` compute units.
+int pick_tiles(int path, int mrows, int ntiles, int nchunks, int cus);
 
 hipError_t launch_repack(const uint8_t* codes, uint8_t* dst, int N, int K, int bits,
                          hipStream_t s);

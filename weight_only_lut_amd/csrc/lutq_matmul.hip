@@ -707,14 +707,15 @@ void matmul_kernel(const MatmulParams pk) {
 
 // Kernel shapes. GEMV: 8 waves, each covering 1 or 2 tiles. MFMA: 8 or 7
 // tiles per wave with 4 waves (wide matrices: each activation fragment feeds
-// 8 or 7 tiles), 4 tiles with 4 waves (8 at 32 batch rows), or 2 tiles with
-// 8 waves (narrow matrices, which need many workgroups to fill the device).
+// 8 or 7 tiles), 4 tiles with 4 waves (8 at 32 batch rows), 2 tiles with 8
+// waves (narrow matrices, which need many workgroups to fill the device), or
+// 1 tile with 8 waves (at most one tile per CU on a short K).
 constexpr int kPf = 2;
 
 // Host-side shape rules: compiled once (in the width-4 object).
 #if LUTQ_MATMUL_BITS == 4
 bool tiles_supported(int path, int tiles) {
-  if (path == kPathMfma) return tiles == 2 || tiles == 4 || tiles == 7 || tiles == 8;
+  if (path == kPathMfma) return tiles == 1 || tiles == 2 || tiles == 4 || tiles == 7 || tiles == 8;
   return tiles == 1 || tiles == 2;
 }
 
@@ -724,12 +725,18 @@ bool tiles_supported(int path, int tiles) {
 // lookups, so the busiest CU sets the time: 7 tiles when that puts exactly
 // one workgroup on every CU (28672 rows: 8 tiles leave 32 of 256 CUs idle,
 // 4 tiles put two workgroups on 192 of them; 31.6 -> 27.4 us at 32 batch
-// rows, 26.6 -> 21.6 us at 16).
-int pick_tiles(int path, int mrows, int ntiles, int cus) {
+// rows, 26.6 -> 21.6 us at 16). At most one tile per CU on a short K (fewer
+// than 64 chunks): one tile per workgroup, which spreads the rows over the
+// most CUs without the round trips of a K split (4096 x 4096: 6.97 -> 6.38
+// us at 16 batch rows; 1024 x 4096: 6.87 -> 5.78 us). A long K keeps two
+// tiles and splits K instead (4096 x 14336 at 16 rows: 12.41 us against
+// 13.37 with one tile).
+int pick_tiles(int path, int mrows, int ntiles, int nchunks, int cus) {
   if (path != kPathMfma) return ntiles >= 2 * cus ? 2 : 1;
   if (ntiles > 6 * cus && ntiles <= 7 * cus) return 7;
   if (mrows > 16 && ntiles >= 6 * cus) return 8;
   if (ntiles >= 2 * cus) return 4;
+  if (ntiles <= cus && nchunks < 64) return 1;
   return 2;
 }
 #endif
@@ -792,6 +799,15 @@ static hipError_t launch_mfma(const MatmulParams& p, int tiles, hipStream_t s) {
     case 4:
       if constexpr (MROWS == 32) return launch_t<BITS, true, MROWS, 4, 8, 2, true>(p, s);
       else return launch_t<BITS, true, MROWS, 4, 4, 2>(p, s);
+    case 1:
+      // one tile per workgroup: matrices of at most one tile per CU get a
+      // workgroup on every CU without splitting K
+      if constexpr (MROWS == 32) {
+        return launch_t<BITS, true, MROWS, 1, 8, 2, true>(p, s);
+      } else {
+        if (p.M > 8) return launch_t<BITS, true, MROWS, 1, 8, 2, true>(p, s);
+        return launch_t<BITS, true, MROWS, 1, 8, 2>(p, s);
+      }
     default:
       if constexpr (MROWS == 32) {
         return launch_t<BITS, true, MROWS, 2, 8, 2, true>(p, s);
