@@ -470,26 +470,29 @@ class BcqCase:
 
 def variant_section(lutq, torch, args):
     """bf16 activations, per-group zero points, per-group data types (four
-    tables) and binary-coded weights (q = 3) on the headline matrix's shape
-    at batch 1 and 16, against the plain launch (cold)."""
+    tables) on the headline matrix's shape at batch 1 and 16, against the
+    plain launch, and binary-coded weights (q = 3) on that shape at batch 1,
+    16 and 32 (cold)."""
     out = {}
     steps = max(20, args.steps // 4)
-    for M in (1, 16):
-        vc = VariantCase(lutq, torch, "int4_up_proj", None, M)
-        rec = {}
-        for mode in ("plain", "bf16", "zeros", "types"):
-            vc.mode = mode
-            us = time_case(lutq, torch, vc, steps, args.warmup, repeats=EXTRA_REPEATS)
-            nbytes = vc.base_bytes + vc.extra_bytes[mode]
-            rec[mode] = {"us": round(us, 3), "GBps": round(nbytes / (us * 1e-6) / 1e9, 1)}
-            log(f"[bench] variants M={M} {mode}: {us:.2f} us")
-        out[f"int4_up_proj_M{M}"] = rec
-        del vc
-        torch.cuda.empty_cache()
+    for M in (1, 16, 32):
+        if M < 32:
+            vc = VariantCase(lutq, torch, "int4_up_proj", None, M)
+            rec = {}
+            for mode in ("plain", "bf16", "zeros", "types"):
+                vc.mode = mode
+                us = time_case(lutq, torch, vc, steps, args.warmup, repeats=EXTRA_REPEATS)
+                nbytes = vc.base_bytes + vc.extra_bytes[mode]
+                rec[mode] = {"us": round(us, 3), "GBps": round(nbytes / (us * 1e-6) / 1e9, 1)}
+                log(f"[bench] variants M={M} {mode}: {us:.2f} us")
+            out[f"int4_up_proj_M{M}"] = rec
+            del vc
+            torch.cuda.empty_cache()
         bc = BcqCase(lutq, torch, "int4_up_proj", M, q=3)
         us = time_case(lutq, torch, bc, steps, args.warmup, repeats=EXTRA_REPEATS)
         out[f"bcq3_{bc.N}x{bc.K}_M{M}"] = {"us": round(us, 3),
-                                           "GBps": round(bc.bytes / (us * 1e-6) / 1e9, 1)}
+                                           "GBps": round(bc.bytes / (us * 1e-6) / 1e9, 1),
+                                           "plan": lutq.plan(M, bc.N, bc.K, 3)}
         log(f"[bench] variants M={M} bcq q=3: {us:.2f} us")
         del bc
         torch.cuda.empty_cache()

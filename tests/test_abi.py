@@ -334,9 +334,8 @@ def test_matmul_bcq_validates_before_launching(lib):
     assert call(desc=_desc(bits=3, group=0)) == EGROUP
     assert call(alphas=P(0)) == EINVAL
     assert call(alphas=P(0x3001)) == EALIGN
-    for tiles in (1, 4):
-        o = _lib.Options(); o.path, o.tiles = 2, tiles
-        assert call(opts=ctypes.byref(o)) == EINVAL      # MFMA runs 2 tiles per wave
+    o = _lib.Options(); o.path, o.tiles = 2, 3
+    assert call(opts=ctypes.byref(o)) == EINVAL          # no 3-tile MFMA shape
     assert call(M=0) == OK
 
 

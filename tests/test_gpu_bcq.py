@@ -2,12 +2,16 @@
 per plane, row and group, W_hat = sum_p alpha_p (2 bit_p(c) - 1), against the
 oracle.
 
-- every GEMV shape and the MFMA shape, with and without K splits, q = 2, 3,
-  4, groups of 128 and 256, ragged widths and ragged / sliced batches;
+- every GEMV and MFMA shape, with and without K splits, q = 2, 3, 4, groups
+  of 128 and 256, ragged widths and ragged / sliced batches;
+- one-hot activations on every shape and width: each output is one weight,
+  sum_p alpha_p (2 bit_p - 1) summed in plane order in fp32, so a plane bit
+  read from the wrong position (the GEMV table or the MFMA path's register
+  decode) changes it; compared bit for bit;
 - power-of-two plane factors against the plain LUT launch of the uniform
   table 2c - (2^q - 1) (both against the oracle, and each other);
 - a Llama-3-8B projection at q = 3 at the benchmark's batch sizes (sampled
-  rows); MFMA shapes other than 2 tiles are rejected.
+  rows).
 """
 
 import numpy as np
@@ -47,7 +51,7 @@ def check(y, x, c, a, group, rows=None):
     assert ok, f"max err/bound = {worst:.3g}"
 
 
-SHAPES = [("gemv", 1), ("gemv", 2), ("mfma", 2)]
+SHAPES = [("gemv", 1), ("gemv", 2), ("mfma", 1), ("mfma", 2), ("mfma", 4), ("mfma", 7), ("mfma", 8)]
 
 
 @pytest.mark.parametrize("path,tiles", SHAPES)
@@ -85,13 +89,21 @@ def test_bcq_power_of_two_planes_match_the_lut_launch(lutq, q, M):
     assert ok, worst
 
 
-def test_bcq_rejects_other_mfma_shapes(lutq):
-    c, a = make(3, 64, 256, 128, 820)
-    P = lutq.repack(dev(c), 3, 128)
-    x = dev(draw.activations(4, 256, (821,)))
-    for tiles in (1, 4, 8):
-        with pytest.raises(lutq.LutqError):
-            lutq.matmul_bcq(x, P, dev(a), path="mfma", tiles=tiles)
+@pytest.mark.parametrize("path,tiles", SHAPES)
+@pytest.mark.parametrize("q", [2, 3, 4])
+def test_bcq_one_hot_every_shape(lutq, path, tiles, q):
+    N, K = 150, 256
+    c, a = make(q, N, K, 128, 820 + q)
+    x = np.eye(K, dtype=np.float16)
+    P = lutq.repack(dev(c), q, 128)
+    y = lutq.matmul_bcq(dev(x), P, dev(a), path=path, tiles=tiles).cpu().numpy()
+    # y[k, n] = sum over planes, in order, of alpha_p[n][k / 128] * (+-1), in fp32
+    g = np.arange(K) // 128
+    want = np.zeros((N, K), np.float32)
+    for p in range(q):
+        sign = (2 * ((c >> p) & 1).astype(np.int32) - 1).astype(np.float32)
+        want = want + a[p][:, g].astype(np.float32) * sign
+    assert np.array_equal(y.view(np.uint16), want.astype(np.float16).T.view(np.uint16))
 
 
 def test_bcq_llama_projection(lutq):

@@ -147,9 +147,8 @@ int read_options(const lutq_options_t* opts, lutq_options_t* o) {
 }
 
 // Fills the automatic fields of *o (checked by read_options) for an
-// M x N x K product (M, N, K > 0). Binary-coded weights (bcq) take the
-// 2-tile MFMA shape.
-void plan(int M, int N, int K, int cus, lutq_options_t* o, bool bcq = false) {
+// M x N x K product (M, N, K > 0).
+void plan(int M, int N, int K, int cus, lutq_options_t* o) {
   const int nchunks = K / lutq::kChunk;
   const int ntiles = (N + lutq::kTileRows - 1) / lutq::kTileRows;
   if (o->path == LUTQ_PATH_AUTO) {
@@ -163,9 +162,7 @@ void plan(int M, int N, int K, int cus, lutq_options_t* o, bool bcq = false) {
   const int kpath = kernel_path(o->path);
   if (o->tiles == 0) {
     const int rl = rows_per_launch(o->path);
-    o->tiles = (bcq && o->path == LUTQ_PATH_MFMA)
-                   ? 2
-                   : lutq::pick_tiles(kpath, M < rl ? M : rl, ntiles, nchunks, cus);
+    o->tiles = lutq::pick_tiles(kpath, M < rl ? M : rl, ntiles, nchunks, cus);
   }
   const int nrb = (ntiles + o->tiles - 1) / o->tiles;
   if (o->ksplit == 0) {
@@ -203,8 +200,6 @@ int run_matmul(const uint16_t* x, const lutq_matmul_item_t* items, int count, in
   lutq_options_t o;
   int rc = read_options(opts, &o);
   if (rc) return rc;
-  // binary-coded weights run the GEMV shapes and the 2-tile MFMA shape
-  if (bcq && o.path == LUTQ_PATH_MFMA && o.tiles != 0 && o.tiles != 2) return LUTQ_EINVAL;
   const bool bf16 = o.dtype == LUTQ_DTYPE_BF16;
   if (bf16 && (bcq || types)) return LUTQ_EUNSUPPORTED;
   int live[LUTQ_MAX_FUSED];
@@ -243,7 +238,7 @@ int run_matmul(const uint16_t* x, const lutq_matmul_item_t* items, int count, in
   if (!x) return LUTQ_EINVAL;
   if (!aligned(x, 16)) return LUTQ_EALIGN;
 
-  plan(M, ntiles_all * lutq::kTileRows, K, cu_count(), &o, bcq);
+  plan(M, ntiles_all * lutq::kTileRows, K, cu_count(), &o);
   const int path = kernel_path(o.path);
   const int ksplit = o.ksplit;
   const int rl = rows_per_launch(o.path);

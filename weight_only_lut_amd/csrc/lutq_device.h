@@ -200,6 +200,41 @@ __device__ __forceinline__ u32x4 lds_load_bcq(const uint32_t* table, uint32_t by
   }
 }
 
+// Binary-coded weights on the MFMA path: the planes' fp16 (bit, bit) pairs
+// of k-step j decoded in registers instead of looked up. For each plane, one
+// or two bit operations place every pair's two bits as the two 4-bit halves
+// of a byte, as FP4 (E2M1) codes that are 0 or one power of two (a bit in
+// the mantissa or exponent field, never the sign); gfx950's scaled FP4 to
+// fp16 conversion turns byte i into the fp16 pair of pair i, with the scale
+// that makes the power of two 1.0 -- so pw[i][p] is exactly the entry the
+// table of build_bcq_table holds for pair i, plane p. The bit positions are
+// those step_indices gives: BITS = 4, codes c0 | c1 << 4; BITS = 2 and 3,
+// the two low bits of c0 and c1 in bits 0-3 and (BITS = 3) the high bits
+// of c0 and c1 in bits 4 and 5.
+template <int BITS>
+__device__ __forceinline__ void bcq_planes_decode(uint32_t idx4, u32x4 (&pw)[4]) {
+  uint32_t d[4] = {0u, 0u, 0u, 0u};
+  float sc[4] = {1.f, 1.f, 1.f, 1.f};
+  if constexpr (BITS == 4) {
+    d[0] = idx4 & 0x11111111u; sc[0] = 2.f;        // mantissa bit: 0.5
+    d[1] = idx4 & 0x22222222u;                     // low exponent bit: 1.0
+    d[2] = idx4 & 0x44444444u; sc[2] = 0.5f;       // high exponent bit: 2.0
+    d[3] = (idx4 >> 1) & 0x44444444u; sc[3] = 0.5f;  // bit 3 (the sign) moved to 2.0
+  } else {
+    const uint32_t w2 = idx4 << 2;  // c1's low bits into the upper half
+    d[0] = (idx4 & 0x01010101u) | (w2 & 0x10101010u); sc[0] = 2.f;
+    d[1] = (idx4 & 0x02020202u) | (w2 & 0x20202020u);
+    if constexpr (BITS == 3) d[2] = ((idx4 >> 3) & 0x02020202u) | (idx4 & 0x20202020u);
+  }
+#pragma unroll
+  for (int pl = 0; pl < BITS; ++pl) {
+    pw[0][pl] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d[pl], sc[pl], 0));
+    pw[1][pl] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d[pl], sc[pl], 1));
+    pw[2][pl] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d[pl], sc[pl], 2));
+    pw[3][pl] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d[pl], sc[pl], 3));
+  }
+}
+
 template <int BITS, int THREADS>
 __device__ __forceinline__ void build_bcq_table(uint32_t* table, int tid) {
   static_assert(THREADS % kPairEntries == 0, "whole threads per entry");
@@ -274,11 +309,16 @@ __device__ __forceinline__ void build_pair_table(uint32_t* table, uint32_t lut_l
 // activation pair straight from the broadcasting lane, so no separate
 // broadcast move is issued. `j` must fold to a constant.
 // The compiler inserts no wait states around inline assembly, so the block
-// carries its own: s_nop 1 before (a DPP read of a VGPR needs 2 after a
-// VALU write of it), s_nop 3 after (measured on gfx950: a plain VALU read
-// of a v_dot2c_f32_f16_dpp result within 2 wait states sees the value from
-// before the block; 3 suffice, 4 are given). DPP dots chained on one
-// accumulator need none between them.
+// carries its own:
+//  - s_nop 1 before: the "manually inserted wait states" table of the CDNA3
+//    and CDNA4 instruction set references requires 2 between a VALU write of
+//    a VGPR and a DPP read of it;
+//  - s_nop 3 after: that table has no entry for a plain VALU read of a DPP
+//    result, but on gfx950 (built with AMD clang 22.0.0git, ROCm 7.2.0) such
+//    a read within 2 wait states saw the value from before the block; 3
+//    sufficed, 4 are given. The GEMV parity tests (every shape and variant)
+//    fail if this margin is too small.
+// DPP dots chained on one accumulator need none between them.
 #define LUTQ_DOT2_BCAST4(A, B, C, D)                                                 \
   asm("s_nop 1\n\t"                                                                 \
       "v_dot2c_f32_f16_dpp %0, %1, %2 row_newbcast:" #A " row_mask:0xf bank_mask:0xf\n\t" \
@@ -410,9 +450,12 @@ __device__ __forceinline__ uint32_t max_over_quarters(uint32_t a) {
 // the upper half of the first with the lower half of the second; pairing x
 // with zero leaves each lane r of row 0 (and of row 2) with x_r and its
 // partner. Only lanes 0..15 hold the sum. (VALU; no LDS round trips.)
-// (Written in assembly: with the builtins this compiler added the first
-// swapped register to itself instead of to the second. The s_nop covers the
-// wait states between a VALU write and a lane swap reading it.)
+// (Written in assembly: with the builtins, AMD clang 22.0.0git of ROCm 7.2.0
+// added the first swapped register to itself instead of to the second. The
+// s_nop gives the 2 wait states that the CDNA4 instruction set reference's
+// wait-state table asks for between a VALU write of a VGPR and a
+// cross-lane operation reading it; the compiler adds none around inline
+// assembly. The GEMV parity tests fail if either is wrong.)
 __device__ __forceinline__ float sum_over_quarters_r(float x) {
   uint32_t a0 = __builtin_bit_cast(uint32_t, x), a1 = 0u;
   asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(a0), "+v"(a1));

@@ -94,12 +94,15 @@ void matmul_kernel(const MatmulParams pk) {
   constexpr int RP = ROWS + 4;
   static_assert(ROWS % 16 == 0, "pitch rule assumes whole tiles");
   constexpr int kRedWords = kWaves * MROWS * RP;
-  constexpr int kMainWords = kTableWords + (XS ? kWaves * kXStageWords : 0);
+  // Binary-coded weights on the MFMA path decode their planes in registers
+  // and need no table.
+  constexpr int kTabWords = (BCQ && MFMA) ? 0 : kTableWords;
+  constexpr int kMainWords = kTabWords + (XS ? kWaves * kXStageWords : 0);
   constexpr int kLdsWords = kRedWords > kMainWords ? kRedWords : kMainWords;
   static_assert(kThreads >= kPairEntries, "table build needs one thread per entry");
 
   __shared__ __attribute__((aligned(16))) uint32_t table[kLdsWords];
-  uint32_t* const xstage = table + kTableWords;  // staged: per-wave areas
+  uint32_t* const xstage = table + kTabWords;  // staged: per-wave areas
   __shared__ int arrive_last;
 
   const int tid = threadIdx.x;
@@ -479,19 +482,16 @@ void matmul_kernel(const MatmulParams pk) {
         }
       }
       if constexpr (BCQ) {
-        // Binary coding: the entry of each pair carries every plane's
-        // (bit, bit) pair; plane p's four pairs of k-step j are its B
-        // operand. No lookahead (the planes' operands take the registers).
+        // Binary coding: every plane's (bit, bit) pairs of k-step j, decoded
+        // in registers (bcq_planes_decode); plane p's four pairs are its B
+        // operand.
 #pragma unroll
         for (int t = 0; t < TPW; ++t) {
-          const uint32_t lb = step_lane_byte(t, u);
           f32x4 cg[QS][MT];
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            const uint32_t idx4 = step_indices<BITS>(cbuf[s][t], j);
             u32x4 pw[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) pw[i] = lds_load_bcq<BITS>(table, pair_addr(idx4, lb, i));
+            bcq_planes_decode<BITS>(step_indices<BITS>(cbuf[s][t], j), pw);
 #pragma unroll
             for (int pl = 0; pl < QS; ++pl) {
               const f16x8 b = __builtin_bit_cast(f16x8, u32x4{pw[0][pl], pw[1][pl], pw[2][pl], pw[3][pl]});
@@ -573,8 +573,11 @@ void matmul_kernel(const MatmulParams pk) {
   if constexpr (GROUPED) issue_scales(0);
   static_for<PF - 1>([&](auto S) { issue(S, chunk(decltype(S)::value)); });
 
-  if constexpr (BCQ) build_bcq_table<BITS, kThreads>(table, tid);
-  else build_pair_table<BITS, kThreads, TYPED>(table, lut_lane, tid);
+  if constexpr (BCQ) {
+    if constexpr (!MFMA) build_bcq_table<BITS, kThreads>(table, tid);
+  } else {
+    build_pair_table<BITS, kThreads, TYPED>(table, lut_lane, tid);
+  }
   __syncthreads();
 
   // One step at position u of a U-step group starting at i0. Steps past the
@@ -759,12 +762,14 @@ static hipError_t launch_t(const MatmulParams& p, hipStream_t s) {
 #define LUTQ_LAUNCH(G, Z, T, Q, H, OCCV, XSV)                                              \
   matmul_kernel<BITS, MFMA, MROWS, G, Z, T, Q, H, PFK, TPW, WAVES, OCCV, XSV><<<grid, block, 0, s>>>(p)
   if (p.bcq) {
-    // binary-coded weights: GEMV shapes and the 2-tile MFMA shape only
-    // (not staged at 16 rows: the plane lookups already load the LDS)
-    if constexpr (!MFMA || TPW == 2)
-      LUTQ_LAUNCH(true, false, false, true, false, OCC_G, XS && MROWS == 32);
-    else
+    // binary-coded weights: staged at 32 batch rows only (at 16, staging the
+    // 2-tile shape measured 16.0 -> 17.3 us on 14336 x 4096, q = 3). Four
+    // planes at 32 rows x 4 tiles take the 4-wave shape (launch_mfma), so
+    // the 8-wave one, which would spill, is not built for them.
+    if constexpr (BITS == 4 && MFMA && MROWS == 32 && TPW == 4 && WAVES == 8)
       return hipErrorInvalidValue;
+    else
+      LUTQ_LAUNCH(true, false, false, true, false, OCC_G, XS && MROWS == 32);
   } else if (p.bf16) {
     // bf16 activations, plain tables
     if (p.group == 0)
@@ -797,8 +802,14 @@ static hipError_t launch_mfma(const MatmulParams& p, int tiles, hipStream_t s) {
     case 8: return launch_t<BITS, true, MROWS, 8, 4, 2>(p, s);
     case 7: return launch_t<BITS, true, MROWS, 7, 4, 2>(p, s);
     case 4:
-      if constexpr (MROWS == 32) return launch_t<BITS, true, MROWS, 4, 8, 2, true>(p, s);
-      else return launch_t<BITS, true, MROWS, 4, 4, 2>(p, s);
+      if constexpr (MROWS == 32) {
+        // four binary planes' operands at 32 rows need more than the 256
+        // registers of two waves per SIMD: one wave per SIMD, unstaged
+        if (BITS == 4 && p.bcq) return launch_t<BITS, true, MROWS, 4, 4, 1>(p, s);
+        return launch_t<BITS, true, MROWS, 4, 8, 2, true>(p, s);
+      } else {
+        return launch_t<BITS, true, MROWS, 4, 4, 2>(p, s);
+      }
     case 1:
       // one tile per workgroup: matrices of at most one tile per CU get a
       // workgroup on every CU without splitting K
