@@ -40,6 +40,7 @@ CACHE_BYTES = 256 << 20        # Infinity Cache (MALL)
 COLD_SET_BYTES = 2 * CACHE_BYTES
 EXTRA_REPEATS = 3    # timed replays per secondary line (median)
 HEADLINE_REPEATS = 7  # timed replays of the headline (median, spread reported)
+SETTLE_MS = 30.0      # untimed graph replays before the timed ones, per line
 
 
 def algorithmic_bytes(M, N, K, bits, group):
@@ -327,10 +328,11 @@ def time_replays(lutq, torch, case, steps, warmup, repeats=1):
     """Microseconds per call of every timed replay of `steps` back-to-back calls.
 
     `warmup` eager calls, then the `steps` calls are captured in a HIP graph,
-    replayed once untimed, and replayed `repeats` more times, each between
-    HIP events recorded on the stream the kernels run on (host-side launch
-    cost stays outside the timed region), with a device synchronization on
-    both sides.
+    replayed untimed for about SETTLE_MS milliseconds (the first replays
+    after an idle spell run at lower clocks), and replayed `repeats` more
+    times, each between HIP events recorded on the stream the kernels run on
+    (host-side launch cost stays outside the timed region), with a device
+    synchronization on both sides.
     """
     stream = torch.cuda.Stream()
     with torch.cuda.stream(stream):
@@ -341,8 +343,16 @@ def time_replays(lutq, torch, case, steps, warmup, repeats=1):
     with torch.cuda.graph(graph, stream=stream):
         for i in range(steps):
             case.call(lutq, i)
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     with torch.cuda.stream(stream):
+        start.record()
         graph.replay()
+        stop.record()
+    torch.cuda.synchronize()
+    settle = min(2000, int(SETTLE_MS / max(start.elapsed_time(stop), 1e-3)))
+    with torch.cuda.stream(stream):
+        for _ in range(settle):
+            graph.replay()
     torch.cuda.synchronize()
     times = []
     for _ in range(repeats):

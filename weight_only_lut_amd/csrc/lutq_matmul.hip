@@ -570,8 +570,18 @@ void matmul_kernel(const MatmulParams pk) {
   // issued when step i opens a batch. Within the loop every step issues the
   // same loads (those past the wave's last chunk read nothing); the loop
   // ends with the wave's last chunk.
+  // The first chunk's loads go out before the first scale batch: the load
+  // counter drains in issue order, so the first step's wait for its codes
+  // does not include the scales, which it needs only at its end (measured
+  // 7.8 -> 7.6 us on 14336 x 4096 at batch 1, 4.65 -> 4.39 us on 4096 x
+  // 4096; issuing the scales after every prologue chunk instead lost 0.3 us
+  // on 4096 x 14336).
+  issue(std::integral_constant<int, 0>{}, chunk(0));
   if constexpr (GROUPED) issue_scales(0);
-  static_for<PF - 1>([&](auto S) { issue(S, chunk(decltype(S)::value)); });
+  static_for<PF - 2>([&](auto S) {
+    constexpr int i = decltype(S)::value + 1;
+    issue(std::integral_constant<int, i>{}, chunk(i));
+  });
 
   if constexpr (BCQ) {
     if constexpr (!MFMA) build_bcq_table<BITS, kThreads>(table, tid);
