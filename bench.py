@@ -1021,6 +1021,15 @@ def _find(dirpath, suffix):
     raise FileNotFoundError(f"no *{suffix} under {dirpath}")
 
 
+def _median_duration_us(trace, name_part):
+    """Median per-dispatch duration (kernel trace) of the kernels whose name
+    contains name_part, in microseconds."""
+    import statistics
+    d = [int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in trace
+         if name_part in r["Kernel_Name"]]
+    return round(statistics.median(d) / 1e3, 3) if d else None
+
+
 def _counter_per_dispatch(dirpath, counter, name_part):
     import statistics
     per = {}
@@ -1037,6 +1046,7 @@ def summarize_profile(kt_dir, fetch_dir, write_dir, command=""):
     summary per kernel and workload, plus the counters json."""
     from weight_only_lut_amd.build import source_digest
     stats = _read_csv(_find(kt_dir, "kernel_stats.csv"))
+    trace = _read_csv(_find(kt_dir, "kernel_trace.csv"))
     copy_name = "neg_kernel"
     f_copy, _ = _counter_per_dispatch(fetch_dir, "FETCH_SIZE", copy_name)
     w_copy, _ = _counter_per_dispatch(write_dir, "WRITE_SIZE", copy_name)
@@ -1064,6 +1074,7 @@ def summarize_profile(kt_dir, fetch_dir, write_dir, command=""):
                "calls": int(dur[0]["Calls"]) if dur else 0, "avg_duration_us": avg,
                "min_duration_us": float(dur[0]["MinNs"]) / 1e3 if dur else None,
                "max_duration_us": float(dur[0]["MaxNs"]) / 1e3 if dur else None,
+               "median_duration_us": _median_duration_us(trace, part),
                "plan": plan, "algorithmic_bytes": nbytes, "flops": flops}
         if avg:
             rec["achieved_GBps"] = round(nbytes / (avg * 1e3), 1)
@@ -1081,7 +1092,8 @@ def summarize_profile(kt_dir, fetch_dir, write_dir, command=""):
                  "| quantity | value |", "|---|---|",
                  f"| calls traced | {rec['calls']} |",
                  f"| average duration (kernel trace) | {avg if avg is None else round(avg, 3)} us |",
-                 f"| min / max duration | {rec['min_duration_us']} / {rec['max_duration_us']} us |",
+                 f"| min / median / max duration | {rec['min_duration_us']} / "
+                 f"{rec['median_duration_us']} / {rec['max_duration_us']} us |",
                  f"| algorithmic bytes per launch | {nbytes:,} |",
                  f"| achieved (algorithmic bytes / average duration) | {rec.get('achieved_GBps')} GB/s, "
                  f"{rec.get('achieved_TFLOPs')} TFLOP/s |",
