@@ -140,11 +140,12 @@ def test_parity_every_shape(lutq, path, tiles, bits, table, group, M, ksplit):
 
 
 @pytest.mark.parametrize("path,tiles", SHAPES)
-def test_one_hot_every_shape(lutq, path, tiles):
+@pytest.mark.parametrize("bits,table", [(2, "int"), (3, "lloyd_max"), (4, "nf")])
+def test_one_hot_every_shape(lutq, path, tiles, bits, table):
     N, K = 150, 256
-    c, T, s, _ = workloads.small_case(3, "lloyd_max", 128, 1, N, K, seed=60)
+    c, T, s, _ = workloads.small_case(bits, table, 128, 1, N, K, seed=60 + bits)
     x = np.eye(K, dtype=np.float16)
-    y = run(lutq, c, T, s, x, 3, 128, path=path, tiles=tiles)
+    y = run(lutq, c, T, s, x, bits, 128, path=path, tiles=tiles)
     want = (T[c].astype(np.float32) * s[:, np.arange(K) // 128].astype(np.float32)).astype(np.float16)
     assert np.array_equal(y.view(np.uint16), want.T.view(np.uint16))
 

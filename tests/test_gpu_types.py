@@ -3,6 +3,8 @@ reads table types[n, g], W_hat = s * (T_type[c] - z), against the oracle.
 
 - every path and workgroup shape, with and without K splits and zero
   points, 1 to 4 tables of 2, 3 and 4 bits, ragged widths and batches;
+- one-hot activations on every shape, with and without zero points: each
+  output is one weight of its group's table, compared bit for bit;
 - one table with all ids 0 gives the plain launch bit for bit;
 - ids at or above the table count follow the documented mapping;
 - a Llama-3-8B projection with four table kinds (sampled rows).
@@ -55,6 +57,26 @@ def check(y, x, c, luts, types, s, z, group, rows=None):
 
 
 SHAPES = [("gemv", 1), ("gemv", 2), ("mfma", 1), ("mfma", 2), ("mfma", 4), ("mfma", 7), ("mfma", 8)]
+
+
+@pytest.mark.parametrize("path,tiles", SHAPES)
+@pytest.mark.parametrize("bits", [2, 3, 4])
+@pytest.mark.parametrize("zeros", [False, True])
+def test_types_one_hot_every_shape(lutq, path, tiles, bits, zeros):
+    # one-hot activations: each output is one weight of its group's table,
+    # s * (T_type[c] - z), rounded once in fp32 per step, then to fp16
+    N, K = 150, 512
+    c, luts, types, s, z = make(bits, 4, N, K, 128, 740 + bits, zeros)
+    x = np.eye(K, dtype=np.float16)
+    P = lutq.repack(dev(c), bits, 128)
+    y = lutq.matmul(dev(x), P, dev(luts), dev(s), types=dev(types),
+                    zeros=dev(z) if z is not None else None, path=path, tiles=tiles).cpu().numpy()
+    g = np.arange(K) // 128
+    w = luts[types[:, g], c].astype(np.float32)
+    if z is not None:
+        w = w - z[:, g].astype(np.float32)
+    want = (s[:, g].astype(np.float32) * w).astype(np.float16)
+    assert np.array_equal(y.view(np.uint16), want.T.view(np.uint16))
 
 
 @pytest.mark.parametrize("path,tiles", SHAPES)

@@ -3,6 +3,8 @@ fused launch): W_hat = s * (T[c] - z) against the oracle.
 
 - every path and workgroup shape, with and without K splits, 2/3/4 bits,
   groups of 128 and 256, ragged widths and ragged / sliced batches;
+- one-hot activations on every shape: each output is s * (T[c] - z),
+  compared bit for bit;
 - z = 0 gives bit for bit the launch without zero points;
 - asymmetric INT (uniform table 0..2^b-1, zero points inside the range);
 - a fused launch mixing matrices with and without zero points equals the
@@ -72,6 +74,23 @@ def test_zero_points_every_shape(lutq, path, tiles, bits, table, group, M, kspli
                      ksplit=ksplit)
     y1 = lutq.matmul(xd, P, Td, sd, path=path, tiles=tiles, ksplit=ksplit)
     assert torch.equal(y0.view(torch.int16), y1.view(torch.int16))
+
+
+@pytest.mark.parametrize("path,tiles", SHAPES)
+@pytest.mark.parametrize("bits,table", [(2, "int"), (3, "lloyd_max"), (4, "nf")])
+def test_zero_points_one_hot_every_shape(lutq, path, tiles, bits, table):
+    # one-hot activations: each output is one weight, s * (T[c] - z), with the
+    # difference and the product each rounded once in fp32, then to fp16
+    N, K = 150, 256
+    c, T, s, _ = workloads.small_case(bits, table, 128, 1, N, K, seed=630 + bits)
+    z = zeros_for(s, T, 631 + bits)
+    x = np.eye(K, dtype=np.float16)
+    P = lutq.repack(dev(c), bits, 128)
+    y = lutq.matmul(dev(x), P, dev(T), dev(s), zeros=dev(z), path=path, tiles=tiles).cpu().numpy()
+    g = np.arange(K) // 128
+    d = T[c].astype(np.float32) - z[:, g].astype(np.float32)
+    want = (s[:, g].astype(np.float32) * d).astype(np.float16)
+    assert np.array_equal(y.view(np.uint16), want.T.view(np.uint16))
 
 
 @pytest.mark.parametrize("bits", [2, 3, 4])
