@@ -743,6 +743,9 @@ def main():
                     help="write profiles/ summaries from rocprofv3 output and exit")
     ap.add_argument("--summarize-sq", metavar="SQ_DIR",
                     help="write the SQ-counter summary from a rocprofv3 --pmc run and exit")
+    ap.add_argument("--summarize-mem", nargs=2, metavar=("PASS_A_DIR", "PASS_B_DIR"),
+                    help="write the memory-pipeline counter summary from the two rocprofv3 --pmc "
+                         "passes (MEM_COUNTERS_A, MEM_COUNTERS_B) and exit")
     ap.add_argument("--profile-command", default="", help="command line recorded in the summary")
     args = ap.parse_args()
     if args.summarize_profile:
@@ -750,6 +753,9 @@ def main():
         return
     if args.summarize_sq:
         summarize_sq(args.summarize_sq, command=args.profile_command)
+        return
+    if args.summarize_mem:
+        summarize_mem(*args.summarize_mem, command=args.profile_command)
         return
     if args.gpus != 1:
         print(json.dumps({"error": "runs on one GPU only: --gpus above 1 is not supported "
@@ -1159,6 +1165,86 @@ def summarize_sq(sq_dir, command=""):
         lines.append(f"| {cname} | " + " | ".join(row) + " |")
     lines += ["", "Kernels:", ""] + [f"- `{c[0]}`: `{c[1]}`" for c in cols]
     with open(os.path.join(ROOT, "profiles", "matmul_kernel_sq_counters.md"), "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+
+
+# Memory-pipeline counters of the profiled kernels, in two rocprofv3 --pmc
+# passes (each within one pass's counter limits): the address (TA) and data
+# (TD) units and the vector L1 (TCP), then the L2 (TCC) and the address
+# unit's stalls on it. GRBM_GUI_ACTIVE (GPU busy cycles) normalizes both.
+MEM_COUNTERS_A = ("TA_TA_BUSY_sum", "TA_BUFFER_READ_WAVEFRONTS_sum", "TD_TD_BUSY_sum",
+                  "TCP_TOTAL_CACHE_ACCESSES_sum", "TCP_TCC_READ_REQ_sum",
+                  "TCP_TCP_TA_DATA_STALL_CYCLES_sum", "TCP_PENDING_STALL_CYCLES_sum", "GRBM_GUI_ACTIVE")
+MEM_COUNTERS_B = ("TCC_HIT_sum", "TCC_MISS_sum", "TA_ADDR_STALLED_BY_TC_CYCLES_sum",
+                  "TA_DATA_STALLED_BY_TC_CYCLES_sum", "GRBM_GUI_ACTIVE")
+
+
+def _gpu_cu_count(dirpath):
+    for r in _read_csv(_find(dirpath, "agent_info.csv")):
+        if r.get("Agent_Type") == "GPU":
+            return int(r["Cu_Count"])
+    return None
+
+
+def summarize_mem(dir_a, dir_b, command=""):
+    """profiles/matmul_kernel_mem_counters.md: the memory-pipeline counters of
+    the PROFILE_CASES kernels (median per dispatch), with the busy fractions
+    and hit rates derived from them."""
+    import weight_only_lut_amd as lutq
+    from synth import workloads
+    from weight_only_lut_amd.build import source_digest
+    lutq.load_library()
+    cus = _gpu_cu_count(dir_a) or 256
+    cols = []
+    for label, wname, mat, M in PROFILE_CASES:
+        wl = workloads.WORKLOADS[wname]
+        _, m = wl.matrix(mat)
+        part = kernel_signature(wl.bits, wl.group, M, lutq.plan(M, m.N, m.K, wl.bits))
+        vals = {c: _counter_per_dispatch(dir_a, c, part)[0] for c in MEM_COUNTERS_A}
+        vals.update({f"{c}@B": _counter_per_dispatch(dir_b, c, part)[0] for c in MEM_COUNTERS_B})
+        cols.append((label, part, vals))
+
+    def frac(a, b):
+        return f"{a / b:.1%}" if a is not None and b else "-"
+
+    derived = [
+        ("address unit (TA) busy, of GPU busy cycles x CUs",
+         lambda v: frac(v["TA_TA_BUSY_sum"], v["GRBM_GUI_ACTIVE"] and v["GRBM_GUI_ACTIVE"] * cus)),
+        ("data unit (TD) busy, of GPU busy cycles x CUs",
+         lambda v: frac(v["TD_TD_BUSY_sum"], v["GRBM_GUI_ACTIVE"] and v["GRBM_GUI_ACTIVE"] * cus)),
+        ("buffer-load wave instructions per dispatch",
+         lambda v: f"{v['TA_BUFFER_READ_WAVEFRONTS_sum']:,.0f}" if v["TA_BUFFER_READ_WAVEFRONTS_sum"] else "-"),
+        ("L1 (TCP) tag accesses per buffer-load instruction",
+         lambda v: (f"{v['TCP_TOTAL_CACHE_ACCESSES_sum'] / v['TA_BUFFER_READ_WAVEFRONTS_sum']:.1f}"
+                    if v["TCP_TOTAL_CACHE_ACCESSES_sum"] and v["TA_BUFFER_READ_WAVEFRONTS_sum"] else "-")),
+        ("L1 accesses that go on to the L2",
+         lambda v: frac(v["TCP_TCC_READ_REQ_sum"], v["TCP_TOTAL_CACHE_ACCESSES_sum"])),
+        ("L2 (TCC) hit rate",
+         lambda v: frac(v["TCC_HIT_sum@B"], (v["TCC_HIT_sum@B"] or 0) + (v["TCC_MISS_sum@B"] or 0))),
+        ("TA address stalled by the cache, of TA busy (second pass)",
+         lambda v: frac(v["TA_ADDR_STALLED_BY_TC_CYCLES_sum@B"], v["TA_TA_BUSY_sum"])),
+        ("TA data stalled by the cache, of TA busy (second pass)",
+         lambda v: frac(v["TA_DATA_STALLED_BY_TC_CYCLES_sum@B"], v["TA_TA_BUSY_sum"])),
+        ("L1 pending-request stall cycles, per CU and GPU busy cycle",
+         lambda v: frac(v["TCP_PENDING_STALL_CYCLES_sum"], v["GRBM_GUI_ACTIVE"] and v["GRBM_GUI_ACTIVE"] * cus)),
+    ]
+    lines = ["# lutq matmul kernels: memory-pipeline counters (rocprofv3 --pmc)", "",
+             f"Source digest of the matmul kernel sources: `{source_digest()}`. Medians per dispatch "
+             f"over each run ({cus} CUs); kernels as in the per-case summaries `matmul_kernel_<case>.md`.",
+             "The two passes are separate runs of the same workload, so ratios across them are "
+             "approximate.", "",
+             "Commands (`<repo>` is the repository root):", "", "```", command or "(not recorded)", "```", "",
+             "| derived | " + " | ".join(f"`{c[0]}`" for c in cols) + " |",
+             "|---|" + "---|" * len(cols)]
+    for name, fn in derived:
+        lines.append(f"| {name} | " + " | ".join(fn(v) for _, _, v in cols) + " |")
+    lines += ["", "| counter (median per dispatch) | " + " | ".join(f"`{c[0]}`" for c in cols) + " |",
+              "|---|" + "---|" * len(cols)]
+    for cname in list(MEM_COUNTERS_A) + [f"{c}@B" for c in MEM_COUNTERS_B]:
+        lines.append(f"| {cname.replace('@B', ' (second pass)')} | " + " | ".join(
+            f"{v[cname]:,.0f}" if v[cname] is not None else "-" for _, _, v in cols) + " |")
+    lines += ["", "Kernels:", ""] + [f"- `{c[0]}`: `{c[1]}`" for c in cols]
+    with open(os.path.join(ROOT, "profiles", "matmul_kernel_mem_counters.md"), "w") as fh:
         fh.write("\n".join(lines) + "\n")
 
 
