@@ -307,34 +307,39 @@ __device__ __forceinline__ void build_pair_table(uint32_t* table, uint32_t lut_l
 // acc += dot(x from lane 4j+i of this lane's 16-lane row, p_i), i = 0..3, in
 // that order: four v_dot2c_f32_f16 whose DPP row_newbcast reads the
 // activation pair straight from the broadcasting lane, so no separate
-// broadcast move is issued. `j` must fold to a constant.
-// The compiler inserts no wait states around inline assembly, so the block
+// broadcast move is issued. `j` must fold to a constant, and the four k-steps
+// j = 0..3 of one accumulator must be issued as one chain, in order: between
+// them the accumulator is read only by the next DPP dot.
+// The compiler inserts no wait states around inline assembly, so the chain
 // carries its own:
-//  - s_nop 1 before: the "manually inserted wait states" table of the CDNA3
-//    and CDNA4 instruction set references requires 2 between a VALU write of
-//    a VGPR and a DPP read of it;
-//  - s_nop 3 after: that table has no entry for a plain VALU read of a DPP
-//    result, but on gfx950 (built with AMD clang 22.0.0git, ROCm 7.2.0) such
-//    a read within 2 wait states saw the value from before the block; 3
-//    sufficed, 4 are given. The GEMV parity tests (every shape and variant)
-//    fail if this margin is too small.
-// DPP dots chained on one accumulator need none between them.
-#define LUTQ_DOT2_BCAST4(A, B, C, D)                                                 \
-  asm("s_nop 1\n\t"                                                                 \
+//  - s_nop 1 before step 0: the "manually inserted wait states" table of the
+//    CDNA3 and CDNA4 instruction set references requires 2 between a VALU
+//    write of a VGPR and a DPP read of it (x is written by VALU in the bf16
+//    path, and the accumulator is zeroed just before);
+//  - s_nop 3 after step 3: that table has no entry for a plain VALU read of a
+//    DPP dot's result, but on gfx950 (built with AMD clang 22.0.0git, ROCm
+//    7.2.0) such a read within 2 wait states saw the value from before the
+//    dot; 3 sufficed, 4 are given;
+//  - none in between: DPP dots chained on one accumulator read it correctly
+//    back to back (as the four dots of one step already do).
+// The GEMV parity tests (every shape and variant, bit-exact one-hot cases
+// included) fail if any of these is too small.
+#define LUTQ_DOT2_BCAST4(PRE, POST, A, B, C, D)                                      \
+  asm(PRE                                                                           \
       "v_dot2c_f32_f16_dpp %0, %1, %2 row_newbcast:" #A " row_mask:0xf bank_mask:0xf\n\t" \
       "v_dot2c_f32_f16_dpp %0, %1, %3 row_newbcast:" #B " row_mask:0xf bank_mask:0xf\n\t" \
       "v_dot2c_f32_f16_dpp %0, %1, %4 row_newbcast:" #C " row_mask:0xf bank_mask:0xf\n\t" \
       "v_dot2c_f32_f16_dpp %0, %1, %5 row_newbcast:" #D " row_mask:0xf bank_mask:0xf\n\t" \
-      "s_nop 3"                                                                      \
+      POST                                                                           \
       : "+v"(acc)                                                                    \
       : "v"(x), "v"(p0), "v"(p1), "v"(p2), "v"(p3))
 __device__ __forceinline__ float dot2_bcast4(float acc, uint32_t x, uint32_t p0, uint32_t p1,
                                              uint32_t p2, uint32_t p3, int j) {
   switch (j) {
-    case 0: LUTQ_DOT2_BCAST4(0, 1, 2, 3); break;
-    case 1: LUTQ_DOT2_BCAST4(4, 5, 6, 7); break;
-    case 2: LUTQ_DOT2_BCAST4(8, 9, 10, 11); break;
-    default: LUTQ_DOT2_BCAST4(12, 13, 14, 15); break;
+    case 0: LUTQ_DOT2_BCAST4("s_nop 1\n\t", "", 0, 1, 2, 3); break;
+    case 1: LUTQ_DOT2_BCAST4("", "", 4, 5, 6, 7); break;
+    case 2: LUTQ_DOT2_BCAST4("", "", 8, 9, 10, 11); break;
+    default: LUTQ_DOT2_BCAST4("", "s_nop 3", 12, 13, 14, 15); break;
   }
   return acc;
 }
