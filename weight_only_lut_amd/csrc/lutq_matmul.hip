@@ -26,6 +26,10 @@
 //    the A operand is the matching 16x32 activation tile, loaded from
 //    global memory (L2-resident) in fragment order, or (8-wave shapes from
 //    9 batch rows) loaded row-contiguous and rearranged through LDS.
+// Binary-coded weights (AlphaTuning abstract: binary planes and separate
+// scaling factors) run the same skeleton with one partial sum per plane: the
+// GEMV reads each pair's plane bits from an LDS table, the MFMA path decodes
+// them in registers (bcq_planes_decode) and needs no table.
 // Waves are combined in LDS in a fixed order; splits along K across
 // workgroups are combined by the last-arriving workgroup, again in a fixed
 // order, so results are deterministic.
@@ -625,7 +629,7 @@ void matmul_kernel(const MatmulParams pk) {
   }
 
   // ---- combine the waves (fixed order) ------------------------------------
-  __syncthreads();  // every wave is done with the table; reuse it
+  __syncthreads();  // every wave is done with the table and staging areas; reuse them
   float* red = reinterpret_cast<float*>(table);  // [kWaves][MROWS][RP]
 #pragma unroll
   for (int t = 0; t < TPW; ++t) {
