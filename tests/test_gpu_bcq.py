@@ -10,8 +10,8 @@ oracle.
   decode) changes it; compared bit for bit;
 - power-of-two plane factors against the plain LUT launch of the uniform
   table 2c - (2^q - 1) (both against the oracle, and each other);
-- a Llama-3-8B projection at q = 3 at the benchmark's batch sizes (sampled
-  rows).
+- a Llama-3-8B projection (14336 x 4096, the benchmark's binary-coded
+  shape) at q = 3 at the benchmark's batch sizes, every output compared.
 """
 
 import numpy as np
@@ -113,9 +113,7 @@ def test_bcq_llama_projection(lutq):
     c, a = make(3, N, K, 128, 830)
     P = lutq.repack(dev(c), 3, 128)
     ad = dev(a)
-    rows = np.unique(np.concatenate([np.random.default_rng(831).choice(N, 512, replace=False),
-                                     [0, N - 1]]))
     for M in (1, 8, 16, 32):
         x = workloads.activations(w, M, "gate")
         y = lutq.matmul_bcq(dev(x), P, ad).cpu().numpy()
-        check(y, x, c, a, 128, rows)
+        check(y, x, c, a, 128)

@@ -9,7 +9,8 @@ the fp16 bound plus one bf16 rounding (oracle.error_bound_bf16).
 - activations far outside fp16's range (1e-30 .. 1e30, mixed within a chunk
   and across chunks and rows);
 - fused launches in bf16 equal the single launches bit for bit;
-- a Llama-3-8B projection at the benchmark's batch sizes (sampled rows).
+- a Llama-3-8B projection at the benchmark's batch sizes, every output
+  compared.
 """
 
 import numpy as np
@@ -121,10 +122,7 @@ def test_bf16_llama_projection(lutq):
     c, T, s = workloads.quantized(w, "down")
     P = lutq.repack(dev(c), w.bits, w.group)
     Td, sd = dev(T), dev(s)
-    N = c.shape[0]
-    rows = np.unique(np.concatenate([np.random.default_rng(931).choice(N, 512, replace=False),
-                                     [0, N - 1]]))
     for M in (1, 8, 16, 32):
         xb, xv = bf16(workloads.activations(w, M, "down").astype(np.float32))
         y = from_bf16(lutq.matmul(dev_bf16(xb), P, Td, sd))
-        check(y, xv, c, T, s, w.group, rows)
+        check(y, xv, c, T, s, w.group)

@@ -7,7 +7,7 @@ reads table types[n, g], W_hat = s * (T_type[c] - z), against the oracle.
   output is one weight of its group's table, compared bit for bit;
 - one table with all ids 0 gives the plain launch bit for bit;
 - ids at or above the table count follow the documented mapping;
-- a Llama-3-8B projection with four table kinds (sampled rows).
+- a Llama-3-8B projection with four table kinds, every output compared.
 """
 
 import numpy as np
@@ -128,10 +128,7 @@ def test_types_llama_projection(lutq):
     types = np.random.default_rng(730).integers(0, 4, s.shape).astype(np.uint8)
     P = lutq.repack(dev(c), 4, w.group)
     Ld, sd, td = dev(luts), dev(s), dev(types)
-    N = c.shape[0]
-    rows = np.unique(np.concatenate([np.random.default_rng(731).choice(N, 512, replace=False),
-                                     [0, N - 1]]))
     for M in (1, 8, 16, 32):
         x = workloads.activations(w, M, "up")
         y = lutq.matmul(dev(x), P, Ld, sd, types=td).cpu().numpy()
-        check(y, x, c, luts, types, s, None, w.group, rows)
+        check(y, x, c, luts, types, s, None, w.group)

@@ -9,7 +9,8 @@ fused launch): W_hat = s * (T[c] - z) against the oracle.
 - asymmetric INT (uniform table 0..2^b-1, zero points inside the range);
 - a fused launch mixing matrices with and without zero points equals the
   single-matrix launches bit for bit;
-- a Llama-3-8B projection at the benchmark's batch sizes (sampled rows).
+- a Llama-3-8B projection at the benchmark's batch sizes, every output
+  compared.
 """
 
 import numpy as np
@@ -145,10 +146,7 @@ def test_zero_points_llama_projection(lutq):
     z = zeros_for(s, T, 630)
     P = lutq.repack(dev(c), w.bits, w.group)
     Td, sd, zd = dev(T), dev(s), dev(z)
-    N = c.shape[0]
-    rows = np.unique(np.concatenate([np.random.default_rng(631).choice(N, 512, replace=False),
-                                     [0, N - 1]]))
     for M in (1, 8, 16, 32):
         x = workloads.activations(w, M, "gate")
         y = lutq.matmul(dev(x), P, Td, sd, zeros=zd).cpu().numpy()
-        assert_close(y, x, c, T, s, w.group, z, rows)
+        assert_close(y, x, c, T, s, w.group, z)
