@@ -1,0 +1,133 @@
+"""GPU parity at the size limits of the C ABI: K = 2^20 codes per row
+(LUTQ_MAX_K) and N close to 2^24 rows (LUTQ_MAX_N).
+
+- K = 2^20 over 40 rows (two whole tiles and a ragged half tile): 4-bit NF
+  and 3-bit Lloyd-Max with groups of 128, 2-bit INT with one scale per
+  tensor, batch 1, 5 and 32, on the automatic plan (which splits K up to 256
+  ways) and on each path: every output against the oracle. One-hot
+  activations at the first and the last k of the row: each output is one
+  weight, compared bit for bit.
+- N = 2^24 - 5 rows of K = 128 (the last tile ragged), 4-bit: one-hot
+  activations at eight positions of the chunk, every one of the 16.8 M
+  outputs per row compared bit for bit; random activations at batch 1 and
+  32 against the oracle on the first and last tiles and 4096 random rows.
+  The codes repeat with a prime period of 65521 rows (generating 2 GiB of
+  random bytes would dominate the test); the scales do not repeat, so an
+  output read from the wrong row still fails.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+from synth import draw, tables
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+MAX_K = 1 << 20
+MAX_N = 1 << 24
+
+
+@pytest.fixture(scope="module")
+def lutq():
+    import weight_only_lut_amd as m
+    m.load_library()
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return m
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def one_hot_want(c, T, s, group, ks):
+    """y[m, n] for x = e_{ks[m]}: fp16(fp32(s[n, k / group]) * fp32(T[c[n, k]]))."""
+    out = []
+    for k in ks:
+        sc = s.reshape(-1)[0] if group == 0 else s[:, k // group]
+        out.append((T[c[:, k]].astype(np.float32) * sc.astype(np.float32)).astype(np.float16))
+    return np.stack(out)
+
+
+@pytest.fixture(scope="module", params=[(4, "nf", 128), (3, "lloyd_max", 128), (2, "int", 0)],
+                ids=["4bit-g128", "3bit-g128", "2bit-tensor"])
+def longest_k(lutq, request):
+    bits, table, group = request.param
+    N, K = 40, MAX_K
+    rng = np.random.default_rng(900 + bits)
+    c = rng.integers(0, 1 << bits, (N, K), dtype=np.uint8)
+    T = tables.make(table, bits)
+    shape = (1,) if group == 0 else (N, K // group)
+    s = rng.uniform(0.005, 0.03, shape).astype(np.float16)
+    P = lutq.repack(dev(c), bits, group)
+    return bits, group, c, T, s, P, dev(T), dev(s)
+
+
+@pytest.mark.parametrize("M", [1, 5, 32])
+@pytest.mark.parametrize("path", [None, "gemv", "mfma"])
+def test_longest_k(lutq, longest_k, M, path):
+    bits, group, c, T, s, P, Td, sd = longest_k
+    K = c.shape[1]
+    x = draw.activations(M, K, (910, bits, M))
+    kw = {} if path is None else {"path": path}
+    plan = lutq.plan(M, c.shape[0], K, bits, **kw)
+    assert plan["ksplit"] > 1          # the limit case runs through the K split
+    y = lutq.matmul(dev(x), P, Td, sd, **kw).cpu().numpy()
+    y_ref, B = oracle.reference(x, c, T, s, group)
+    ok, worst = oracle.check(y, y_ref, B)
+    assert ok, f"{plan}: max err/bound = {worst:.3g}"
+
+
+@pytest.mark.parametrize("path", [None, "gemv", "mfma"])
+def test_longest_k_one_hot(lutq, longest_k, path):
+    bits, group, c, T, s, P, Td, sd = longest_k
+    K = c.shape[1]
+    ks = [0, 1, K // 2 + 77, K - 2, K - 1]
+    x = np.zeros((len(ks), K), np.float16)
+    x[np.arange(len(ks)), ks] = 1
+    kw = {} if path is None else {"path": path}
+    y = lutq.matmul(dev(x), P, Td, sd, **kw).cpu().numpy()
+    want = one_hot_want(c, T, s, group, ks)
+    assert np.array_equal(y.view(np.uint16), want.view(np.uint16))
+
+
+@pytest.fixture(scope="module")
+def most_rows(lutq):
+    N, K, bits, group = MAX_N - 5, 128, 4, 128
+    rng = np.random.default_rng(920)
+    c = np.resize(rng.integers(0, 16, (65521, K), dtype=np.uint8), (N, K))
+    T = tables.make("nf", bits)
+    s = rng.uniform(0.005, 0.03, (N, 1)).astype(np.float16)
+    cd = dev(c)
+    P = lutq.repack(cd, bits, group)
+    del cd
+    torch.cuda.synchronize()
+    return c, T, s, P, dev(T), dev(s)
+
+
+@pytest.mark.parametrize("path", [None, "gemv", "mfma"])
+def test_most_rows_one_hot(lutq, most_rows, path):
+    c, T, s, P, Td, sd = most_rows
+    ks = [0, 17, 38, 63, 64, 90, 111, 127]
+    x = np.zeros((len(ks), 128), np.float16)
+    x[np.arange(len(ks)), ks] = 1
+    kw = {} if path is None else {"path": path}
+    y = lutq.matmul(dev(x), P, Td, sd, **kw).cpu().numpy()
+    want = one_hot_want(c, T, s, 128, ks)
+    assert np.array_equal(y.view(np.uint16), want.view(np.uint16))
+
+
+@pytest.mark.parametrize("M", [1, 32])
+def test_most_rows_random(lutq, most_rows, M):
+    c, T, s, P, Td, sd = most_rows
+    N = c.shape[0]
+    x = draw.activations(M, 128, (921, M))
+    y = lutq.matmul(dev(x), P, Td, sd).cpu().numpy()
+    rng = np.random.default_rng(922)
+    rows = np.unique(np.concatenate([np.arange(16), np.arange(N - 27, N),
+                                     rng.integers(0, N, 4096)]))
+    y_ref, B = oracle.reference_rows(x, c, T, s, 128, rows)
+    ok, worst = oracle.check(y[:, rows], y_ref, B)
+    assert ok, f"max err/bound = {worst:.3g}"
