@@ -3,8 +3,8 @@
 
 - K = 2^20 over 40 rows (two whole tiles and a ragged half tile): 4-bit NF
   and 3-bit Lloyd-Max with groups of 128, 2-bit INT with one scale per
-  tensor, batch 1, 5 and 32, on the automatic plan (which splits K up to 256
-  ways) and on each path: every output against the oracle. One-hot
+  tensor, batch 1, 5 and 32, on the automatic plan and on each path (each
+  splits K 85 or 128 ways): every output against the oracle. One-hot
   activations at the first and the last k of the row: each output is one
   weight, compared bit for bit.
 - N = 2^24 - 5 rows of K = 128 (the last tile ragged), 4-bit: one-hot
