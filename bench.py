@@ -296,6 +296,7 @@ def configs_section(lutq, torch, args, inputs):
                        "bits": w.bits, "table": w.table, "group": w.group,
                        "plan": lutq.plan(M, m.N, m.K, w.bits)}
                 rec.update(row_stats(us, case.bytes, case.flops))
+                rec["bits_read_per_weight"] = round(case.bytes * 8 / (m.N * m.K), 4)
                 rows.append(rec)
                 log(f"[bench] config {wname}/{m.name} M={M}: {us:.2f} us, {rec['GBps']} GB/s, "
                     f"{rec['frac_of_roof']:.3f} of roof")
