@@ -6,7 +6,9 @@
   tensor, batch 1, 5 and 32, on the automatic plan and on each path (each
   splits K 85 or 128 ways): every output against the oracle. One-hot
   activations at the first and the last k of the row: each output is one
-  weight, compared bit for bit.
+  weight, compared bit for bit. Zero points, four data types, binary coding
+  (q = 3), bf16 activations and a fused launch of two matrices at the same
+  K, batch 1 and 32, against the oracle.
 - N = 2^24 - 5 rows of K = 128 (the last tile ragged), 4-bit: one-hot
   activations at eight positions of the chunk, every one of the 16.8 M
   outputs per row compared bit for bit; random activations at batch 1 and
@@ -131,3 +133,62 @@ def test_most_rows_random(lutq, most_rows, M):
     y_ref, B = oracle.reference_rows(x, c, T, s, 128, rows)
     ok, worst = oracle.check(y[:, rows], y_ref, B)
     assert ok, f"max err/bound = {worst:.3g}"
+
+
+def _bf16(v):
+    """fp32 values -> (bf16 bits rounded to nearest even, their exact fp32 values)."""
+    f = np.asarray(v, np.float32).view(np.uint32).astype(np.uint64)
+    bits = (((f + 0x7FFF + ((f >> 16) & 1)) >> 16) & 0xFFFF).astype(np.uint16)
+    return bits, (bits.astype(np.uint32) << 16).view(np.float32)
+
+
+@pytest.mark.parametrize("M", [1, 32])
+@pytest.mark.parametrize("variant", ["zeros", "types", "bcq", "bf16", "fused"])
+def test_longest_k_variants(lutq, variant, M):
+    # every variant at K = 2^20 on the automatic plan (split 85 or 128 ways)
+    N, K, group = 40, MAX_K, 128
+    rng = np.random.default_rng(930)
+    x = draw.activations(M, K, (931, M))
+    c = rng.integers(0, 16, (N, K), dtype=np.uint8)
+    T = tables.make("nf", 4)
+    s = rng.uniform(0.005, 0.03, (N, K // group)).astype(np.float16)
+    out = "fp16"
+    if variant == "bcq":
+        q = 3
+        c = c & 7
+        a = np.stack([rng.uniform(0.01, 0.03, (N, K // group)) / 2 ** p
+                      for p in range(q)]).astype(np.float16)
+        y = lutq.matmul_bcq(dev(x), lutq.repack(dev(c), q, group), dev(a)).cpu().numpy()
+        results = [(y, oracle.reference_bcq(x, c, a, group))]
+    elif variant == "zeros":
+        z = rng.uniform(float(T.min()), float(T.max()), s.shape).astype(np.float16)
+        y = lutq.matmul(dev(x), lutq.repack(dev(c), 4, group), dev(T), dev(s),
+                        zeros=dev(z)).cpu().numpy()
+        results = [(y, oracle.reference(x, c, T, s, group, zeros=z))]
+    elif variant == "types":
+        luts = np.stack([tables.make(k, 4) for k in ("nf", "int", "lloyd_max", "log")])
+        ty = rng.integers(0, 4, s.shape).astype(np.uint8)
+        y = lutq.matmul(dev(x), lutq.repack(dev(c), 4, group), dev(luts), dev(s),
+                        types=dev(ty)).cpu().numpy()
+        results = [(y, oracle.reference(x, c, luts, s, group, types=ty))]
+    elif variant == "bf16":
+        xb, xv = _bf16(x.astype(np.float32) * 1e4)
+        xd = torch.from_numpy(xb.view(np.int16)).cuda().view(torch.bfloat16)
+        yt = lutq.matmul(xd, lutq.repack(dev(c), 4, group), dev(T), dev(s))
+        y = (yt.view(torch.int16).cpu().numpy().view(np.uint16).astype(np.uint32) << 16).view(np.float32)
+        results = [(y, oracle.reference(xv, c, T, s, group))]
+        out = "bf16"
+    else:
+        # two matrices sharing x, the second with zero points, in one launch
+        N2 = 24
+        c2 = rng.integers(0, 16, (N2, K), dtype=np.uint8)
+        s2 = rng.uniform(0.005, 0.03, (N2, K // group)).astype(np.float16)
+        z2 = rng.uniform(-0.5, 0.5, s2.shape).astype(np.float16)
+        Td = dev(T)
+        ys = lutq.matmul_multi(dev(x), [(lutq.repack(dev(c), 4, group), Td, dev(s)),
+                                        (lutq.repack(dev(c2), 4, group), Td, dev(s2), dev(z2))])
+        results = [(ys[0].cpu().numpy(), oracle.reference(x, c, T, s, group)),
+                   (ys[1].cpu().numpy(), oracle.reference(x, c2, T, s2, group, zeros=z2))]
+    for y, (y_ref, B) in results:
+        ok, worst = oracle.check(y, y_ref, B, out=out)
+        assert ok, f"{variant}: max err/bound = {worst:.3g}"
