@@ -8,7 +8,9 @@
   activations at the first and the last k of the row: each output is one
   weight, compared bit for bit. Zero points, four data types, binary coding
   (q = 3), bf16 activations and a fused launch of two matrices at the same
-  K, batch 1 and 32, against the oracle.
+  K, batch 1 and 32, against the oracle. The quantizer at the same K
+  (groups of 128, one scale per tensor, one group per row): codes and scales
+  bit for bit.
 - N = 2^24 - 5 rows of K = 128 (the last tile ragged), 4-bit: one-hot
   activations at eight positions of the chunk, every one of the 16.8 M
   outputs per row compared bit for bit; random activations at batch 1 and
@@ -192,3 +194,24 @@ def test_longest_k_variants(lutq, variant, M):
     for y, (y_ref, B) in results:
         ok, worst = oracle.check(y, y_ref, B, out=out)
         assert ok, f"{variant}: max err/bound = {worst:.3g}"
+
+
+@pytest.mark.parametrize("kind,bits,rule,group", [("nf", 4, "absmax", 128), ("int", 4, "range", 128),
+                                                  ("nf", 4, "absmax", 0), ("int", 3, "range", MAX_K)])
+def test_quantizer_longest_k(lutq, kind, bits, rule, group):
+    # the quantizer at K = 2^20: groups of 128, one scale per tensor (three
+    # launches), and one group spanning the whole row (read twice); codes and
+    # scales bit for bit, the weight error to 1e-9 relative
+    from oracle import quantize as Q
+    N, K = 40, MAX_K
+    w = draw.weights("normal", N, K, (940,), sigma=0.02)
+    T = tables.make(kind, bits)
+    wd, Td = dev(w), dev(T)
+    c, s = lutq.quantize(wd, Td, bits, group, rule)
+    c_ref, s_ref = Q.quantize(w, T, group, rule)
+    assert np.array_equal(s.cpu().numpy().view(np.uint16), s_ref.view(np.uint16)), "scales differ"
+    bad = np.argwhere(c.cpu().numpy() != c_ref)
+    assert bad.size == 0, f"{len(bad)} codes differ, first at {bad[0].tolist()}"
+    err = lutq.quant_error(wd, Td, bits, group, rule)
+    want = Q.sq_error(w, T, c_ref, s_ref, group)
+    assert abs(err - want) <= 1e-9 * want
