@@ -15,6 +15,7 @@
   activations at eight positions of the chunk, every one of the 16.8 M
   outputs per row compared bit for bit; random activations at batch 1 and
   32 against the oracle on the first and last tiles and 4096 random rows.
+- At both limits, unpack(repack(c)) == c.
   The codes repeat with a prime period of 65521 rows (generating 2 GiB of
   random bytes would dominate the test); the scales do not repeat, so an
   output read from the wrong row still fails.
@@ -215,3 +216,14 @@ def test_quantizer_longest_k(lutq, kind, bits, rule, group):
     err = lutq.quant_error(wd, Td, bits, group, rule)
     want = Q.sq_error(w, T, c_ref, s_ref, group)
     assert abs(err - want) <= 1e-9 * want
+
+
+def test_longest_k_unpack(lutq, longest_k):
+    # the layout round trip at K = 2^20 (3-bit: the 2-bit and 1-bit planes)
+    bits, group, c, T, s, P, Td, sd = longest_k
+    assert np.array_equal(lutq.unpack(P).cpu().numpy(), c)
+
+
+def test_most_rows_unpack(lutq, most_rows):
+    c, T, s, P, Td, sd = most_rows
+    assert np.array_equal(lutq.unpack(P).cpu().numpy(), c)
