@@ -28,6 +28,7 @@ from __future__ import annotations
 import argparse
 import json
 import os
+import re
 import sys
 import time
 
@@ -1037,6 +1038,16 @@ def _median_duration_us(trace, name_part):
     return round(statistics.median(d) / 1e3, 3) if d else None
 
 
+def _timed_avg_us(trace, name_part, ncalls):
+    """Average duration of the last `ncalls` dispatches (by start time) of the
+    kernels whose name contains name_part: the timed replays of time_replays,
+    which follow the warm-up calls and the settle phase."""
+    d = sorted((int(r["Start_Timestamp"]), int(r["End_Timestamp"])) for r in trace
+               if name_part in r["Kernel_Name"])
+    d = d[-ncalls:]
+    return round(sum(e - b for b, e in d) / len(d) / 1e3, 3) if len(d) == ncalls else None
+
+
 def _counter_per_dispatch(dirpath, counter, name_part):
     import statistics
     per = {}
@@ -1065,6 +1076,9 @@ def summarize_profile(kt_dir, fetch_dir, write_dir, command=""):
     from synth import workloads
     lutq.load_library()
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    # the timed replays of the traced run: EXTRA_REPEATS replays of --steps calls
+    steps = re.search(r"--profile-set --steps (\d+)", command or "")
+    ntimed = EXTRA_REPEATS * int(steps.group(1)) if steps else None
     for label, wname, mat, M in PROFILE_CASES:
         wl = workloads.WORKLOADS[wname]
         _, m = wl.matrix(mat)
@@ -1082,6 +1096,7 @@ def summarize_profile(kt_dir, fetch_dir, write_dir, command=""):
                "min_duration_us": float(dur[0]["MinNs"]) / 1e3 if dur else None,
                "max_duration_us": float(dur[0]["MaxNs"]) / 1e3 if dur else None,
                "median_duration_us": _median_duration_us(trace, part),
+               "timed_avg_duration_us": _timed_avg_us(trace, part, ntimed) if ntimed else None,
                "plan": plan, "algorithmic_bytes": nbytes, "flops": flops}
         if avg:
             rec["achieved_GBps"] = round(nbytes / (avg * 1e3), 1)
@@ -1101,6 +1116,8 @@ def summarize_profile(kt_dir, fetch_dir, write_dir, command=""):
                  f"| average duration (kernel trace) | {avg if avg is None else round(avg, 3)} us |",
                  f"| min / median / max duration | {rec['min_duration_us']} / "
                  f"{rec['median_duration_us']} / {rec['max_duration_us']} us |",
+                 f"| average of the timed replays (the last {ntimed} dispatches, after the warm-up calls "
+                 f"and the settle phase, as the benchmark times them) | {rec['timed_avg_duration_us']} us |",
                  f"| algorithmic bytes per launch | {nbytes:,} |",
                  f"| achieved (algorithmic bytes / average duration) | {rec.get('achieved_GBps')} GB/s, "
                  f"{rec.get('achieved_TFLOPs')} TFLOP/s |",

@@ -252,18 +252,21 @@ __device__ __forceinline__ void build_bcq_table(uint32_t* table, int tid) {
     d[pl] = (((c0 >> pl) & 1u) ? 0x3C00u : 0u) | (((c1 >> pl) & 1u) ? 0x3C000000u : 0u);
   const u32x4 q = BITS == 2 ? u32x4{d[0], d[1], d[0], d[1]} : u32x4{d[0], d[1], d[2], d[3]};
   u32x4* dst = reinterpret_cast<u32x4*>(table) + idx * kStores + part * C;
+  // rotated by the thread, as in build_pair_table
 #pragma unroll
-  for (int k = 0; k < C; ++k) dst[(k + idx) & (C - 1)] = q;
+  for (int k = 0; k < C; ++k) dst[(k + (uint32_t)tid) & (C - 1)] = q;
 }
 
 // Fill the duplicated pair table. `lut_lane` holds T[lane] in lanes
 // 0..2^BITS-1 of every wave; entries are gathered with cross-lane reads.
 // THREADS / 256 threads share an entry: each computes the entry's value once
 // and writes its share of the 64 copies as 16-byte stores. Store k of a
-// thread goes to chunk (k + entry) mod C of its share, so the 64 lanes of a
-// store instruction cover all 64 banks evenly (4 dwords per bank, the
-// minimum for 16-byte stores) instead of piling onto two bank groups. The
-// caller issues a barrier before the first lookup.
+// thread goes to chunk (k + thread) mod C of its share. Measured on gfx950
+// (SQ_LDS_BANK_CONFLICT), 16-byte stores are served eight lanes at a time
+// over 32 four-byte banks: rotating by the entry instead put the two threads
+// of an entry (8 waves) on the same banks, 64 conflict cycles per wave; by
+// the thread, eight consecutive lanes always cover the 32 banks. The caller
+// issues a barrier before the first lookup.
 template <int BITS, int THREADS, bool TYPED = false>
 __device__ __forceinline__ void build_pair_table(uint32_t* table, uint32_t lut_lane, int tid) {
   static_assert(THREADS % kPairEntries == 0, "whole threads per entry");
@@ -282,7 +285,7 @@ __device__ __forceinline__ void build_pair_table(uint32_t* table, uint32_t lut_l
     const uint32_t v = v0 | (v1 << 16);
     const u32x4 q = {v, v, v, v};
 #pragma unroll
-    for (int k = 0; k < C; ++k) dst[(k + idx) & (C - 1)] = q;
+    for (int k = 0; k < C; ++k) dst[(k + (uint32_t)tid) & (C - 1)] = q;
   } else {
     // the pair of every type (lut_lane holds table t's entries at lanes t 2^BITS + c)
     uint32_t v[kMaxTypes];
@@ -294,7 +297,7 @@ __device__ __forceinline__ void build_pair_table(uint32_t* table, uint32_t lut_l
     }
 #pragma unroll
     for (int k = 0; k < C; ++k) {
-      const int slot4 = (k + (int)idx) & (C - 1);                 // 16-byte store in the share
+      const int slot4 = (k + tid) & (C - 1);                      // 16-byte store in the share
       const int type = (int)(part * kCopiesPer + 4 * slot4) / kTypedCopies;
       uint32_t w = v[0];
 #pragma unroll
